@@ -1,0 +1,260 @@
+/*
+ * fmask.h -- C ABI of libfmask: forward pass of exact softmax attention under a
+ * structured sparse mask that is handed over in compressed form (never as a dense
+ * Sq x Skv boolean matrix), for AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operation (web pages on mask-aware attention):
+ *  - FlashMask rebuttal (arXiv 2410.01359 review response): the mask types (causal
+ *    document, document, shared question), the split between "mask block size" and
+ *    the kernel's "tiling block size", and the point that fully masked blocks must
+ *    not be computed.
+ *  - "Efficiently Dispatching Flash Attention For Partially Filled Attention Masks"
+ *    (Binary Block Masking), abstract: block-level mask awareness, sequence packing
+ *    and Medusa tree masks.
+ *  - Ascend CANN "sparseMode" page: attenMask semantics (the QK^T product is masked
+ *    where the mask is set), the preTokens/nextTokens band anchored at the lower
+ *    right corner, and cumulative sequence-length arrays.
+ *  - llama.cpp fork PR "vulkan: selected-key flash attention for QSA block
+ *    selection": attention whose visibility is a per-query list of K/V blocks of 32
+ *    cells, with invalid (-1) and duplicate entries skipped.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless the comment says (host).
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *  - The library never allocates or frees device memory; the caller owns every
+ *    buffer and sizes it with the *_bytes queries.  All launches are asynchronous
+ *    on `stream`; host arrays named in a descriptor are consumed before the call
+ *    returns (they are copied into the caller's `out` buffer).
+ *  - Errors that the host can detect (null pointers, bad sizes, inconsistent
+ *    descriptors, unsupported dtype / head size / tile shape, undersized buffers)
+ *    return a negative status BEFORE anything is launched.  A failed launch
+ *    returns FMASK_ERR_HIP.  No combination that a kernel does not implement is
+ *    ever served by a kernel that ignores the mask: it returns
+ *    FMASK_ERR_UNSUPPORTED instead.
+ *  - fmask_last_error() gives a human-readable detail of the last failure on the
+ *    calling thread.
+ */
+#ifndef FMASK_H
+#define FMASK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t fmask_status;
+#define FMASK_OK               0
+#define FMASK_ERR_INVALID     (-1) /* inconsistent or out-of-range argument        */
+#define FMASK_ERR_UNSUPPORTED (-2) /* valid, but no kernel implements it           */
+#define FMASK_ERR_CAPACITY    (-3) /* a caller buffer is smaller than required     */
+#define FMASK_ERR_HIP         (-4) /* the HIP runtime reported an error            */
+
+/* Mask families.  vis(i, j) = 1 means query row i attends to key column j.
+ * Row and column indices are 0-based token positions.                         */
+enum fmask_family {
+  /* j <= i (anchored at the upper left corner, Ascend "leftUpCausal").          */
+  FMASK_CAUSAL = 1,
+  /* seg(i) == seg(j), segments given by cu_seg (requires sq == skv).            */
+  FMASK_DOCUMENT = 2,
+  /* seg(i) == seg(j) and j <= i: packed sequences (FlashMask "causal document"). */
+  FMASK_CAUSAL_DOCUMENT = 3,
+  /* Segment 0 of cu_seg is the question, segments 1.. are answers:
+   * j <= i and (seg(j) == seg(i) or seg(j) == 0)  (FlashMask "shared question"). */
+  FMASK_SHARED_QUESTION = 4,
+  /* Ascend band, anchored at the lower right corner:
+   * with r = i + skv - sq:  r - pre_tokens <= j <= r + next_tokens (inclusive).
+   * Negative pre_tokens or next_tokens are allowed; rows may become empty.      */
+  FMASK_BAND = 5,
+  /* Causal prefix of tree_prefix tokens followed by tree_n draft tokens whose
+   * parents are tree_parent[t] (< t, -1 for a root).  Prefix rows are causal; a
+   * draft row sees the whole prefix and its own ancestors and itself
+   * (Medusa-style tree mask).  Requires sq == skv == tree_prefix + tree_n.      */
+  FMASK_TREE = 6,
+  /* 64 x 64 block pattern: per block SKIP / PARTIAL / FULL, PARTIAL blocks carry
+   * 64 row words (bit c of word r = element (64*bi + r, 64*bj + c)); if
+   * force_diag, every element (i, i) is visible as well (Binary Block Masking).  */
+  FMASK_BLOCK_BITMAP = 7,
+  /* Per query a list of sel_n block indices of sel_cells cells; a key is visible
+   * iff its block floor(j / sel_cells) is listed.  Entries outside
+   * [0, ceil(skv / sel_cells)) are ignored; duplicates count once.  No causal
+   * term (visibility lives only in the list).                                   */
+  FMASK_SELECTED_KEY = 8,
+  /* Raw per-key-column masked row intervals [UTS, UTE) and [LTS, LTE) (the
+   * FlashMask column encoding): element (i, j) is masked iff
+   * UTS_j <= i < UTE_j or LTS_j <= i < LTE_j.                                   */
+  FMASK_INTERVALS = 9,
+  /* j <= i + skv - sq (anchored at the lower right corner, "rightDownCausal"). */
+  FMASK_CAUSAL_BOTTOM_RIGHT = 10
+};
+
+/* Kinds of canonical encoding written by fmask_encode. */
+enum fmask_kind {
+  FMASK_ENC_INTERVALS = 1, /* int32 SoA [batch][heads][4][skv]: UTS, UTE, LTS, LTE */
+  FMASK_ENC_BITMAP    = 2, /* 64 x 64 block states + canonical word pool          */
+  FMASK_ENC_SELECTED  = 3  /* sorted, de-duplicated, validated block lists        */
+};
+
+/* Tile-state byte values. */
+enum fmask_tile_state { FMASK_SKIP = 0, FMASK_PARTIAL = 1, FMASK_FULL = 2 };
+
+enum fmask_dtype { FMASK_F32 = 0, FMASK_BF16 = 1 };
+
+#define FMASK_BLOCK          64          /* granularity of the bitmap encoding */
+#define FMASK_LIST_FULL_BIT  0x80000000u /* flag in tile lists: tile is FULL   */
+#define FMASK_MAX_SEL_N      64          /* longest selected-key list          */
+
+/* Mask description (host struct).  Only the fields of `family` are read.
+ *
+ * batch / heads: number of distinct masks along the batch axis / query-head
+ *   axis.  1 means one mask shared by every batch entry / head.  The segment,
+ *   band, causal and tree families describe one mask (batch = heads = 1).
+ *   FMASK_BLOCK_BITMAP and FMASK_INTERVALS accept batch >= 1 and heads >= 1;
+ *   FMASK_SELECTED_KEY accepts batch >= 1 and heads == 1 (one list per query,
+ *   shared by all heads).                                                       */
+typedef struct fmask_mask_desc {
+  int32_t family;
+  int32_t batch;
+  int32_t heads;
+  int32_t reserved0;
+  int64_t sq, skv;
+  /* segment families: (host) cumulative boundaries cu_seg[0] = 0 <
+   * cu_seg[1] < ... < cu_seg[n_seg] = sq; n_seg >= 1 segments.                  */
+  const int32_t *cu_seg;
+  int32_t n_seg;
+  int32_t reserved1;
+  /* band */
+  int64_t pre_tokens, next_tokens;
+  /* tree: (host) tree_parent[tree_n]                                            */
+  const int32_t *tree_parent;
+  int32_t tree_prefix, tree_n;
+  /* block bitmap (device): blk_state uint8 [batch][heads][nbq][nbk] with
+   * nbq = ceil(sq / 64), nbk = ceil(skv / 64); blk_index int32 same shape (pool
+   * entry of a PARTIAL block, ignored otherwise); blk_bits [blk_pool_n][64].     */
+  const uint8_t *blk_state;
+  const int32_t *blk_index;
+  const uint64_t *blk_bits;
+  int64_t blk_pool_n;
+  int32_t force_diag;
+  int32_t reserved2;
+  /* selected key (device): sel int32 [batch][sq][sel_n], sel_n <= 64.           */
+  const int32_t *sel;
+  int32_t sel_n, sel_cells;
+  /* raw intervals (device): int32 [batch][heads][4][skv] in the order
+   * UTS, UTE, LTS, LTE.                                                         */
+  const int32_t *raw_intervals;
+} fmask_mask_desc;
+
+/* Canonical encoding (host struct filled by fmask_encode; device views into the
+ * caller's `out` buffer, valid while that buffer lives).
+ *
+ * INTERVALS: for each (b, h, column j) the masked rows of column j, split into
+ *   maximal runs: no run -> UT = [0,0), LT = [sq,sq); one run [a,b) -> UT = [0,b)
+ *   if a == 0 else LT = [a,b) (the other one empty as above); two runs -> UT =
+ *   the first, LT = the second.  Columns that would need more than two runs are
+ *   not representable; fmask_encode then writes the BITMAP kind (tree family).
+ * BITMAP: blk_state recomputed from the words (all valid elements set -> FULL,
+ *   none -> SKIP), blk_index = -1 unless PARTIAL, pool entries in row-major
+ *   (b, h, bi, bj) order, bits outside [0,sq) x [0,skv) cleared.
+ * SELECTED: per (b, query) the valid distinct entries in ascending order,
+ *   padded with -1 to sel_n, and their count.                                   */
+typedef struct fmask_encoded {
+  int32_t kind;
+  int32_t batch, heads;
+  int32_t blk;                     /* 64 (BITMAP) or sel_cells (SELECTED)       */
+  int64_t sq, skv;
+  const int32_t *intervals;        /* INTERVALS: [batch][heads][4][skv]         */
+  const uint8_t *blk_state;        /* BITMAP: [batch][heads][nbq][nbk]          */
+  const int32_t *blk_index;        /* BITMAP: same shape                        */
+  const uint64_t *blk_bits;        /* BITMAP: [pool_cap][64]                    */
+  const int32_t *blk_pool_count;   /* BITMAP: device scalar, entries used       */
+  int64_t nbq, nbk, pool_cap;
+  const int32_t *sel_list;         /* SELECTED: [batch][sq][sel_n]              */
+  const int32_t *sel_count;        /* SELECTED: [batch][sq]                     */
+  int32_t sel_n;
+  int32_t reserved0;
+} fmask_encoded;
+
+/* Tile table (host struct filled by fmask_classify; device views into `out`).
+ * Tile (qt, kt) covers rows [qt*bm, min((qt+1)*bm, sq)) and columns
+ * [kt*bn, min((kt+1)*bn, skv)).  state is SKIP if no element of the tile is
+ * visible, FULL if all are, PARTIAL otherwise (exact, element by element).
+ * list[b][h][qt][0..count) holds the non-SKIP kt in ascending order, with
+ * FMASK_LIST_FULL_BIT set for FULL tiles.  order[] lists the batch*heads*nqt
+ * tile rows (index (b*heads + h)*nqt + qt) by decreasing count, ties by index.   */
+typedef struct fmask_tiles {
+  int32_t bm, bn;
+  int32_t nqt, nkt;
+  int32_t batch, heads;
+  int32_t reserved0, reserved1;
+  const uint8_t *state;            /* [batch][heads][nqt][nkt]                  */
+  const int32_t *list;             /* [batch][heads][nqt][nkt]                  */
+  const int32_t *count;            /* [batch][heads][nqt]                       */
+  const int32_t *order;            /* [batch*heads*nqt]                         */
+} fmask_tiles;
+
+/* Attention problem.  Q [b][hq][sq][d], K and V [b][hkv][skv][d], O like Q, in
+ * `dtype` (FMASK_BF16: bfloat16, FMASK_F32: float); strides in elements for the
+ * batch, head and sequence axes, the d axis is contiguous.  Query head h reads
+ * K/V head h / (hq / hkv).  LSE (optional) is float [b][hq][sq], contiguous.   */
+typedef struct fmask_attn_args {
+  int32_t dtype;
+  int32_t b, hq, hkv;
+  int64_t sq, skv;
+  int32_t d;
+  int32_t reserved0;
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
+  float scale;
+  int32_t reserved1;
+} fmask_attn_args;
+
+/* Bytes of device memory fmask_encode needs for `desc`; 0 if desc is invalid. */
+size_t fmask_encode_bytes(const fmask_mask_desc *desc);
+
+/* Turn the mask description into its canonical compressed encoding (mask
+ * encoder).  out: device buffer of at least fmask_encode_bytes(desc) bytes, 256-
+ * byte aligned.  *enc (host) receives the kind and device views into out.       */
+fmask_status fmask_encode(const fmask_mask_desc *desc, void *out, size_t out_bytes,
+                          fmask_encoded *enc, void *stream);
+
+/* Bytes of device memory fmask_classify needs; 0 if the arguments are invalid. */
+size_t fmask_classify_bytes(const fmask_encoded *enc, int32_t bm, int32_t bn);
+
+/* Reduce an INTERVALS or BITMAP encoding to the exact per-tile SKIP / PARTIAL /
+ * FULL table at tile size bm x bn, plus per-row compact lists of the non-SKIP
+ * tiles and a longest-first order of tile rows (tile classifier).  bm and bn are
+ * multiples of 16 in [16, 256]; the BITMAP kind needs multiples of 64.          */
+fmask_status fmask_classify(const fmask_encoded *enc, int32_t bm, int32_t bn, void *out,
+                            size_t out_bytes, fmask_tiles *tiles, void *stream);
+
+/* Masked attention forward: for every (batch, q head, row) with visible set V_i,
+ * s_ij = scale * <Q_i, K_j>, O_i = sum_{j in V_i} softmax(s_i)_j V_j and
+ * LSE_i = log sum_{j in V_i} exp(s_ij); a row with no visible key gets O_i = 0
+ * and LSE_i = -inf.  SKIP tiles are never loaded, FULL tiles are computed
+ * without per-element masking, PARTIAL tiles are masked element by element.
+ * tiles must come from fmask_classify on the same encoding (NULL for the
+ * SELECTED kind, whose kernel walks the lists directly).  The tile shape must be
+ * one that fmask_preferred_tile can return for (dtype, d, kind).
+ * Supported: BF16 with d in {64, 128} on INTERVALS / BITMAP; F32 with d in
+ * {64, 128} on INTERVALS / BITMAP; BF16 with d == 256 and sel_cells == 32 on
+ * SELECTED.                                                                     */
+fmask_status fmask_attn_fwd(const fmask_attn_args *args, const void *q, const void *k,
+                            const void *v, void *o, float *lse, const fmask_encoded *enc,
+                            const fmask_tiles *tiles, void *stream);
+
+/* Tile shape the attention kernel for (dtype, d, encoding kind) uses. */
+fmask_status fmask_preferred_tile(int32_t dtype, int32_t d, int32_t kind, int32_t *bm,
+                                  int32_t *bn);
+
+/* Static description of a status code. */
+const char *fmask_status_str(fmask_status s);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *fmask_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FMASK_H */

@@ -1,0 +1,155 @@
+"""Masked softmax attention in float64 (oracle; test infrastructure only).
+
+Definition (the forward pass every page on the subject computes; the mask is
+applied to the QK^T product as on the Ascend sparseMode page, masked positions
+contributing nothing):
+    g      = h // (Hq / Hkv)                       query head h reads K/V head g
+    s_ij   = scale * sum_d Q[b,h,i,d] * K[b,g,j,d]
+    V_i    = {j : vis(i, j)}
+    V_i empty:  O_i = 0, LSE_i = -inf
+    else:       m = max_{j in V_i} s_ij,  p_j = exp(s_ij - m) (0 off V_i),
+                l = sum_j p_j,  O_i = sum_j (p_j / l) V[b,g,j,:],
+                LSE_i = m + log(l)
+
+``attention_dense`` evaluates this with dense QK^T over ALL key columns for a
+chunk of rows, applies the materialised mask with np.where and multiplies the
+dense P by V.  ``attention_rows`` does the same for a list of sampled rows,
+``attention_bruteforce`` with scalar Python loops, and
+``attention_listed_cells`` only over the cells a selected-key list names (the
+host FP64 reference "over the listed cells" that the llama.cpp selected-key PR
+tests its shader against).
+"""
+
+import math
+
+import numpy as np
+
+from . import masks
+
+
+def bf16_bits_to_f64(bits):
+    """float64 values of bfloat16 bit patterns (uint16)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def _softmax_rows(s, vis, vrows):
+    """O and LSE of rows with scores s [R, Skv] (float64), mask vis [R, Skv]."""
+    nonempty = vis.any(axis=1)
+    s_m = np.where(vis, s, -np.inf)
+    m = np.where(nonempty, s_m.max(axis=1, initial=-np.inf), 0.0)
+    p = np.where(vis, np.exp(s - m[:, None]), 0.0)
+    l = p.sum(axis=1)
+    o = p @ vrows
+    safe_l = np.where(nonempty, l, 1.0)
+    o = np.where(nonempty[:, None], o / safe_l[:, None], 0.0)
+    lse = np.where(nonempty, m + np.log(safe_l), -np.inf)
+    return o, lse
+
+
+def attention_dense(q, k, v, vis_fn, scale, row_chunk=512):
+    """Dense masked attention.  q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] (float64).
+
+    vis_fn(b, h, rows) -> bool [len(rows), Skv].  Returns (O float64, LSE float64).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Sq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    O = np.zeros((B, Hq, Sq, v.shape[3]))
+    LSE = np.full((B, Hq, Sq), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for r0 in range(0, Sq, row_chunk):
+                rows = np.arange(r0, min(Sq, r0 + row_chunk))
+                vis = np.asarray(vis_fn(b, h, rows), dtype=bool)
+                s = scale * (q[b, h, rows] @ k[b, g].T)
+                O[b, h, rows], LSE[b, h, rows] = _softmax_rows(s, vis, v[b, g])
+    return O, LSE
+
+
+def spec_vis_fn(spec):
+    """vis_fn for attention_dense from a mask spec (see oracle.masks)."""
+    return lambda b, h, rows: masks.dense_vis(spec, b, h, rows)
+
+
+def attention_rows(q, k, v, vis_fn, scale, samples):
+    """O [n, D] and LSE [n] for sampled rows samples = [(b, h, i), ...]."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    G = Hq // Hkv
+    outs, lses = [], []
+    for b, h, i in samples:
+        g = h // G
+        vis = np.asarray(vis_fn(b, h, np.array([i])), dtype=bool)
+        qi = np.asarray(q[b, h, i], dtype=np.float64)
+        kk = np.asarray(k[b, g], dtype=np.float64)
+        s = scale * (kk @ qi)[None, :]
+        o, lse = _softmax_rows(s, vis, np.asarray(v[b, g], dtype=np.float64))
+        outs.append(o[0])
+        lses.append(lse[0])
+    return np.array(outs), np.array(lses)
+
+
+def attention_bruteforce(q, k, v, vis, scale):
+    """Scalar Python evaluation for one (b, h) slice: q [Sq,D], k/v [Skv,D], vis [Sq,Skv]."""
+    sq, d = len(q), len(q[0])
+    skv = len(k)
+    O = [[0.0] * d for _ in range(sq)]
+    LSE = [-math.inf] * sq
+    for i in range(sq):
+        scores = {}
+        for j in range(skv):
+            if vis[i][j]:
+                acc = 0.0
+                for t in range(d):
+                    acc += float(q[i][t]) * float(k[j][t])
+                scores[j] = scale * acc
+        if not scores:
+            continue
+        m = max(scores.values())
+        w = {j: math.exp(s - m) for j, s in scores.items()}
+        l = sum(w.values())
+        for t in range(d):
+            O[i][t] = sum(w[j] * float(v[j][t]) for j in w) / l
+        LSE[i] = m + math.log(l)
+    return np.array(O), np.array(LSE)
+
+
+def listed_cells(entries, cells, skv):
+    """Key cells named by one selected-key list: valid blocks, each once, ascending."""
+    nblk = -(-skv // cells)
+    blocks = sorted({int(e) for e in entries if 0 <= int(e) < nblk})
+    out = [np.arange(e * cells, min(skv, (e + 1) * cells)) for e in blocks]
+    return np.concatenate(out) if out else np.zeros(0, dtype=np.int64)
+
+
+def attention_listed_cells(q, k, v, sel, cells, scale, samples):
+    """Selected-key attention over exactly the listed cells, for sampled rows.
+
+    sel [B_m][Sq][n] lists (shared by every head); samples = [(b, h, i), ...].
+    """
+    Hq, Hkv = q.shape[1], k.shape[1]
+    G = Hq // Hkv
+    skv = k.shape[2]
+    sel = np.asarray(sel)
+    outs, lses = [], []
+    for b, h, i in samples:
+        g = h // G
+        bm = b if sel.shape[0] > 1 else 0
+        keys = listed_cells(sel[bm, i], cells, skv)
+        if keys.size == 0:
+            outs.append(np.zeros(v.shape[3]))
+            lses.append(-np.inf)
+            continue
+        kk = np.asarray(k[b, g, keys], dtype=np.float64)
+        vv = np.asarray(v[b, g, keys], dtype=np.float64)
+        s = scale * (kk @ np.asarray(q[b, h, i], dtype=np.float64))
+        m = s.max()
+        p = np.exp(s - m)
+        l = p.sum()
+        outs.append((p @ vv) / l)
+        lses.append(m + math.log(l))
+    return np.array(outs), np.array(lses)

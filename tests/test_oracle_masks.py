@@ -1,0 +1,280 @@
+"""Pins of the oracle's mask families and canonical encodings.
+
+- special cases that reduce to another family (one document = causal, band with
+  a huge preTokens and nextTokens = 0 = causal as the Ascend sparseMode page
+  states for mode 0, tree as a chain = causal, ...);
+- exact visible-pair counts of the workloads, from closed forms;
+- the Ascend sparseMode page's worked varlen splits (tests/golden);
+- the band's non-empty condition the Ascend page states for negative
+  nextTokens / preTokens (which pins inclusive ends);
+- dense -> canonical intervals -> dense round trips, closed-form intervals per
+  family, closed-form causal / band tile states, brute-force tile states.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import encode as E
+from oracle import masks as M
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def dense(spec, b=0, h=0):
+    return np.asarray(M.dense_vis(spec, b, h))
+
+
+def causal(s):
+    return np.tril(np.ones((s, s), dtype=bool))
+
+
+# ---------------------------------------------------------------- families
+
+def test_family_reductions():
+    S = 40
+    one_doc = np.array([0, S], dtype=np.int32)
+    np.testing.assert_array_equal(dense(dict(family="causal_document", sq=S, skv=S, cu_seg=one_doc)), causal(S))
+    assert dense(dict(family="document", sq=S, skv=S, cu_seg=one_doc)).all()
+    np.testing.assert_array_equal(dense(dict(family="shared_question", sq=S, skv=S, cu_seg=one_doc)), causal(S))
+    np.testing.assert_array_equal(dense(dict(family="causal", sq=S, skv=S)), causal(S))
+    # Ascend mode 0: nextTokens = 0 and preTokens >= Sq is causal (diagonal included)
+    np.testing.assert_array_equal(dense(dict(family="band", sq=S, skv=S, pre=S, next=0)), causal(S))
+    np.testing.assert_array_equal(dense(dict(family="band", sq=S, skv=S, pre=10 ** 12, next=0)), causal(S))
+    assert dense(dict(family="band", sq=S, skv=S, pre=S, next=S)).all()
+    chain = np.arange(-1, 23, dtype=np.int32)  # parent[t] = t - 1
+    np.testing.assert_array_equal(
+        dense(dict(family="tree", sq=S, skv=S, tree_prefix=S - 24, tree_parent=chain)), causal(S))
+    sel = np.tile(np.arange(4, dtype=np.int32), (1, S, 1))
+    assert dense(dict(family="selected_key", sq=S, skv=100, sel=sel, sel_cells=32)).all()
+    st = np.full((1, 1, 1, 2), 2, dtype=np.uint8)
+    assert dense(dict(family="block_bitmap", sq=S, skv=100, blk_state=st,
+                      blk_index=np.full((1, 1, 1, 2), -1, np.int32),
+                      blk_bits=np.zeros((0, 64), np.uint64))).all()
+    raw = np.zeros((1, 1, 4, S), dtype=np.int32)
+    raw[0, 0, 1] = np.arange(S)       # UT = [0, j)
+    raw[0, 0, 2:] = S                 # LT empty
+    np.testing.assert_array_equal(dense(dict(family="intervals", sq=S, skv=S, raw_intervals=raw)), causal(S))
+    np.testing.assert_array_equal(dense(dict(family="causal_bottom_right", sq=S, skv=S)), causal(S))
+
+
+def test_family_definitions_small():
+    cu = np.array([0, 3, 5, 8], dtype=np.int32)  # segments [0,3) [3,5) [5,8)
+    seg = np.array([0, 0, 0, 1, 1, 2, 2, 2])
+    doc = seg[:, None] == seg[None, :]
+    np.testing.assert_array_equal(dense(dict(family="document", sq=8, skv=8, cu_seg=cu)), doc)
+    np.testing.assert_array_equal(dense(dict(family="causal_document", sq=8, skv=8, cu_seg=cu)), doc & causal(8))
+    sq_vis = causal(8) & (doc | (seg[None, :] == 0))
+    np.testing.assert_array_equal(dense(dict(family="shared_question", sq=8, skv=8, cu_seg=cu)), sq_vis)
+    # answers never see each other: row 6 (answer 2) sees the question and its own answer
+    assert dense(dict(family="shared_question", sq=8, skv=8, cu_seg=cu))[6].tolist() == [1, 1, 1, 0, 0, 1, 1, 0]
+    # tree: prefix 2, nodes 0..3 with parents -1, 0, 0, 1
+    t = dense(dict(family="tree", sq=6, skv=6, tree_prefix=2, tree_parent=np.array([-1, 0, 0, 1])))
+    exp = np.array([[1, 0, 0, 0, 0, 0],
+                    [1, 1, 0, 0, 0, 0],
+                    [1, 1, 1, 0, 0, 0],
+                    [1, 1, 1, 1, 0, 0],
+                    [1, 1, 1, 0, 1, 0],
+                    [1, 1, 1, 1, 0, 1]], dtype=bool)
+    np.testing.assert_array_equal(t, exp)
+    # bitmap: one PARTIAL block with a known word, force_diag adds (i, i)
+    bits = np.zeros((1, 64), dtype=np.uint64)
+    bits[0, 1] = np.uint64(0b1010)
+    st = np.array([[[[1]]]], dtype=np.uint8)
+    spec = dict(family="block_bitmap", sq=3, skv=5, blk_state=st,
+                blk_index=np.zeros((1, 1, 1, 1), np.int32), blk_bits=bits, force_diag=False)
+    assert dense(spec).astype(int).tolist() == [[0] * 5, [0, 1, 0, 1, 0], [0] * 5]
+    spec["force_diag"] = True
+    assert dense(spec).astype(int).tolist() == [[1, 0, 0, 0, 0], [0, 1, 0, 1, 0], [0, 0, 1, 0, 0]]
+
+
+def test_pair_counts_of_workloads():
+    # tiny causal document, documents 64/128/64: 64*65/2 + 128*129/2 + 64*65/2
+    w = synth.workload("tiny_causal_doc")
+    assert M.pair_count(w["mask"]) == 12416
+    # causal document at 8192: sum of L(L+1)/2 over the drawn documents
+    w = synth.workload("causal_doc_8k")
+    assert M.pair_count(w["mask"]) == sum(L * (L + 1) // 2 for L in w["doc_lengths"])
+    # band preTokens 9, nextTokens -3 at 4096: rows 0..2 empty, 3..8 see 1..6 keys, others 7
+    w = synth.workload("band_neg_4k")
+    vis = dense(w["mask"])
+    assert int(vis.sum()) == 28630
+    assert not vis[:3].any() and vis[3:].any(axis=1).all()
+    # band preTokens 4096, nextTokens 0 on a shorter sequence: closed form
+    S, pre = 6144, 4096
+    spec = dict(family="band", sq=S, skv=S, pre=pre, next=0)
+    assert M.pair_count(spec) == (pre + 1) * (pre + 2) // 2 - (pre + 1) + (S - pre) * (pre + 1)
+
+
+@pytest.mark.slow
+def test_pair_count_band_32k():
+    w = synth.workload("band_32k")
+    assert M.pair_count(w["mask"], chunk=1024) == 125_859_840
+
+
+def test_ascend_varlen_split_examples():
+    with open(os.path.join(GOLDEN, "ascend_varlen_split.json")) as f:
+        gold = json.load(f)
+    for case in gold["cases"]:
+        b = case["batch"]
+        qlen = np.diff([0] + case["actual_seq_qlen"])
+        kvlen = np.diff([0] + case["actual_seq_kvlen"])
+        sq, skv = int(qlen[b]), int(kvlen[b])
+        assert (sq, skv) == (case["sq"], case["skv"])
+        spec = dict(family=case["family"], sq=sq, skv=skv, pre=case.get("pre"), next=case.get("next"))
+        np.testing.assert_array_equal(dense(spec).astype(int), np.array(case["expected"]), err_msg=case["name"])
+
+
+def test_band_nonempty_condition_pins_inclusive_ends():
+    # Ascend sparseMode page: negative nextTokens needs preTokens >= |nextTokens|,
+    # negative preTokens needs nextTokens >= |preTokens|: exactly the condition for
+    # a non-empty band with both ends inclusive.
+    S = 64
+    for pre, nxt in [(3, -3), (2, -3), (9, -3), (-3, 7), (-3, 3), (-4, 3)]:
+        vis = dense(dict(family="band", sq=S, skv=S, pre=pre, next=nxt))
+        interior = vis[20:40]
+        nonempty = interior.any(axis=1).all()
+        assert nonempty == (pre + nxt >= 0), (pre, nxt)
+        if nonempty:
+            assert (interior.sum(axis=1) == pre + nxt + 1).all()
+
+
+# ---------------------------------------------------------------- encodings
+
+def _family_specs():
+    S = 200
+    cu = np.array([0, 64, 70, 150, 200], dtype=np.int32)
+    return [
+        dict(family="causal", sq=S, skv=S),
+        dict(family="causal_bottom_right", sq=150, skv=S),
+        dict(family="document", sq=S, skv=S, cu_seg=cu),
+        dict(family="causal_document", sq=S, skv=S, cu_seg=cu),
+        dict(family="shared_question", sq=S, skv=S, cu_seg=cu),
+        dict(family="band", sq=S, skv=S, pre=17, next=4),
+        dict(family="band", sq=S, skv=S, pre=9, next=-3),
+        dict(family="band", sq=S, skv=S, pre=-3, next=7),
+        dict(family="band", sq=120, skv=S, pre=30, next=0),
+        dict(family="tree", sq=S, skv=S, tree_prefix=S - 40,
+             tree_parent=synth.random_tree(np.random.default_rng(3), 40, order="dfs")),
+    ]
+
+
+def test_interval_round_trip_and_fast_path():
+    for spec in _family_specs():
+        vis = dense(spec)
+        iv = E.intervals_from_dense(vis)
+        np.testing.assert_array_equal(E.dense_from_intervals(iv, spec["sq"]), vis, err_msg=str(spec["family"]))
+        np.testing.assert_array_equal(E.intervals_from_dense_fast(vis), iv, err_msg=str(spec["family"]))
+        # canonical form: runs disjoint and non-abutting, UT starts at 0
+        assert (iv[0] == 0).all()
+        assert ((iv[1] < iv[2]) | (iv[2] == iv[3]) | (iv[0] == iv[1])).all()
+
+
+def test_bfs_tree_not_interval_representable():
+    spec = synth.workload("tree_4k", Sq=4096)["mask"]
+    vis = dense(spec)
+    with pytest.raises(E.NotRepresentable):
+        E.intervals_from_dense(vis[:, 4032:])
+    with pytest.raises(E.NotRepresentable):
+        E.intervals_from_dense_fast(vis)
+
+
+def test_closed_form_intervals():
+    S = 200
+    cu = np.array([0, 64, 70, 150, 200])
+    j = np.arange(S)
+    seg = np.searchsorted(cu, j, side="right") - 1
+    ds, de = cu[seg], cu[seg + 1]
+    # causal document: UT = [0, j), LT = [doc_end, S)
+    iv = E.intervals_from_dense(dense(dict(family="causal_document", sq=S, skv=S, cu_seg=cu)))
+    exp_ut_end = j
+    exp_lt = np.where(de < S, de, S)
+    np.testing.assert_array_equal(iv[1], exp_ut_end)
+    np.testing.assert_array_equal(iv[2], exp_lt)
+    np.testing.assert_array_equal(iv[3], np.full(S, S))
+    # document: UT = [0, doc_start) and LT = [doc_end, S) (one-run cases canonicalised)
+    iv = E.intervals_from_dense(dense(dict(family="document", sq=S, skv=S, cu_seg=cu)))
+    for c in range(S):
+        runs = []
+        if ds[c] > 0:
+            runs.append((0, ds[c]))
+        if de[c] < S:
+            runs.append((de[c], S))
+        assert tuple(iv[:, c]) == E.canonical_from_runs(runs, S)
+    # band next >= 0: UT = [0, max(0, j - next)), LT = [min(S, j + pre + 1), S)
+    pre, nxt = 17, 4
+    iv = E.intervals_from_dense(dense(dict(family="band", sq=S, skv=S, pre=pre, next=nxt)))
+    ut_end = np.maximum(0, j - nxt)
+    lt_start = np.minimum(S, j + pre + 1)
+    for c in range(S):
+        runs = ([(0, ut_end[c])] if ut_end[c] > 0 else []) + ([(lt_start[c], S)] if lt_start[c] < S else [])
+        assert tuple(iv[:, c]) == E.canonical_from_runs(runs, S)
+    # band pre = 9, next = -3: masked [0, min(S, j + 3)) and [min(S, j + 10), S)
+    iv = E.intervals_from_dense(dense(dict(family="band", sq=S, skv=S, pre=9, next=-3)))
+    np.testing.assert_array_equal(iv[1], np.minimum(S, j + 3))
+    lt = np.minimum(S, j + 10)
+    np.testing.assert_array_equal(iv[2], lt)
+
+
+def test_tile_states_closed_form_and_bruteforce():
+    S = 300
+    vis = causal(S)
+    for bm, bn in [(128, 64), (64, 64), (32, 48)]:
+        st = E.tile_states(vis, bm, bn)
+        nqt, nkt = st.shape
+        for qt in range(nqt):
+            r0, r1 = qt * bm, min(S, (qt + 1) * bm) - 1
+            for kt in range(nkt):
+                c0, c1 = kt * bn, min(S, (kt + 1) * bn) - 1
+                exp = 2 if c1 <= r0 else (0 if c0 > r1 else 1)
+                assert st[qt, kt] == exp
+        np.testing.assert_array_equal(E.tile_states_fast(vis, bm, bn), st)
+    rng = np.random.default_rng(9)
+    for _ in range(5):
+        sq, skv = rng.integers(1, 90, 2)
+        v = rng.random((sq, skv)) < rng.random()
+        st = E.tile_states(v, 16, 32)
+        for qt in range(st.shape[0]):
+            for kt in range(st.shape[1]):
+                cells = [v[i, j] for i in range(qt * 16, min(sq, qt * 16 + 16))
+                         for j in range(kt * 32, min(skv, kt * 32 + 32))]
+                exp = 2 if all(cells) else (1 if any(cells) else 0)
+                assert st[qt, kt] == exp
+        np.testing.assert_array_equal(E.tile_states_fast(v, 16, 32), st)
+
+
+def test_tile_lists_and_order():
+    st = np.array([[0, 2, 1, 0], [0, 0, 0, 0], [2, 2, 2, 1], [1, 0, 0, 2]], dtype=np.uint8)
+    lists, counts = E.tile_lists(st)
+    assert counts.tolist() == [2, 0, 4, 2]
+    full = 1 << 31
+    assert (lists[0, :2].view(np.uint32).tolist() == [1 | full, 2])
+    assert (lists[2].view(np.uint32).tolist() == [0 | full, 1 | full, 2 | full, 3])
+    assert (lists[3, :2].view(np.uint32).tolist() == [0, 3 | full])
+    assert E.tile_order(counts).tolist() == [2, 0, 3, 1]
+
+
+def test_bitmap_round_trip():
+    rng = np.random.default_rng(11)
+    for sq, skv in [(130, 200), (64, 64), (1, 70)]:
+        vis = rng.random((sq, skv)) < 0.2
+        vis[:40, :40] = True
+        vis[:, 128:192] = False
+        st, ix, pool = E.bitmap_from_dense(vis)
+        spec = dict(family="block_bitmap", sq=sq, skv=skv, blk_state=st[None, None],
+                    blk_index=ix[None, None], blk_bits=np.array(pool, dtype=np.uint64).reshape(-1, 64))
+        np.testing.assert_array_equal(dense(spec), vis)
+        # pool entries in row-major order, partial blocks only
+        order = [tuple(x) for x in np.argwhere(st == 1)]
+        assert [int(ix[b]) for b in order] == list(range(len(pool)))
+
+
+def test_canonical_lists():
+    sel = np.array([[[5, -1, 3, 5, 9, 3], [-1, -1, -1, -1, -1, -1], [0, 8, 7, 7, 1, 2]]], dtype=np.int32)
+    lists, counts = E.canonical_lists(sel, nblk=8)
+    assert lists[0, 0].tolist() == [3, 5, -1, -1, -1, -1]
+    assert lists[0, 1].tolist() == [-1] * 6 and counts[0, 1] == 0
+    assert lists[0, 2].tolist() == [0, 1, 2, 7, -1, -1] and counts[0, 2] == 4

@@ -1,0 +1,512 @@
+// libfmask C ABI: argument checking, buffer layout and kernel launches.
+// Every host-detectable error is reported before anything is launched; the
+// library never allocates, frees or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "internal.h"
+
+using namespace fmask;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fmask_status fail(fmask_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+fmask_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return FMASK_OK;
+  return fail(FMASK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxSeq = (int64_t)1 << 30;
+constexpr int32_t kMaxTree = 4096;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+bool is_segment_family(int f) {
+  return f == FMASK_DOCUMENT || f == FMASK_CAUSAL_DOCUMENT || f == FMASK_SHARED_QUESTION;
+}
+
+bool is_param_family(int f) {
+  return f == FMASK_CAUSAL || f == FMASK_CAUSAL_BOTTOM_RIGHT || f == FMASK_BAND || f == FMASK_TREE ||
+         is_segment_family(f);
+}
+
+// Tree analysis on the host copy of the parent array: validity, and whether
+// every subtree is a contiguous node range (then the interval form holds).
+fmask_status tree_check(const fmask_mask_desc* d, bool* contiguous) {
+  const int n = d->tree_n;
+  std::vector<int> size(n, 0), hi(n, 0);
+  for (int t = 0; t < n; ++t) {
+    int p = d->tree_parent[t];
+    if (p < -1 || p >= t) return fail(FMASK_ERR_INVALID, "tree_parent[%d] = %d is not in [-1, %d)", t, p, t);
+  }
+  for (int t = 0; t < n; ++t) {
+    for (int a = t; a >= 0; a = d->tree_parent[a]) {
+      size[a] += 1;
+      hi[a] = std::max(hi[a], t);
+    }
+  }
+  bool ok = true;
+  for (int c = 0; c < n && ok; ++c) ok = size[c] == hi[c] - c + 1;
+  *contiguous = ok;
+  return FMASK_OK;
+}
+
+fmask_status check_desc(const fmask_mask_desc* d, int* kind) {
+  if (!d) return fail(FMASK_ERR_INVALID, "null mask descriptor");
+  if (d->sq < 0 || d->skv < 0 || d->sq > kMaxSeq || d->skv > kMaxSeq)
+    return fail(FMASK_ERR_INVALID, "sq / skv out of range [0, 2^30]");
+  if (d->batch < 1 || d->heads < 1) return fail(FMASK_ERR_INVALID, "batch and heads must be >= 1");
+  const int f = d->family;
+  if (is_param_family(f) && (d->batch != 1 || d->heads != 1))
+    return fail(FMASK_ERR_INVALID, "family %d describes one mask: batch = heads = 1", f);
+  switch (f) {
+    case FMASK_CAUSAL:
+    case FMASK_CAUSAL_BOTTOM_RIGHT:
+    case FMASK_BAND:
+      *kind = FMASK_ENC_INTERVALS;
+      return FMASK_OK;
+    case FMASK_DOCUMENT:
+    case FMASK_CAUSAL_DOCUMENT:
+    case FMASK_SHARED_QUESTION: {
+      if (d->sq != d->skv) return fail(FMASK_ERR_INVALID, "segment families need sq == skv");
+      if (!d->cu_seg || d->n_seg < 1) return fail(FMASK_ERR_INVALID, "cu_seg missing or n_seg < 1");
+      if (d->cu_seg[0] != 0) return fail(FMASK_ERR_INVALID, "cu_seg[0] must be 0");
+      for (int s = 0; s < d->n_seg; ++s)
+        if (d->cu_seg[s + 1] <= d->cu_seg[s])
+          return fail(FMASK_ERR_INVALID, "cu_seg not strictly increasing at %d", s);
+      if (d->cu_seg[d->n_seg] != d->sq) return fail(FMASK_ERR_INVALID, "cu_seg[n_seg] != sq");
+      *kind = FMASK_ENC_INTERVALS;
+      return FMASK_OK;
+    }
+    case FMASK_TREE: {
+      if (d->tree_n < 0 || d->tree_n > kMaxTree || d->tree_prefix < 0)
+        return fail(FMASK_ERR_INVALID, "tree_n must be in [0, %d], tree_prefix >= 0", kMaxTree);
+      if (d->sq != d->skv || d->sq != (int64_t)d->tree_prefix + d->tree_n)
+        return fail(FMASK_ERR_INVALID, "tree needs sq == skv == tree_prefix + tree_n");
+      if (d->tree_n > 0 && !d->tree_parent) return fail(FMASK_ERR_INVALID, "tree_parent missing");
+      bool contiguous = true;
+      fmask_status st = tree_check(d, &contiguous);
+      if (st != FMASK_OK) return st;
+      *kind = contiguous ? FMASK_ENC_INTERVALS : FMASK_ENC_BITMAP;
+      return FMASK_OK;
+    }
+    case FMASK_BLOCK_BITMAP:
+      if ((d->sq > 0 && d->skv > 0) && (!d->blk_state || !d->blk_index))
+        return fail(FMASK_ERR_INVALID, "blk_state / blk_index missing");
+      if (d->blk_pool_n < 0 || (d->blk_pool_n > 0 && !d->blk_bits))
+        return fail(FMASK_ERR_INVALID, "blk_bits missing or blk_pool_n < 0");
+      *kind = FMASK_ENC_BITMAP;
+      return FMASK_OK;
+    case FMASK_SELECTED_KEY:
+      if (d->heads != 1) return fail(FMASK_ERR_INVALID, "selected-key lists are shared by all heads");
+      if (d->sel_n < 1 || d->sel_n > FMASK_MAX_SEL_N)
+        return fail(FMASK_ERR_INVALID, "sel_n must be in [1, %d]", FMASK_MAX_SEL_N);
+      if (d->sel_cells < 1) return fail(FMASK_ERR_INVALID, "sel_cells must be >= 1");
+      if (d->sq > 0 && !d->sel) return fail(FMASK_ERR_INVALID, "sel missing");
+      *kind = FMASK_ENC_SELECTED;
+      return FMASK_OK;
+    case FMASK_INTERVALS:
+      if (d->sq > 0 && d->skv > 0 && !d->raw_intervals)
+        return fail(FMASK_ERR_INVALID, "raw_intervals missing");
+      *kind = FMASK_ENC_INTERVALS;
+      return FMASK_OK;
+    default:
+      return fail(FMASK_ERR_INVALID, "unknown mask family %d", f);
+  }
+}
+
+struct EncLayout {
+  int kind = 0;
+  size_t total = 0;
+  size_t iv = 0, cu = 0, parent = 0, tree_hi = 0;
+  size_t bstate = 0, bindex = 0, bbits = 0, row_count = 0, row_offset = 0, pool_count = 0;
+  size_t list = 0, count = 0;
+  int64_t nbq = 0, nbk = 0, cap = 0;
+};
+
+EncLayout enc_layout(const fmask_mask_desc* d, int kind) {
+  EncLayout L;
+  L.kind = kind;
+  Carve c;
+  const int64_t nmask = (int64_t)d->batch * d->heads;
+  if (kind == FMASK_ENC_INTERVALS) {
+    L.iv = c.take((size_t)nmask * 4 * d->skv * sizeof(int32_t));
+    if (is_segment_family(d->family)) L.cu = c.take((size_t)(d->n_seg + 1) * sizeof(int32_t));
+    if (d->family == FMASK_TREE) {
+      L.parent = c.take((size_t)std::max(1, d->tree_n) * sizeof(int32_t));
+      L.tree_hi = c.take((size_t)std::max(1, d->tree_n) * sizeof(int32_t));
+    }
+  } else if (kind == FMASK_ENC_BITMAP) {
+    L.nbq = ceil_div(d->sq, kBlk);
+    L.nbk = ceil_div(d->skv, kBlk);
+    const int64_t nblocks = nmask * L.nbq * L.nbk;
+    // Worst case: every block PARTIAL (the canonical pool is compact, this
+    // only reserves room; no dense mask is ever written).
+    L.cap = nblocks;
+    L.bstate = c.take((size_t)nblocks);
+    L.bindex = c.take((size_t)nblocks * sizeof(int32_t));
+    L.bbits = c.take((size_t)L.cap * kBlk * sizeof(uint64_t));
+    L.row_count = c.take((size_t)std::max<int64_t>(1, nmask * L.nbq) * sizeof(int32_t));
+    L.row_offset = c.take((size_t)std::max<int64_t>(1, nmask * L.nbq) * sizeof(int32_t));
+    L.pool_count = c.take(sizeof(int32_t));
+    if (d->family == FMASK_TREE) L.parent = c.take((size_t)std::max(1, d->tree_n) * sizeof(int32_t));
+  } else {
+    L.list = c.take((size_t)d->batch * d->sq * d->sel_n * sizeof(int32_t));
+    L.count = c.take((size_t)d->batch * d->sq * sizeof(int32_t));
+  }
+  L.total = std::max<size_t>(c.off, kAlign);
+  return L;
+}
+
+template <class T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+struct TileLayout {
+  size_t state = 0, list = 0, count = 0, order = 0, total = 0;
+  int64_t nqt = 0, nkt = 0, rows = 0;
+};
+
+fmask_status check_tiles_args(const fmask_encoded* e, int32_t bm, int32_t bn) {
+  if (!e) return fail(FMASK_ERR_INVALID, "null encoding");
+  if (e->kind != FMASK_ENC_INTERVALS && e->kind != FMASK_ENC_BITMAP)
+    return fail(FMASK_ERR_INVALID, "tile tables exist for the INTERVALS and BITMAP kinds only");
+  if (bm < 16 || bm > 256 || bn < 16 || bn > 256 || bm % 16 || bn % 16)
+    return fail(FMASK_ERR_INVALID, "bm, bn must be multiples of 16 in [16, 256]");
+  if (e->kind == FMASK_ENC_BITMAP && (bm % kBlk || bn % kBlk))
+    return fail(FMASK_ERR_INVALID, "BITMAP tiles must be multiples of 64");
+  if (e->batch < 1 || e->heads < 1 || e->sq < 0 || e->skv < 0 || e->sq > kMaxSeq || e->skv > kMaxSeq)
+    return fail(FMASK_ERR_INVALID, "malformed encoding");
+  return FMASK_OK;
+}
+
+TileLayout tile_layout(const fmask_encoded* e, int32_t bm, int32_t bn) {
+  TileLayout T;
+  Carve c;
+  T.nqt = ceil_div(e->sq, bm);
+  T.nkt = ceil_div(e->skv, bn);
+  T.rows = (int64_t)e->batch * e->heads * T.nqt;
+  T.state = c.take((size_t)T.rows * T.nkt);
+  T.list = c.take((size_t)T.rows * T.nkt * sizeof(int32_t));
+  T.count = c.take((size_t)T.rows * sizeof(int32_t));
+  T.order = c.take((size_t)T.rows * sizeof(int32_t));
+  T.total = std::max<size_t>(c.off, kAlign);
+  return T;
+}
+
+void preferred(int32_t dtype, int32_t d, int32_t kind, int32_t* bm, int32_t* bn) {
+  (void)d;
+  *bn = 64;
+  if (dtype == FMASK_F32) *bm = 64;
+  else *bm = (kind == FMASK_ENC_BITMAP) ? 64 : 128;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fmask_status_str(fmask_status s) {
+  switch (s) {
+    case FMASK_OK: return "ok";
+    case FMASK_ERR_INVALID: return "invalid argument";
+    case FMASK_ERR_UNSUPPORTED: return "unsupported combination";
+    case FMASK_ERR_CAPACITY: return "buffer too small";
+    case FMASK_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* fmask_last_error(void) { return g_err; }
+
+fmask_status fmask_preferred_tile(int32_t dtype, int32_t d, int32_t kind, int32_t* bm, int32_t* bn) {
+  if (!bm || !bn) return fail(FMASK_ERR_INVALID, "null output pointer");
+  if (kind != FMASK_ENC_INTERVALS && kind != FMASK_ENC_BITMAP)
+    return fail(FMASK_ERR_INVALID, "tiles exist for the INTERVALS and BITMAP kinds only");
+  if ((dtype != FMASK_BF16 && dtype != FMASK_F32) || (d != 64 && d != 128))
+    return fail(FMASK_ERR_UNSUPPORTED, "no tile kernel for dtype %d, d %d", dtype, d);
+  preferred(dtype, d, kind, bm, bn);
+  return FMASK_OK;
+}
+
+size_t fmask_encode_bytes(const fmask_mask_desc* desc) {
+  int kind = 0;
+  if (check_desc(desc, &kind) != FMASK_OK) return 0;
+  return enc_layout(desc, kind).total;
+}
+
+fmask_status fmask_encode(const fmask_mask_desc* desc, void* out, size_t out_bytes, fmask_encoded* enc,
+                          void* stream) {
+  g_err[0] = 0;
+  int kind = 0;
+  fmask_status st = check_desc(desc, &kind);
+  if (st != FMASK_OK) return st;
+  if (!enc) return fail(FMASK_ERR_INVALID, "null fmask_encoded");
+  if (!out || ((uintptr_t)out % kAlign)) return fail(FMASK_ERR_INVALID, "out must be 256-byte aligned");
+  const EncLayout L = enc_layout(desc, kind);
+  if (out_bytes < L.total)
+    return fail(FMASK_ERR_CAPACITY, "out has %zu bytes, %zu needed", out_bytes, L.total);
+  hipStream_t s = (hipStream_t)stream;
+  const int f = desc->family;
+  const int32_t sq = (int32_t)desc->sq, skv = (int32_t)desc->skv;
+  const int32_t nmask = desc->batch * desc->heads;
+
+  memset(enc, 0, sizeof(*enc));
+  enc->kind = kind;
+  enc->batch = desc->batch;
+  enc->heads = desc->heads;
+  enc->sq = desc->sq;
+  enc->skv = desc->skv;
+
+  hipError_t e = hipSuccess;
+  if (kind == FMASK_ENC_INTERVALS) {
+    int32_t* iv = at<int32_t>(out, L.iv);
+    enc->intervals = iv;
+    if (f == FMASK_INTERVALS) {
+      e = launch_encode_raw_intervals(desc->raw_intervals, nmask, sq, skv, iv, s);
+    } else {
+      SegParams p{};
+      p.family = f;
+      p.sq = sq;
+      p.skv = skv;
+      int64_t lim = (int64_t)sq + skv + 1;
+      p.pre = std::min(std::max(desc->pre_tokens, -lim), lim);
+      p.next = std::min(std::max(desc->next_tokens, -lim), lim);
+      if (is_segment_family(f)) {
+        int32_t* cu = at<int32_t>(out, L.cu);
+        e = hipMemcpyAsync(cu, desc->cu_seg, (size_t)(desc->n_seg + 1) * sizeof(int32_t),
+                           hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_status(e, "copy cu_seg");
+        p.cu = cu;
+        p.n_seg = desc->n_seg;
+      }
+      if (f == FMASK_TREE) {
+        int32_t* par = at<int32_t>(out, L.parent);
+        int32_t* hi = at<int32_t>(out, L.tree_hi);
+        p.tree_prefix = desc->tree_prefix;
+        p.tree_hi = hi;
+        if (desc->tree_n > 0) {
+          e = hipMemcpyAsync(par, desc->tree_parent, (size_t)desc->tree_n * sizeof(int32_t),
+                             hipMemcpyHostToDevice, s);
+          if (e != hipSuccess) return hip_status(e, "copy tree_parent");
+          e = launch_tree_hi(par, desc->tree_n, hi, s);
+          if (e != hipSuccess) return hip_status(e, "tree kernel");
+        }
+      }
+      e = launch_encode_family_intervals(p, iv, s);
+    }
+    return hip_status(e, "encode kernel");
+  }
+  if (kind == FMASK_ENC_BITMAP) {
+    BitmapSrc src{};
+    src.nmask = nmask;
+    src.nbq = (int32_t)L.nbq;
+    src.nbk = (int32_t)L.nbk;
+    src.sq = sq;
+    src.skv = skv;
+    if (f == FMASK_TREE) {
+      src.kind = 1;
+      src.tree_prefix = desc->tree_prefix;
+      src.tree_n = desc->tree_n;
+      int32_t* par = at<int32_t>(out, L.parent);
+      if (desc->tree_n > 0) {
+        e = hipMemcpyAsync(par, desc->tree_parent, (size_t)desc->tree_n * sizeof(int32_t),
+                           hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_status(e, "copy tree_parent");
+      }
+      src.parent = par;
+    } else {
+      src.kind = 0;
+      src.state = desc->blk_state;
+      src.index = desc->blk_index;
+      src.bits = desc->blk_bits;
+      src.pool_n = desc->blk_pool_n;
+      src.force_diag = desc->force_diag != 0;
+    }
+    BitmapOut o{};
+    o.state = at<uint8_t>(out, L.bstate);
+    o.index = at<int32_t>(out, L.bindex);
+    o.bits = at<uint64_t>(out, L.bbits);
+    o.cap = L.cap;
+    o.row_count = at<int32_t>(out, L.row_count);
+    o.row_offset = at<int32_t>(out, L.row_offset);
+    o.pool_count = at<int32_t>(out, L.pool_count);
+    enc->blk = kBlk;
+    enc->blk_state = o.state;
+    enc->blk_index = o.index;
+    enc->blk_bits = o.bits;
+    enc->blk_pool_count = o.pool_count;
+    enc->nbq = L.nbq;
+    enc->nbk = L.nbk;
+    enc->pool_cap = L.cap;
+    if (L.nbq * L.nbk == 0) {
+      e = hipMemsetAsync(o.pool_count, 0, sizeof(int32_t), s);
+      return hip_status(e, "clear pool count");
+    }
+    e = launch_encode_bitmap(src, o, s);
+    return hip_status(e, "bitmap encode kernels");
+  }
+  // SELECTED
+  int32_t* list = at<int32_t>(out, L.list);
+  int32_t* count = at<int32_t>(out, L.count);
+  const int64_t nblk = ceil_div(desc->skv, desc->sel_cells);
+  enc->blk = desc->sel_cells;
+  enc->sel_list = list;
+  enc->sel_count = count;
+  enc->sel_n = desc->sel_n;
+  e = launch_encode_selected(desc->sel, desc->batch, sq, desc->sel_n, (int32_t)nblk, list, count, s);
+  return hip_status(e, "selected-key encode kernel");
+}
+
+size_t fmask_classify_bytes(const fmask_encoded* enc, int32_t bm, int32_t bn) {
+  if (check_tiles_args(enc, bm, bn) != FMASK_OK) return 0;
+  return tile_layout(enc, bm, bn).total;
+}
+
+fmask_status fmask_classify(const fmask_encoded* enc, int32_t bm, int32_t bn, void* out, size_t out_bytes,
+                            fmask_tiles* tiles, void* stream) {
+  g_err[0] = 0;
+  fmask_status st = check_tiles_args(enc, bm, bn);
+  if (st != FMASK_OK) return st;
+  if (!tiles) return fail(FMASK_ERR_INVALID, "null fmask_tiles");
+  if (!out || ((uintptr_t)out % kAlign)) return fail(FMASK_ERR_INVALID, "out must be 256-byte aligned");
+  const TileLayout T = tile_layout(enc, bm, bn);
+  if (out_bytes < T.total) return fail(FMASK_ERR_CAPACITY, "out has %zu bytes, %zu needed", out_bytes, T.total);
+  if (T.rows > INT32_MAX || T.rows * T.nkt > ((int64_t)1 << 40))
+    return fail(FMASK_ERR_UNSUPPORTED, "tile table too large");
+  hipStream_t s = (hipStream_t)stream;
+  memset(tiles, 0, sizeof(*tiles));
+  tiles->bm = bm;
+  tiles->bn = bn;
+  tiles->nqt = (int32_t)T.nqt;
+  tiles->nkt = (int32_t)T.nkt;
+  tiles->batch = enc->batch;
+  tiles->heads = enc->heads;
+  uint8_t* state = at<uint8_t>(out, T.state);
+  int32_t* list = at<int32_t>(out, T.list);
+  int32_t* count = at<int32_t>(out, T.count);
+  int32_t* order = at<int32_t>(out, T.order);
+  tiles->state = state;
+  tiles->list = list;
+  tiles->count = count;
+  tiles->order = order;
+  const int32_t nmask = enc->batch * enc->heads;
+  hipError_t e;
+  if (enc->kind == FMASK_ENC_INTERVALS)
+    e = launch_classify_intervals(enc->intervals, nmask, (int32_t)enc->sq, (int32_t)enc->skv, bm, bn,
+                                  (int32_t)T.nqt, (int32_t)T.nkt, state, s);
+  else
+    e = launch_classify_bitmap(enc->blk_state, nmask, (int32_t)enc->nbq, (int32_t)enc->nbk, bm, bn,
+                               (int32_t)T.nqt, (int32_t)T.nkt, state, s);
+  if (e != hipSuccess) return hip_status(e, "classify kernel");
+  e = launch_tile_lists(state, (int32_t)T.rows, (int32_t)T.nkt, list, count, s);
+  if (e != hipSuccess) return hip_status(e, "tile list kernel");
+  e = launch_tile_order(count, (int32_t)T.rows, order, s);
+  return hip_status(e, "tile order kernel");
+}
+
+fmask_status fmask_attn_fwd(const fmask_attn_args* a, const void* q, const void* k, const void* v, void* o,
+                            float* lse, const fmask_encoded* enc, const fmask_tiles* tiles, void* stream) {
+  g_err[0] = 0;
+  if (!a || !enc) return fail(FMASK_ERR_INVALID, "null args or encoding");
+  if (a->dtype != FMASK_BF16 && a->dtype != FMASK_F32) return fail(FMASK_ERR_UNSUPPORTED, "dtype %d", a->dtype);
+  if (a->b < 1 || a->hq < 1 || a->hkv < 1 || a->hq % a->hkv)
+    return fail(FMASK_ERR_INVALID, "need b, hq, hkv >= 1 and hq %% hkv == 0");
+  if (a->sq < 0 || a->skv < 0 || a->sq > kMaxSeq || a->skv > kMaxSeq)
+    return fail(FMASK_ERR_INVALID, "sq / skv out of range");
+  if (a->sq != enc->sq || a->skv != enc->skv) return fail(FMASK_ERR_INVALID, "sq / skv differ from the encoding");
+  if (!(enc->batch == 1 || enc->batch == a->b)) return fail(FMASK_ERR_INVALID, "encoding batch must be 1 or b");
+  if (!(enc->heads == 1 || enc->heads == a->hq)) return fail(FMASK_ERR_INVALID, "encoding heads must be 1 or hq");
+  if (!q || !k || !v || !o) return fail(FMASK_ERR_INVALID, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(FMASK_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
+  const int64_t vec = a->dtype == FMASK_BF16 ? 8 : 4;
+  for (int i = 0; i < 3; ++i) {
+    if (a->q_stride[i] % vec || a->k_stride[i] % vec || a->v_stride[i] % vec || a->o_stride[i] % vec)
+      return fail(FMASK_ERR_UNSUPPORTED, "strides must be multiples of %lld elements", (long long)vec);
+    if (a->q_stride[i] < 0 || a->k_stride[i] < 0 || a->v_stride[i] < 0 || a->o_stride[i] < 0)
+      return fail(FMASK_ERR_INVALID, "negative stride");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const int32_t group = a->hq / a->hkv;
+
+  if (enc->kind == FMASK_ENC_SELECTED) {
+    if (a->dtype != FMASK_BF16 || (a->d != 256 && a->d != 128) || enc->blk != 32 ||
+        !(group == 1 || group == 2 || group == 4 || group == 8 || group == 16))
+      return fail(FMASK_ERR_UNSUPPORTED, "selected-key kernel: bf16, d in {128, 256}, 32-cell blocks, "
+                                         "hq/hkv in {1,2,4,8,16}");
+    if (enc->heads != 1) return fail(FMASK_ERR_INVALID, "selected-key lists are shared by all heads");
+    SelAttnParams p{};
+    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+    memcpy(p.qs, a->q_stride, sizeof(p.qs));
+    memcpy(p.ks, a->k_stride, sizeof(p.ks));
+    memcpy(p.vs, a->v_stride, sizeof(p.vs));
+    memcpy(p.os, a->o_stride, sizeof(p.os));
+    p.b = a->b; p.hq = a->hq; p.hkv = a->hkv; p.group = group;
+    p.sq = (int32_t)a->sq; p.skv = (int32_t)a->skv; p.scale = a->scale;
+    p.list = enc->sel_list; p.count = enc->sel_count;
+    p.n = enc->sel_n; p.cells = enc->blk; p.mb = enc->batch;
+    if ((int64_t)a->hkv * a->b * a->sq > INT32_MAX) return fail(FMASK_ERR_UNSUPPORTED, "grid too large");
+    return hip_status(launch_attn_selected_bf16(p, a->d, s), "selected-key attention kernel");
+  }
+
+  if (!tiles) return fail(FMASK_ERR_INVALID, "tile table required for this encoding");
+  int32_t bm = 0, bn = 0;
+  if ((a->dtype != FMASK_BF16 && a->dtype != FMASK_F32) || (a->d != 64 && a->d != 128))
+    return fail(FMASK_ERR_UNSUPPORTED, "tile kernels: d in {64, 128}");
+  preferred(a->dtype, a->d, enc->kind, &bm, &bn);
+  if (tiles->bm != bm || tiles->bn != bn)
+    return fail(FMASK_ERR_UNSUPPORTED, "tile table is %dx%d, the kernel needs %dx%d", tiles->bm, tiles->bn, bm, bn);
+  if (tiles->nqt != ceil_div(a->sq, bm) || tiles->nkt != ceil_div(a->skv, bn) ||
+      tiles->batch != enc->batch || tiles->heads != enc->heads)
+    return fail(FMASK_ERR_INVALID, "tile table does not match the encoding");
+  TileAttnParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  memcpy(p.qs, a->q_stride, sizeof(p.qs));
+  memcpy(p.ks, a->k_stride, sizeof(p.ks));
+  memcpy(p.vs, a->v_stride, sizeof(p.vs));
+  memcpy(p.os, a->o_stride, sizeof(p.os));
+  p.b = a->b; p.hq = a->hq; p.hkv = a->hkv; p.group = group;
+  p.sq = (int32_t)a->sq; p.skv = (int32_t)a->skv; p.scale = a->scale;
+  p.list = tiles->list; p.count = tiles->count; p.order = tiles->order;
+  p.nqt = tiles->nqt; p.nkt = tiles->nkt; p.bm = bm; p.bn = bn;
+  p.mb = enc->batch; p.mh = enc->heads;
+  p.expand = (enc->batch == 1 ? a->b : 1) * (enc->heads == 1 ? a->hq : 1);
+  const int64_t items = (int64_t)enc->batch * enc->heads * tiles->nqt * p.expand;
+  if (items > INT32_MAX / 2) return fail(FMASK_ERR_UNSUPPORTED, "grid too large");
+  p.n_items = (int32_t)items;
+  p.kind = enc->kind;
+  p.iv = enc->intervals;
+  p.bstate = enc->blk_state; p.bindex = enc->blk_index; p.bbits = enc->blk_bits;
+  p.nbq = (int32_t)enc->nbq; p.nbk = (int32_t)enc->nbk;
+  if (a->sq == 0) return FMASK_OK;
+  hipError_t e = a->dtype == FMASK_BF16 ? launch_attn_tile_bf16(p, a->d, s) : launch_attn_tile_f32(p, a->d, s);
+  return hip_status(e, "attention kernel");
+}
+
+}  // extern "C"

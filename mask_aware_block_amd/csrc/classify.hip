@@ -1,0 +1,165 @@
+// Tile classifier: canonical encoding -> exact SKIP / PARTIAL / FULL state of
+// every bm x bn tile, compact per-row lists of the tiles to compute, and a
+// longest-first order of tile rows.
+//
+// The skip / full / partial split is what lets the attention kernel avoid the
+// cost the FlashMask rebuttal page points at in a token-by-token dense mask:
+// fully masked tiles are never loaded and fully visible tiles need no mask.
+//
+// Exactness on the interval form: canonical runs are disjoint, so the number
+// of masked rows of column j inside [r0, r1) is |[r0,r1) & UT_j| + |[r0,r1) &
+// LT_j|.  A tile is SKIP iff that equals r1 - r0 for every column, FULL iff it
+// is 0 for every column.
+#include "internal.h"
+
+namespace fmask {
+namespace {
+
+__device__ inline int32_t overlap(int32_t r0, int32_t r1, int32_t a, int32_t b) {
+  int32_t lo = max(r0, a), hi = min(r1, b);
+  return hi > lo ? hi - lo : 0;
+}
+
+// One thread per tile; threads of a workgroup share kt and read the same columns.
+__global__ void __launch_bounds__(256) k_classify_intervals(const int32_t* iv, int32_t nmask,
+                                                            int32_t sq, int32_t skv, int32_t bm,
+                                                            int32_t bn, int32_t nqt, int32_t nkt,
+                                                            uint8_t* state) {
+  int64_t total = (int64_t)nmask * nqt * nkt;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    int32_t qt = (int32_t)(t % nqt);
+    int32_t kt = (int32_t)((t / nqt) % nkt);
+    int64_t m = t / ((int64_t)nqt * nkt);
+    int32_t r0 = qt * bm, r1 = min(sq, r0 + bm);
+    int32_t c0 = kt * bn, c1 = min(skv, c0 + bn);
+    const int32_t* col = iv + m * 4 * (int64_t)skv;
+    bool all_masked = true, none_masked = true;
+    for (int32_t j = c0; j < c1 && (all_masked || none_masked); ++j) {
+      int32_t mc = overlap(r0, r1, col[j], col[skv + j]) +
+                   overlap(r0, r1, col[2 * (int64_t)skv + j], col[3 * (int64_t)skv + j]);
+      all_masked = all_masked && mc == r1 - r0;
+      none_masked = none_masked && mc == 0;
+    }
+    uint8_t st = all_masked ? FMASK_SKIP : (none_masked ? FMASK_FULL : FMASK_PARTIAL);
+    state[(m * nqt + qt) * (int64_t)nkt + kt] = st;
+  }
+}
+
+// Bitmap form, tiles made of whole 64 x 64 blocks: combine the exact block states.
+__global__ void __launch_bounds__(256) k_classify_bitmap(const uint8_t* bstate, int32_t nmask,
+                                                         int32_t nbq, int32_t nbk, int32_t bm,
+                                                         int32_t bn, int32_t nqt, int32_t nkt,
+                                                         uint8_t* state) {
+  int64_t total = (int64_t)nmask * nqt * nkt;
+  int rb = bm / kBlk, cb = bn / kBlk;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    int32_t kt = (int32_t)(t % nkt);
+    int32_t qt = (int32_t)((t / nkt) % nqt);
+    int64_t m = t / ((int64_t)nqt * nkt);
+    bool all_skip = true, all_full = true;
+    for (int i = 0; i < rb; ++i) {
+      int bi = qt * rb + i;
+      if (bi >= nbq) break;
+      for (int j = 0; j < cb; ++j) {
+        int bj = kt * cb + j;
+        if (bj >= nbk) break;
+        uint8_t s = bstate[(m * nbq + bi) * (int64_t)nbk + bj];
+        all_skip = all_skip && s == FMASK_SKIP;
+        all_full = all_full && s == FMASK_FULL;
+      }
+    }
+    state[t] = all_skip ? FMASK_SKIP : (all_full ? FMASK_FULL : FMASK_PARTIAL);
+  }
+}
+
+// One wave per tile row: stream compaction of the non-SKIP tiles.
+__global__ void __launch_bounds__(256) k_tile_lists(const uint8_t* state, int32_t rows, int32_t nkt,
+                                                    int32_t* list, int32_t* count) {
+  int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const uint8_t* st = state + (int64_t)row * nkt;
+  int32_t* out = list + (int64_t)row * nkt;
+  int running = 0;
+  for (int base = 0; base < nkt; base += 64) {
+    int kt = base + lane;
+    uint8_t s = kt < nkt ? st[kt] : (uint8_t)FMASK_SKIP;
+    bool keep = s != FMASK_SKIP;
+    uint64_t bal = __ballot(keep);
+    int rank = running + __popcll(bal & ((1ull << lane) - 1ull));
+    if (keep) out[rank] = (int32_t)((uint32_t)kt | (s == FMASK_FULL ? FMASK_LIST_FULL_BIT : 0u));
+    running += __popcll(bal);
+  }
+  for (int i = running + lane; i < nkt; i += 64) out[i] = 0;
+  if (lane == 0) count[row] = running;
+}
+
+// Rank of every tile row under (count descending, index ascending); the rank
+// is unique, so order[rank] = row is a permutation.
+__global__ void __launch_bounds__(256) k_tile_order(const int32_t* count, int32_t rows,
+                                                    int32_t* order) {
+  __shared__ int32_t chunk[1024];
+  int x = blockIdx.x * blockDim.x + threadIdx.x;
+  int32_t cx = x < rows ? count[x] : 0;
+  int rank = 0;
+  for (int base = 0; base < rows; base += 1024) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < 1024; i += blockDim.x)
+      chunk[i] = base + i < rows ? count[base + i] : -1;
+    __syncthreads();
+    int lim = min(1024, rows - base);
+    for (int i = 0; i < lim; ++i) {
+      int32_t cy = chunk[i];
+      int y = base + i;
+      rank += (cy > cx) || (cy == cx && y < x);
+    }
+  }
+  if (x < rows) order[rank] = x;
+}
+
+inline int grid_for(int64_t n, int per_block, int cap = 65535 * 16) {
+  int64_t g = (n + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_classify_intervals(const int32_t* iv, int32_t nmask, int32_t sq, int32_t skv,
+                                     int32_t bm, int32_t bn, int32_t nqt, int32_t nkt,
+                                     uint8_t* state, hipStream_t s) {
+  int64_t total = (int64_t)nmask * nqt * nkt;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_classify_intervals, dim3(grid_for(total, 256)), dim3(256), 0, s, iv, nmask,
+                     sq, skv, bm, bn, nqt, nkt, state);
+  return hipGetLastError();
+}
+
+hipError_t launch_classify_bitmap(const uint8_t* bstate, int32_t nmask, int32_t nbq, int32_t nbk,
+                                  int32_t bm, int32_t bn, int32_t nqt, int32_t nkt,
+                                  uint8_t* state, hipStream_t s) {
+  int64_t total = (int64_t)nmask * nqt * nkt;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_classify_bitmap, dim3(grid_for(total, 256)), dim3(256), 0, s, bstate, nmask,
+                     nbq, nbk, bm, bn, nqt, nkt, state);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_lists(const uint8_t* state, int32_t rows, int32_t nkt, int32_t* list,
+                             int32_t* count, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_tile_lists, dim3((rows + 3) / 4), dim3(256), 0, s, state, rows, nkt, list,
+                     count);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_order(const int32_t* count, int32_t rows, int32_t* order, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_tile_order, dim3((rows + 255) / 256), dim3(256), 0, s, count, rows, order);
+  return hipGetLastError();
+}
+
+}  // namespace fmask

@@ -1,0 +1,351 @@
+// Mask encoder kernels: mask-family parameters -> canonical compressed forms.
+//
+// * Interval form: per key column j the masked query rows, as at most two
+//   maximal runs UT = [UTS, UTE) and LT = [LTS, LTE) (the per-key-column
+//   lower/upper-triangle start/end encoding of FlashMask, as the FlashMask
+//   rebuttal page's method uses it).  Every interval family has a single
+//   contiguous visible row range per column, so the kernel computes that range
+//   [vlo, vhi) and writes its complement canonically.
+// * Bitmap form: 64 x 64 blocks (Binary Block Masking) with exact states and a
+//   compact pool of 64 row words per PARTIAL block, in row-major block order.
+// * Selected-key lists (llama.cpp selected-key PR): valid, distinct, ascending.
+#include "internal.h"
+
+namespace fmask {
+namespace {
+
+// Canonical (UTS, UTE, LTS, LTE) of a column whose visible rows are [vlo, vhi).
+__device__ inline void store_visible_range(int32_t* iv, int64_t skv, int64_t j, int64_t vlo,
+                                           int64_t vhi, int32_t sq) {
+  if (vlo < 0) vlo = 0;
+  if (vhi > sq) vhi = sq;
+  int32_t uts = 0, ute = 0, lts = sq, lte = sq;
+  if (vlo >= vhi) {
+    ute = sq;  // everything masked: one run starting at row 0
+  } else {
+    if (vlo > 0) ute = (int32_t)vlo;
+    if (vhi < sq) lts = (int32_t)vhi;
+  }
+  iv[j] = uts;
+  iv[skv + j] = ute;
+  iv[2 * skv + j] = lts;
+  iv[3 * skv + j] = lte;
+}
+
+// Largest s in [0, n_seg) with cu[s] <= pos.
+__device__ inline int segment_of(const int32_t* cu, int n_seg, int64_t pos) {
+  int lo = 0, hi = n_seg - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= pos) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ void k_family_intervals(SegParams p, int32_t* iv) {
+  for (int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; j < p.skv;
+       j += (int64_t)gridDim.x * blockDim.x) {
+    int64_t vlo = 0, vhi = p.sq;
+    switch (p.family) {
+      case FMASK_CAUSAL:  // j <= i
+        vlo = j;
+        break;
+      case FMASK_CAUSAL_BOTTOM_RIGHT:  // j <= i + skv - sq
+        vlo = j - ((int64_t)p.skv - p.sq);
+        break;
+      case FMASK_DOCUMENT: {
+        int s = segment_of(p.cu, p.n_seg, j);
+        vlo = p.cu[s];
+        vhi = p.cu[s + 1];
+        break;
+      }
+      case FMASK_CAUSAL_DOCUMENT: {
+        int s = segment_of(p.cu, p.n_seg, j);
+        vlo = j;
+        vhi = p.cu[s + 1];
+        break;
+      }
+      case FMASK_SHARED_QUESTION: {  // question columns: every later row; answers: own answer
+        int s = segment_of(p.cu, p.n_seg, j);
+        vlo = j;
+        vhi = (s == 0) ? p.sq : p.cu[s + 1];
+        break;
+      }
+      case FMASK_BAND: {  // r - pre <= j <= r + next with r = i + skv - sq
+        int64_t off = (int64_t)p.skv - p.sq;
+        vlo = j - p.next - off;
+        vhi = j + p.pre - off + 1;
+        break;
+      }
+      case FMASK_TREE: {  // prefix columns: causal; draft column c: its subtree rows
+        vlo = j;
+        if (j >= p.tree_prefix) vhi = (int64_t)p.tree_prefix + p.tree_hi[j - p.tree_prefix] + 1;
+        break;
+      }
+      default:
+        vlo = 0;
+        vhi = 0;
+        break;
+    }
+    store_visible_range(iv, p.skv, j, vlo, vhi, p.sq);
+  }
+}
+
+// Canonicalise caller-supplied (UTS, UTE, LTS, LTE): clip to [0, sq], drop
+// empty runs, order, merge overlapping or abutting runs.
+__global__ void k_raw_intervals(const int32_t* raw, int32_t nmask, int32_t sq, int32_t skv,
+                                int32_t* iv) {
+  int64_t total = (int64_t)nmask * skv;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    int64_t m = t / skv, j = t % skv;
+    const int32_t* r = raw + m * 4 * (int64_t)skv;
+    int32_t a0 = min(max(r[j], 0), sq), b0 = min(max(r[skv + j], 0), sq);
+    int32_t a1 = min(max(r[2 * (int64_t)skv + j], 0), sq), b1 = min(max(r[3 * (int64_t)skv + j], 0), sq);
+    bool e0 = a0 >= b0, e1 = a1 >= b1;
+    int32_t n = 0, s0 = 0, t0 = 0, s1 = 0, t1 = 0;
+    if (!e0 && !e1) {
+      if (a1 < a0) { int32_t x = a0; a0 = a1; a1 = x; x = b0; b0 = b1; b1 = x; }
+      if (a1 <= b0) { n = 1; s0 = a0; t0 = max(b0, b1); }
+      else { n = 2; s0 = a0; t0 = b0; s1 = a1; t1 = b1; }
+    } else if (!e0) { n = 1; s0 = a0; t0 = b0; }
+    else if (!e1) { n = 1; s0 = a1; t0 = b1; }
+    int32_t uts = 0, ute = 0, lts = sq, lte = sq;
+    if (n == 1) {
+      if (s0 == 0) ute = t0; else { lts = s0; lte = t0; }
+    } else if (n == 2) {
+      uts = s0; ute = t0; lts = s1; lte = t1;
+    }
+    int32_t* o = iv + m * 4 * (int64_t)skv;
+    o[j] = uts;
+    o[skv + j] = ute;
+    o[2 * (int64_t)skv + j] = lts;
+    o[3 * (int64_t)skv + j] = lte;
+  }
+}
+
+// Last descendant of every draft node (parent[t] < t, so a subtree that is a
+// contiguous range is [c, hi[c]]).  One workgroup.
+__global__ void k_tree_hi(const int32_t* parent, int32_t n, int32_t* hi) {
+  for (int t = threadIdx.x; t < n; t += blockDim.x) hi[t] = t;
+  __syncthreads();
+  for (int t = threadIdx.x; t < n; t += blockDim.x) {
+    int a = parent[t];
+    while (a >= 0) {
+      atomicMax(&hi[a], t);
+      a = parent[a];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ bitmap
+__device__ inline uint64_t col_mask(int32_t skv, int bj) {
+  int valid = skv - bj * kBlk;
+  return valid >= 64 ? ~0ull : ((1ull << valid) - 1ull);
+}
+
+// Row word r of block (bi, bj) of mask m: bit c = vis(64 bi + r, 64 bj + c).
+__device__ uint64_t source_word(const BitmapSrc& s, int m, int bi, int bj, int r) {
+  int64_t i = (int64_t)bi * kBlk + r;
+  if (i >= s.sq) return 0;
+  uint64_t w = 0;
+  if (s.kind == 0) {
+    size_t b = ((size_t)m * s.nbq + bi) * s.nbk + bj;
+    uint8_t st = s.state[b];
+    if (st == FMASK_FULL) {
+      w = ~0ull;
+    } else if (st == FMASK_PARTIAL) {
+      int64_t idx = s.index[b];
+      if (idx >= 0 && idx < s.pool_n) w = s.bits[idx * kBlk + r];
+    }
+    if (s.force_diag) {
+      int64_t c = i - (int64_t)bj * kBlk;
+      if (c >= 0 && c < 64) w |= 1ull << c;
+    }
+  } else {
+    int64_t P = s.tree_prefix;
+    int64_t base = (int64_t)bj * kBlk;
+    if (i < P) {  // causal prefix row: columns j <= i
+      int64_t c = i - base;
+      w = c >= 63 ? ~0ull : (c >= 0 ? ((2ull << c) - 1ull) : 0ull);
+    } else {      // draft row: whole prefix, then ancestors and itself
+      int64_t pc = P - base;
+      w = pc >= 64 ? ~0ull : (pc > 0 ? ((1ull << pc) - 1ull) : 0ull);
+      int a = (int)(i - P);
+      while (a >= 0) {
+        int64_t c = P + a - base;
+        if (c >= 0 && c < 64) w |= 1ull << c;
+        a = s.parent[a];
+      }
+    }
+  }
+  return w & col_mask(s.skv, bj);
+}
+
+// One wave per block: exact state from the 64 row words.
+__global__ void __launch_bounds__(256) k_bitmap_state(BitmapSrc s, uint8_t* state) {
+  int64_t nblocks = (int64_t)s.nmask * s.nbq * s.nbk;
+  int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  int r = threadIdx.x & 63;
+  if (blk >= nblocks) return;  // whole wave leaves together
+  int bj = (int)(blk % s.nbk);
+  int bi = (int)((blk / s.nbk) % s.nbq);
+  int m = (int)(blk / ((int64_t)s.nbk * s.nbq));
+  uint64_t w = source_word(s, m, bi, bj, r);
+  bool row_valid = (int64_t)bi * kBlk + r < s.sq;
+  bool full = !row_valid || w == col_mask(s.skv, bj);
+  bool any = __any(w != 0);
+  bool all = __all(full);
+  if (r == 0) state[blk] = any ? (all ? FMASK_FULL : FMASK_PARTIAL) : FMASK_SKIP;
+}
+
+// One wave per block row: row-local rank of every PARTIAL block, and the count.
+__global__ void __launch_bounds__(256) k_bitmap_row_rank(const uint8_t* state, int32_t rows,
+                                                         int32_t nbk, int32_t* index,
+                                                         int32_t* row_count) {
+  int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  int running = 0;
+  for (int base = 0; base < nbk; base += 64) {
+    int bj = base + lane;
+    bool part = bj < nbk && state[(int64_t)row * nbk + bj] == FMASK_PARTIAL;
+    uint64_t bal = __ballot(part);
+    int rank = running + __popcll(bal & ((1ull << lane) - 1ull));
+    if (bj < nbk) index[(int64_t)row * nbk + bj] = part ? rank : -1;
+    running += __popcll(bal);
+  }
+  if (lane == 0) row_count[row] = running;
+}
+
+// Exclusive scan of n counts (one workgroup of 1024 threads), total to *total.
+__global__ void __launch_bounds__(1024) k_exclusive_scan(const int32_t* in, int32_t n, int32_t* out,
+                                                         int32_t* total) {
+  __shared__ int32_t buf[1024];
+  __shared__ int32_t carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < n; base += 1024) {
+    int i = base + threadIdx.x;
+    int32_t x = i < n ? in[i] : 0;
+    buf[threadIdx.x] = x;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      int32_t y = threadIdx.x >= off ? buf[threadIdx.x - off] : 0;
+      __syncthreads();
+      buf[threadIdx.x] += y;
+      __syncthreads();
+    }
+    int32_t incl = buf[threadIdx.x];
+    int32_t c = carry;
+    if (i < n) out[i] = c + incl - x;
+    __syncthreads();
+    if (threadIdx.x == 1023) carry = c + incl;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *total = carry;
+}
+
+// One wave per block: final pool index, and the 64 words of PARTIAL blocks.
+__global__ void __launch_bounds__(256) k_bitmap_words(BitmapSrc s, BitmapOut o) {
+  int64_t nblocks = (int64_t)s.nmask * s.nbq * s.nbk;
+  int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  int r = threadIdx.x & 63;
+  if (blk >= nblocks) return;
+  int32_t local = o.index[blk];
+  if (local < 0) return;  // uniform over the wave
+  int bj = (int)(blk % s.nbk);
+  int64_t row = blk / s.nbk;
+  int bi = (int)(row % s.nbq);
+  int m = (int)(row / s.nbq);
+  int64_t g = (int64_t)o.row_offset[row] + local;
+  __builtin_amdgcn_wave_barrier();
+  if (r == 0) o.index[blk] = (int32_t)g;
+  if (g < o.cap) o.bits[g * kBlk + r] = source_word(s, m, bi, bj, r);
+}
+
+// ------------------------------------------------------------------ selected
+// One wave per (batch, query): keep the valid first occurrences, rank them.
+__global__ void __launch_bounds__(256) k_selected_canon(const int32_t* sel, int32_t nb, int32_t sq,
+                                                        int32_t n, int32_t nblk, int32_t* list,
+                                                        int32_t* count) {
+  __shared__ int32_t vals[4][64];
+  __shared__ int32_t keep[4][64];
+  int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int64_t q = (int64_t)blockIdx.x * 4 + w;
+  bool live = q < (int64_t)nb * sq;
+  int32_t x = (live && lane < n) ? sel[q * n + lane] : -1;
+  bool valid = live && lane < n && x >= 0 && x < nblk;
+  vals[w][lane] = valid ? x : -1;
+  __syncthreads();
+  bool first = valid;
+  for (int e = 0; e < lane && first; ++e) first = vals[w][e] != x;
+  keep[w][lane] = first;
+  __syncthreads();
+  if (!live) return;
+  int rank = 0, total = 0;
+  for (int e = 0; e < n; ++e) {
+    if (keep[w][e]) {
+      ++total;
+      rank += vals[w][e] < x;
+    }
+  }
+  if (first) list[q * n + rank] = x;
+  if (lane < n && lane >= total) list[q * n + lane] = -1;
+  if (lane == 0) count[q] = total;
+}
+
+inline int grid_for(int64_t n, int per_block, int cap = 65535 * 16) {
+  int64_t g = (n + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_encode_family_intervals(const SegParams& p, int32_t* iv, hipStream_t s) {
+  if (p.skv <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_family_intervals, dim3(grid_for(p.skv, 256)), dim3(256), 0, s, p, iv);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_raw_intervals(const int32_t* raw, int32_t nmask, int32_t sq, int32_t skv,
+                                       int32_t* iv, hipStream_t s) {
+  int64_t total = (int64_t)nmask * skv;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_raw_intervals, dim3(grid_for(total, 256)), dim3(256), 0, s, raw, nmask, sq,
+                     skv, iv);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_hi(const int32_t* parent, int32_t n, int32_t* hi, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_tree_hi, dim3(1), dim3(1024), 0, s, parent, n, hi);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_bitmap(const BitmapSrc& src, const BitmapOut& out, hipStream_t s) {
+  int64_t nblocks = (int64_t)src.nmask * src.nbq * src.nbk;
+  int32_t rows = src.nmask * src.nbq;
+  if (nblocks <= 0) return hipSuccess;
+  int g4 = (int)((nblocks + 3) / 4);
+  hipLaunchKernelGGL(k_bitmap_state, dim3(g4), dim3(256), 0, s, src, out.state);
+  hipLaunchKernelGGL(k_bitmap_row_rank, dim3((rows + 3) / 4), dim3(256), 0, s, out.state, rows,
+                     src.nbk, out.index, out.row_count);
+  hipLaunchKernelGGL(k_exclusive_scan, dim3(1), dim3(1024), 0, s, out.row_count, rows,
+                     out.row_offset, out.pool_count);
+  hipLaunchKernelGGL(k_bitmap_words, dim3(g4), dim3(256), 0, s, src, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_selected(const int32_t* sel, int32_t nb, int32_t sq, int32_t n,
+                                  int32_t nblk, int32_t* list, int32_t* count, hipStream_t s) {
+  int64_t q = (int64_t)nb * sq;
+  if (q <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_selected_canon, dim3((unsigned)((q + 3) / 4)), dim3(256), 0, s, sel, nb, sq,
+                     n, nblk, list, count);
+  return hipGetLastError();
+}
+
+}  // namespace fmask

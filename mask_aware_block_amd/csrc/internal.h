@@ -1,0 +1,122 @@
+// Internal declarations shared by the libfmask translation units (not part of
+// the C ABI).  Kernels are written for gfx950 (CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fmask.h"
+
+namespace fmask {
+
+constexpr int kBlk = FMASK_BLOCK;  // 64: bitmap granularity
+constexpr int kXcds = 8;           // MI355X: 8 XCDs, workgroups dealt round-robin
+
+// ---------------------------------------------------------------- encoder
+struct SegParams {
+  int32_t family;
+  int32_t sq, skv;
+  const int32_t* cu;  // device copy of cu_seg, n_seg + 1 entries
+  int32_t n_seg;
+  int64_t pre, next;  // band, clamped by the host to +-(sq + skv + 1)
+  int32_t tree_prefix;
+  const int32_t* tree_hi;  // per draft node: last descendant (interval-form tree)
+};
+
+hipError_t launch_encode_family_intervals(const SegParams& p, int32_t* iv, hipStream_t s);
+hipError_t launch_encode_raw_intervals(const int32_t* raw, int32_t nmask, int32_t sq, int32_t skv,
+                                       int32_t* iv, hipStream_t s);
+hipError_t launch_tree_hi(const int32_t* parent, int32_t n, int32_t* hi, hipStream_t s);
+
+// Source of the 64-bit row words of a 64 x 64 block, for the bitmap encoder.
+struct BitmapSrc {
+  int32_t kind;  // 0 = caller bitmap, 1 = tree
+  int32_t nmask, nbq, nbk;
+  int32_t sq, skv;
+  // caller bitmap
+  const uint8_t* state;
+  const int32_t* index;
+  const uint64_t* bits;
+  int64_t pool_n;
+  int32_t force_diag;
+  // tree
+  int32_t tree_prefix, tree_n;
+  const int32_t* parent;
+};
+
+struct BitmapOut {
+  uint8_t* state;       // [nmask][nbq][nbk]
+  int32_t* index;       // same
+  uint64_t* bits;       // [cap][64]
+  int64_t cap;
+  int32_t* row_count;   // [nmask * nbq]
+  int32_t* row_offset;  // [nmask * nbq]
+  int32_t* pool_count;  // scalar
+};
+
+hipError_t launch_encode_bitmap(const BitmapSrc& src, const BitmapOut& out, hipStream_t s);
+
+hipError_t launch_encode_selected(const int32_t* sel, int32_t nb, int32_t sq, int32_t n,
+                                  int32_t nblk, int32_t* list, int32_t* count, hipStream_t s);
+
+// ---------------------------------------------------------------- classifier
+hipError_t launch_classify_intervals(const int32_t* iv, int32_t nmask, int32_t sq, int32_t skv,
+                                     int32_t bm, int32_t bn, int32_t nqt, int32_t nkt,
+                                     uint8_t* state, hipStream_t s);
+hipError_t launch_classify_bitmap(const uint8_t* bstate, int32_t nmask, int32_t nbq, int32_t nbk,
+                                  int32_t bm, int32_t bn, int32_t nqt, int32_t nkt,
+                                  uint8_t* state, hipStream_t s);
+hipError_t launch_tile_lists(const uint8_t* state, int32_t rows, int32_t nkt, int32_t* list,
+                             int32_t* count, hipStream_t s);
+hipError_t launch_tile_order(const int32_t* count, int32_t rows, int32_t* order, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+struct TileAttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t qs[3], ks[3], vs[3], os[3];
+  int32_t b, hq, hkv, group;  // group = hq / hkv
+  int32_t sq, skv;
+  float scale;
+  // tile table
+  const int32_t* list;
+  const int32_t* count;
+  const int32_t* order;
+  int32_t nqt, nkt, bm, bn;
+  int32_t mb, mh;      // distinct masks along batch / heads
+  int32_t expand;      // (b, h) pairs per tile row
+  int32_t n_items;     // tile rows * expand
+  // mask
+  int32_t kind;        // FMASK_ENC_INTERVALS or FMASK_ENC_BITMAP
+  const int32_t* iv;   // [mb][mh][4][skv]
+  const uint8_t* bstate;
+  const int32_t* bindex;
+  const uint64_t* bbits;
+  int32_t nbq, nbk;
+};
+
+hipError_t launch_attn_tile_bf16(const TileAttnParams& p, int32_t d, hipStream_t s);
+hipError_t launch_attn_tile_f32(const TileAttnParams& p, int32_t d, hipStream_t s);
+
+struct SelAttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t qs[3], ks[3], vs[3], os[3];
+  int32_t b, hq, hkv, group;
+  int32_t sq, skv;
+  float scale;
+  const int32_t* list;   // [mb][sq][n]
+  const int32_t* count;  // [mb][sq]
+  int32_t n, cells, mb;
+};
+
+hipError_t launch_attn_selected_bf16(const SelAttnParams& p, int32_t d, hipStream_t s);
+
+}  // namespace fmask

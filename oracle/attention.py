@@ -76,18 +76,25 @@ def spec_vis_fn(spec):
     return lambda b, h, rows: masks.dense_vis(spec, b, h, rows)
 
 
-def attention_rows(q, k, v, vis_fn, scale, samples):
-    """O [n, D] and LSE [n] for sampled rows samples = [(b, h, i), ...]."""
+def _f64(x, decode):
+    return decode(x) if decode is not None else np.asarray(x, dtype=np.float64)
+
+
+def attention_rows(q, k, v, vis_fn, scale, samples, decode=None):
+    """O [n, D] and LSE [n] for sampled rows samples = [(b, h, i), ...].
+
+    decode (optional) turns stored values into float64, e.g. bf16_bits_to_f64.
+    """
     Hq, Hkv = q.shape[1], k.shape[1]
     G = Hq // Hkv
     outs, lses = [], []
     for b, h, i in samples:
         g = h // G
         vis = np.asarray(vis_fn(b, h, np.array([i])), dtype=bool)
-        qi = np.asarray(q[b, h, i], dtype=np.float64)
-        kk = np.asarray(k[b, g], dtype=np.float64)
+        qi = _f64(q[b, h, i], decode)
+        kk = _f64(k[b, g], decode)
         s = scale * (kk @ qi)[None, :]
-        o, lse = _softmax_rows(s, vis, np.asarray(v[b, g], dtype=np.float64))
+        o, lse = _softmax_rows(s, vis, _f64(v[b, g], decode))
         outs.append(o[0])
         lses.append(lse[0])
     return np.array(outs), np.array(lses)
@@ -126,7 +133,7 @@ def listed_cells(entries, cells, skv):
     return np.concatenate(out) if out else np.zeros(0, dtype=np.int64)
 
 
-def attention_listed_cells(q, k, v, sel, cells, scale, samples):
+def attention_listed_cells(q, k, v, sel, cells, scale, samples, decode=None):
     """Selected-key attention over exactly the listed cells, for sampled rows.
 
     sel [B_m][Sq][n] lists (shared by every head); samples = [(b, h, i), ...].
@@ -144,9 +151,9 @@ def attention_listed_cells(q, k, v, sel, cells, scale, samples):
             outs.append(np.zeros(v.shape[3]))
             lses.append(-np.inf)
             continue
-        kk = np.asarray(k[b, g, keys], dtype=np.float64)
-        vv = np.asarray(v[b, g, keys], dtype=np.float64)
-        s = scale * (kk @ np.asarray(q[b, h, i], dtype=np.float64))
+        kk = _f64(k[b, g, keys], decode)
+        vv = _f64(v[b, g, keys], decode)
+        s = scale * (kk @ _f64(q[b, h, i], decode))
         m = s.max()
         p = np.exp(s - m)
         l = p.sum()

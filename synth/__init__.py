@@ -25,7 +25,7 @@ and for the selected-key PR's model workload):
     Medusa-style) or in depth-first preorder;
   * selected key: per query 64 block indices uniform in [0, nblk), each replaced
     by -1 with probability 1/8; query 0 lists only -1, query 1 one block 64
-    times, query 2 sixty-four distinct blocks.
+    times, query 2 sixty-four distinct blocks (all blocks, repeated, if fewer).
 """
 
 import math
@@ -137,8 +137,8 @@ def selected_lists(rng, sq, nblk, n=64, p_invalid=1 / 8):
         sel[0] = -1
     if sq > 1:
         sel[1] = int(rng.integers(0, nblk))
-    if sq > 2:
-        sel[2] = rng.choice(nblk, size=n, replace=False)
+    if sq > 2:  # distinct entries (every block once, then repeats, if n > nblk)
+        sel[2] = np.resize(rng.permutation(nblk), n)
     return sel.astype(np.int32)
 
 

@@ -1,0 +1,184 @@
+"""GPU masked attention (through the C ABI) vs the float64 oracle.
+
+Small shapes (several tiles and a ragged tail) are compared element by element
+over every output; the workloads at their full sizes are compared on sampled
+rows that the oracle computes one by one.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import attention as OA
+from oracle import masks as OM
+from tests.helpers import TOL, compare, sample_rows, to_device, to_f64
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+fm = pytest.importorskip("mask_aware_block_amd")
+
+
+def _run(w, arrays, spec=None):
+    spec = spec or w["mask"]
+    q, k, v = to_device(w, arrays)
+    enc = fm.encode(spec)
+    tiles = None
+    if enc.kind != fm.ENC_SELECTED:
+        tiles = fm.classify(enc, dtype=w["dtype"], d=w["D"])
+    o, lse = fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"])
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _dense_check(w, spec=None, what=""):
+    spec = spec or w["mask"]
+    arrays = synth.draw_qkv(w)
+    o, lse = _run(w, arrays, spec)
+    q, k, v = (to_f64(w, a) for a in arrays)
+    ro, rl = OA.attention_dense(q, k, v, OA.spec_vis_fn(spec), w["scale"])
+    return compare(w, o, lse, ro, rl, what or spec["family"])
+
+
+def test_tiny_causal_doc_fp32():
+    w = synth.workload("tiny_causal_doc")
+    err = _dense_check(w)
+    assert err[0] <= 1e-5
+
+
+def _small(dtype, D, S=333, K=None, Hq=4, Hkv=2, B=1, seed=11):
+    K = K or S
+    w = dict(name="small", seed=seed, B=B, Hq=Hq, Hkv=Hkv, Sq=S, Skv=K, D=D, dtype=dtype,
+             scale=1 / math.sqrt(D))
+    return w
+
+
+def _specs(S, K):
+    rng = np.random.default_rng(S * 7 + K)
+    cu = np.unique(np.concatenate(([0, S], rng.integers(1, S, 6)))).astype(np.int32)
+    out = [dict(family="causal", sq=S, skv=K),
+           dict(family="band", sq=S, skv=K, pre=40, next=3),
+           dict(family="band", sq=S, skv=K, pre=9, next=-3)]
+    if S == K:
+        out += [dict(family="document", sq=S, skv=K, cu_seg=cu),
+                dict(family="causal_document", sq=S, skv=K, cu_seg=cu),
+                dict(family="shared_question", sq=S, skv=K, cu_seg=cu),
+                dict(family="tree", sq=S, skv=S, tree_prefix=S - 64,
+                     tree_parent=synth.random_tree(rng, 64, order="bfs")),
+                dict(family="tree", sq=S, skv=S, tree_prefix=S - 64,
+                     tree_parent=synth.random_tree(rng, 64, order="dfs"))]
+    else:
+        out += [dict(family="causal_bottom_right", sq=S, skv=K)]
+    return out
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
+@pytest.mark.parametrize("S,K", [(333, 333), (200, 461)])
+def test_small_families(dtype, D, S, K):
+    w = _small(dtype, D, S, K)
+    for spec in _specs(S, K):
+        _dense_check(w, spec, f"{spec['family']} {dtype} d{D} {S}x{K}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_bitmap_and_raw_intervals(dtype):
+    S, K = 320, 260
+    w = _small(dtype, 128, S, K, B=2, Hq=4, Hkv=4)
+    rng = np.random.default_rng(3)
+    nbq, nbk = -(-S // 64), -(-K // 64)
+    sts, ixs, pools, off = [], [], [], 0
+    for _ in range(2):
+        st, ix, bits = synth.block_pattern(rng, nbq, nbk, 0.3, 0.3)
+        sts.append(st)
+        ixs.append(np.where(ix >= 0, ix + off, -1))
+        pools.append(bits)
+        off += bits.shape[0]
+    spec = dict(family="block_bitmap", sq=S, skv=K, batch=2, heads=1,
+                blk_state=np.stack(sts)[:, None], blk_index=np.stack(ixs)[:, None].astype(np.int32),
+                blk_bits=np.concatenate(pools).reshape(-1, 64), force_diag=True)
+    _dense_check(w, spec, "bitmap")
+    raw = rng.integers(-10, S + 10, size=(2, 4, 4, K)).astype(np.int32)
+    spec = dict(family="intervals", sq=S, skv=K, batch=2, heads=4, raw_intervals=raw)
+    _dense_check(w, spec, "raw intervals per head")
+
+
+def test_gqa_groups_and_batch():
+    for Hq, Hkv in [(8, 1), (8, 8), (6, 2)]:
+        w = _small("bf16", 128, 257, 257, Hq=Hq, Hkv=Hkv, B=2)
+        _dense_check(w, dict(family="causal", sq=257, skv=257), f"gqa {Hq}/{Hkv}")
+
+
+def test_empty_and_degenerate():
+    # every row empty: zero output, LSE -inf
+    w = _small("bf16", 128, 130, 130)
+    _dense_check(w, dict(family="band", sq=130, skv=130, pre=2, next=-3), "all empty")
+    # one query row, one key
+    w = _small("bf16", 128, 1, 1)
+    _dense_check(w, dict(family="causal", sq=1, skv=1), "1x1")
+    w = _small("f32", 64, 1, 70)
+    _dense_check(w, dict(family="causal_bottom_right", sq=1, skv=70), "1x70")
+
+
+def test_selected_small():
+    w = _small("bf16", 256, 40, 1000, Hq=8, Hkv=2)
+    rng = np.random.default_rng(4)
+    nblk = -(-1000 // 32)
+    sel = synth.selected_lists(rng, 40, nblk, n=64)[None]
+    spec = dict(family="selected_key", sq=40, skv=1000, batch=1, sel=sel, sel_cells=32)
+    _dense_check(w, spec, "selected")
+    w = _small("bf16", 128, 33, 300, Hq=4, Hkv=4, B=2)
+    sel = np.stack([synth.selected_lists(rng, 33, 10, n=7) for _ in range(2)])
+    spec = dict(family="selected_key", sq=33, skv=300, batch=2, sel=sel, sel_cells=32)
+    _dense_check(w, spec, "selected per batch")
+
+
+FULL = ["causal_doc_8k", "causal_doc_32k", "shared_question_32k", "band_32k", "band_neg_4k",
+        "block_bitmap_16k", "tree_4k", "tree_4k_dfs", "selected_key_128k"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    w = synth.workload(name)
+    spec = w["mask"]
+    arrays = synth.draw_qkv(w)
+    o, lse = _run(w, arrays)
+    rng = np.random.default_rng(1)
+    extra = []
+    if "cu_seg" in spec:
+        cu = np.asarray(spec["cu_seg"])
+        extra = list(cu[1:-1]) + list(cu[1:-1] - 1)
+    samples = sample_rows(w, 96, rng, extra=tuple(int(x) for x in extra[:40]))
+    decode = OA.bf16_bits_to_f64 if w["dtype"] == "bf16" else None
+    q, k, v = arrays
+    if spec["family"] == "selected_key":
+        ro, rl = OA.attention_listed_cells(q, k, v, spec["sel"], spec["sel_cells"], w["scale"],
+                                           samples, decode=decode)
+    else:
+        ro, rl = OA.attention_rows(q, k, v, OA.spec_vis_fn(spec), w["scale"], samples, decode=decode)
+    idx = tuple(np.array(samples).T)
+    compare(w, o[idx], lse[idx], ro, rl, name)
+
+
+def test_poison_masked_kv_does_not_leak():
+    """NaN in K/V columns that no row can see (SKIP tiles) must not reach the output."""
+    w = _small("bf16", 128, 192, 384, Hq=4, Hkv=2)
+    spec = dict(family="causal", sq=192, skv=384)  # keys 192.. are visible to no row
+    arrays = synth.draw_qkv(w)
+    o1, l1 = _run(w, arrays, spec)
+    k, v = arrays[1].copy(), arrays[2].copy()
+    k[:, :, 192:] = 0x7FC0  # bf16 NaN
+    v[:, :, 192:] = 0x7FC0
+    o2, l2 = _run(w, (arrays[0], k, v), spec)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_deterministic():
+    w = synth.workload("causal_doc_8k", Hq=8, Hkv=2)
+    arrays = synth.draw_qkv(w)
+    o1, l1 = _run(w, arrays)
+    o2, l2 = _run(w, arrays)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)

@@ -1,0 +1,222 @@
+"""GPU encoder and tile classifier vs the oracle: bit-exact.
+
+The expected values are derived by the oracle from the dense mask of each
+family (canonical intervals / bitmap / lists, exact tile states, compact lists,
+longest-first order); the GPU path computes them from the compressed
+description only.
+"""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import encode as OE
+from oracle import masks as OM
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+fm = pytest.importorskip("mask_aware_block_amd")
+
+TILE_SHAPES_IV = [(128, 64), (64, 64), (32, 48), (16, 16), (256, 128), (48, 208)]
+TILE_SHAPES_BM = [(128, 64), (64, 64), (64, 128), (256, 192)]
+
+
+def _small_specs():
+    rng = np.random.default_rng(123)
+    out = []
+    for S in (333, 64, 1):
+        cu = np.unique(np.concatenate(([0, S], rng.integers(1, S, size=min(5, S - 1)) if S > 1 else [])))
+        cu = cu.astype(np.int32)
+        out += [
+            dict(family="causal", sq=S, skv=S),
+            dict(family="document", sq=S, skv=S, cu_seg=cu),
+            dict(family="causal_document", sq=S, skv=S, cu_seg=cu),
+            dict(family="shared_question", sq=S, skv=S, cu_seg=cu),
+            dict(family="band", sq=S, skv=S, pre=37, next=5),
+            dict(family="band", sq=S, skv=S, pre=9, next=-3),
+            dict(family="band", sq=S, skv=S, pre=-3, next=7),
+            dict(family="band", sq=S, skv=S, pre=2, next=-3),           # every row empty
+            dict(family="band", sq=S, skv=S, pre=10 ** 15, next=-10 ** 15),
+        ]
+    out += [
+        dict(family="causal", sq=200, skv=333),
+        dict(family="causal_bottom_right", sq=200, skv=333),
+        dict(family="band", sq=100, skv=300, pre=50, next=0),
+        dict(family="band", sq=300, skv=100, pre=6, next=-2),
+        dict(family="tree", sq=300, skv=300, tree_prefix=236,
+             tree_parent=synth.random_tree(rng, 64, order="dfs")),
+    ]
+    return out
+
+
+def _dense_all(spec, b=0, h=0):
+    return np.asarray(OM.dense_vis(spec, b, h))
+
+
+@pytest.mark.parametrize("spec", _small_specs(), ids=lambda s: f"{s['family']}-{s['sq']}x{s['skv']}")
+def test_interval_families_exact(spec):
+    enc = fm.encode(spec)
+    assert enc.kind == fm.ENC_INTERVALS
+    vis = _dense_all(spec)
+    exp = OE.intervals_from_dense(vis)
+    got = enc.intervals().cpu().numpy()[0, 0]
+    np.testing.assert_array_equal(got, exp)
+    for bm, bn in TILE_SHAPES_IV:
+        t = fm.classify(enc, bm, bn)
+        st, ls, cn, od = [x.cpu().numpy() for x in t.arrays()]
+        exp_st = OE.tile_states(vis, bm, bn)
+        np.testing.assert_array_equal(st[0, 0], exp_st, err_msg=f"states {bm}x{bn}")
+        el, ec = OE.tile_lists(exp_st)
+        np.testing.assert_array_equal(ls[0, 0], el, err_msg=f"lists {bm}x{bn}")
+        np.testing.assert_array_equal(cn[0, 0], ec)
+        np.testing.assert_array_equal(od, OE.tile_order(ec))
+
+
+def test_raw_intervals_canonicalised():
+    rng = np.random.default_rng(5)
+    B, H, S, K = 2, 3, 150, 170
+    raw = rng.integers(-20, S + 20, size=(B, H, 4, K)).astype(np.int32)
+    # a few structured columns: abutting, overlapping, nested, empty
+    raw[0, 0, :, 0] = [0, 10, 10, 20]
+    raw[0, 0, :, 1] = [30, 50, 40, 60]
+    raw[0, 0, :, 2] = [30, 80, 40, 60]
+    raw[0, 0, :, 3] = [5, 5, 9, 3]
+    raw[0, 0, :, 4] = [100, 120, 0, 10]
+    spec = dict(family="intervals", sq=S, skv=K, batch=B, heads=H, raw_intervals=raw)
+    enc = fm.encode(spec)
+    got = enc.intervals().cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            vis = _dense_all(spec, b, h)
+            np.testing.assert_array_equal(got[b, h], OE.intervals_from_dense(vis), err_msg=f"{b},{h}")
+    t = fm.classify(enc, 64, 64)
+    st, ls, cn, od = [x.cpu().numpy() for x in t.arrays()]
+    allc = []
+    for b in range(B):
+        for h in range(H):
+            es = OE.tile_states(_dense_all(spec, b, h), 64, 64)
+            np.testing.assert_array_equal(st[b, h], es)
+            allc.append(OE.tile_lists(es)[1])
+    np.testing.assert_array_equal(od, OE.tile_order(np.concatenate(allc)))
+
+
+def _bitmap_expect(spec, b, h):
+    st, ix, pool = OE.bitmap_from_dense(_dense_all(spec, b, h))
+    return st, ix, pool
+
+
+def _check_bitmap(enc, spec, B, H):
+    st, ix, bits, cnt = enc.bitmap()
+    st, ix, bits = st.cpu().numpy(), ix.cpu().numpy(), bits.cpu().numpy().view(np.uint64)
+    pool_all = []
+    for b in range(B):
+        for h in range(H):
+            es, ei, ep = _bitmap_expect(spec, b, h)
+            np.testing.assert_array_equal(st[b, h], es, err_msg=f"state {b},{h}")
+            np.testing.assert_array_equal(ix[b, h] >= 0, ei >= 0)
+            off = len(pool_all)
+            np.testing.assert_array_equal(ix[b, h][ei >= 0], ei[ei >= 0] + off)
+            pool_all += ep
+    assert cnt == len(pool_all)
+    if pool_all:
+        np.testing.assert_array_equal(bits, np.array(pool_all, dtype=np.uint64))
+
+
+@pytest.mark.parametrize("S,K,diag", [(300, 300, True), (130, 200, False), (64, 64, True), (1, 70, True)])
+def test_block_bitmap_exact(S, K, diag):
+    rng = np.random.default_rng(S + K)
+    B = 2
+    nbq, nbk = -(-S // 64), -(-K // 64)
+    sts, ixs, pools, off = [], [], [], 0
+    for _ in range(B):
+        st, ix, bits = synth.block_pattern(rng, nbq, nbk, 0.3, 0.3)
+        sts.append(st)
+        ixs.append(np.where(ix >= 0, ix + off, -1))
+        pools.append(bits)
+        off += bits.shape[0]
+    spec = dict(family="block_bitmap", sq=S, skv=K, batch=B, heads=1,
+                blk_state=np.stack(sts)[:, None], blk_index=np.stack(ixs)[:, None].astype(np.int32),
+                blk_bits=np.concatenate(pools).reshape(-1, 64), force_diag=diag)
+    enc = fm.encode(spec)
+    assert enc.kind == fm.ENC_BITMAP
+    _check_bitmap(enc, spec, B, 1)
+    for bm, bn in TILE_SHAPES_BM:
+        t = fm.classify(enc, bm, bn)
+        st, ls, cn, od = [x.cpu().numpy() for x in t.arrays()]
+        allc = []
+        for b in range(B):
+            es = OE.tile_states(_dense_all(spec, b, 0), bm, bn)
+            np.testing.assert_array_equal(st[b, 0], es, err_msg=f"{bm}x{bn}")
+            el, ec = OE.tile_lists(es)
+            np.testing.assert_array_equal(ls[b, 0], el)
+            allc.append(ec)
+        np.testing.assert_array_equal(od, OE.tile_order(np.concatenate(allc)))
+
+
+def test_tree_bfs_goes_bitmap_dfs_goes_intervals():
+    for name, kind in (("tree_4k", fm.ENC_BITMAP), ("tree_4k_dfs", fm.ENC_INTERVALS)):
+        w = synth.workload(name)
+        spec = w["mask"]
+        enc = fm.encode(spec)
+        assert enc.kind == kind, name
+        vis = _dense_all(spec)
+        if kind == fm.ENC_BITMAP:
+            _check_bitmap(enc, spec, 1, 1)
+        else:
+            np.testing.assert_array_equal(enc.intervals().cpu().numpy()[0, 0], OE.intervals_from_dense_fast(vis))
+        bm, bn = fm.preferred_tile("bf16", 128, kind)
+        t = fm.classify(enc, bm, bn)
+        st = t.arrays()[0].cpu().numpy()[0, 0]
+        np.testing.assert_array_equal(st, OE.tile_states_fast(vis, bm, bn))
+
+
+def test_selected_lists_exact():
+    rng = np.random.default_rng(8)
+    for skv, cells, n in [(131072, 32, 64), (1000, 32, 17), (100, 7, 5)]:
+        nblk = -(-skv // cells)
+        sel = synth.selected_lists(rng, 300, nblk, n=n)
+        sel[5, :3] = [nblk, nblk + 7, -5]  # out-of-range entries are ignored too
+        sel = np.stack([sel, rng.permutation(sel)])
+        spec = dict(family="selected_key", sq=300, skv=skv, batch=2, sel=sel, sel_cells=cells)
+        enc = fm.encode(spec)
+        ls, cn = [x.cpu().numpy() for x in enc.lists()]
+        el, ec = OE.canonical_lists(sel, nblk)
+        np.testing.assert_array_equal(ls, el)
+        np.testing.assert_array_equal(cn, ec)
+
+
+@pytest.mark.parametrize("name", ["causal_doc_8k", "causal_doc_32k", "shared_question_32k", "band_32k",
+                                  "band_neg_4k", "block_bitmap_16k"])
+def test_full_size_tables(name):
+    """Full-size encodings and tile tables: every tile state, sampled columns."""
+    w = synth.workload(name)
+    spec = w["mask"]
+    enc = fm.encode(spec)
+    bm, bn = fm.preferred_tile(w["dtype"], w["D"], enc.kind)
+    t = fm.classify(enc, bm, bn)
+    st, ls, cn, od = [x.cpu().numpy() for x in t.arrays()]
+    S = w["Sq"]
+    rng = np.random.default_rng(0)
+    nb = spec.get("batch", 1)
+    cols = np.unique(np.concatenate((rng.integers(0, w["Skv"], 200), [0, w["Skv"] - 1])))
+    if enc.kind == fm.ENC_INTERVALS:
+        got_iv = enc.intervals().cpu().numpy()[0, 0][:, cols]
+        colvis = np.zeros((S, cols.size), dtype=bool)
+    allc = []
+    for b in range(nb):
+        exp_st = np.zeros((t.struct.nqt, t.struct.nkt), dtype=np.uint8)
+        for qt in range(t.struct.nqt):
+            rows = np.arange(qt * bm, min(S, (qt + 1) * bm))
+            v = np.asarray(OM.dense_vis(spec, b, 0, rows))
+            exp_st[qt] = OE.tile_states_fast(v, bm, bn)[0]
+            if enc.kind == fm.ENC_INTERVALS and b == 0:
+                colvis[rows] = v[:, cols]
+        np.testing.assert_array_equal(st[b, 0], exp_st)
+        el, ec = OE.tile_lists(exp_st)
+        np.testing.assert_array_equal(ls[b, 0], el)
+        np.testing.assert_array_equal(cn[b, 0], ec)
+        allc.append(ec)
+    np.testing.assert_array_equal(od, OE.tile_order(np.concatenate(allc)))
+    if enc.kind == fm.ENC_INTERVALS:
+        np.testing.assert_array_equal(got_iv, OE.intervals_from_dense(colvis))

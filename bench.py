@@ -1,0 +1,236 @@
+"""Benchmark of the mask-aware attention forward path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+fmask_encode (compressed mask -> canonical intervals) -> fmask_classify
+(exact tile table, compact lists, longest-first order) -> fmask_attn_fwd.
+Inputs are resident in HBM before the timed region.
+
+Headline workload: causal-document packing at 32768 tokens, batch 1, 32 query
+heads, 8 K/V heads, head dim 128, bf16, document lengths drawn uniformly from
+the multiples of 64 in [256, 4096].  value = effective TFLOP/s counting only
+unmasked FLOPs: 4 * d * (visible (i, j) pairs) * heads / step time.
+
+Also reported (one object each under "workloads"): the other workloads at
+their full sizes, attention kernel time and effective TFLOP/s (gathered GB/s
+for the selected-key workload).
+
+Prints ONE JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def _bf16(torch, a):
+    return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def visible_pairs(torch, enc):
+    """Visible (i, j) pairs per mask, from the encoder's canonical intervals."""
+    iv = enc.intervals().to(torch.int64)
+    sq = enc.struct.sq
+    masked = (iv[:, :, 1] - iv[:, :, 0]) + (iv[:, :, 3] - iv[:, :, 2])
+    return (sq - masked).sum(dim=-1)  # [batch][heads]
+
+
+def visible_pairs_bitmap(torch, enc):
+    st, ix, bits, cnt = enc.bitmap()
+    e = enc.struct
+    n_full = 0
+    st64 = st.to(torch.int64)
+    # valid elements of every FULL block
+    rows = torch.clamp(e.sq - torch.arange(e.nbq, device=st.device) * 64, max=64)
+    cols = torch.clamp(e.skv - torch.arange(e.nbk, device=st.device) * 64, max=64)
+    area = rows[:, None] * cols[None, :]
+    n_full = ((st64 == 2) * area).sum(dim=(-1, -2))
+    # popcount of the partial pool words, attributed to their mask
+    words = bits.view(torch.int64)
+    pc = torch.zeros_like(words)
+    x = words.clone()
+    for _ in range(64):
+        pc += x & 1
+        x = torch.bitwise_right_shift(x, 1) & 0x7FFFFFFFFFFFFFFF
+    per_entry = pc.sum(dim=1)
+    owner = torch.zeros(cnt, dtype=torch.int64, device=st.device)
+    flat_ix = ix.reshape(e.batch * e.heads, -1)
+    for m in range(e.batch * e.heads):
+        sel = flat_ix[m][flat_ix[m] >= 0].to(torch.int64)
+        owner[sel] = m
+    part = torch.zeros(e.batch * e.heads, dtype=torch.int64, device=st.device)
+    part.index_add_(0, owner, per_entry)
+    return n_full + part.reshape(e.batch, e.heads)
+
+
+def time_workload(torch, fm, synth, name, steps, warmup, headline=False):
+    w = synth.workload(name)
+    q, k, v = (_bf16(torch, a) if w["dtype"] == "bf16" else torch.from_numpy(a).cuda()
+               for a in synth.draw_qkv(w))
+    mi = fm.MaskInput(w["mask"])
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    selected = w["mask"]["family"] == "selected_key"
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        enc = fm.encode(mi)
+        if ev:
+            ev[1].record(stream)
+        tiles = None if selected else fm.classify(enc, dtype=w["dtype"], d=w["D"])
+        if ev:
+            ev[2].record(stream)
+        fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"], out=o, lse=lse)
+        if ev:
+            ev[3].record(stream)
+        return enc, tiles
+
+    for _ in range(warmup):
+        enc, tiles = step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        enc, tiles = step(evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    t_enc = np.mean([a[0].elapsed_time(a[1]) for a in evs])
+    t_cls = np.mean([a[1].elapsed_time(a[2]) for a in evs])
+    t_att = np.mean([a[2].elapsed_time(a[3]) for a in evs])
+
+    rec = dict(workload=name, B=w["B"], Hq=w["Hq"], Hkv=w["Hkv"], Sq=w["Sq"], Skv=w["Skv"], D=w["D"],
+               dtype=w["dtype"], ms_per_step=wall * 1e3, encode_ms=float(t_enc),
+               classify_ms=float(t_cls), attn_ms=float(t_att))
+    if selected:
+        ls, cn = enc.lists()
+        cells = int(cn.sum().item()) * w["mask"]["sel_cells"]  # listed cells per (b, query)
+        nvis = cells * w["Hq"]                                 # every head of the query
+        gathered = cells * w["Hkv"] * 2 * w["D"] * 2            # K and V rows per kv head, bf16
+        rec.update(visible_pairs=int(nvis), effective_tflops=4 * w["D"] * nvis / (t_att * 1e-3) / 1e12,
+                   gathered_gbs=gathered / (t_att * 1e-3) / 1e9, gathered_bytes=int(gathered))
+    else:
+        if enc.kind == fm.ENC_INTERVALS:
+            pairs = visible_pairs(torch, enc)
+        else:
+            pairs = visible_pairs_bitmap(torch, enc)
+        mb, mh = enc.struct.batch, enc.struct.heads
+        nvis = int(pairs.sum().item()) * (w["B"] // mb) * (w["Hq"] // mh)
+        flops = 4 * w["D"] * nvis
+        st = tiles.arrays()[0]
+        rec.update(visible_pairs=int(nvis), effective_flop=int(flops),
+                   effective_tflops=flops / (wall) / 1e12,
+                   attn_effective_tflops=flops / (t_att * 1e-3) / 1e12,
+                   tiles=dict(bm=tiles.struct.bm, bn=tiles.struct.bn,
+                              skip=int((st == 0).sum().item()), partial=int((st == 1).sum().item()),
+                              full=int((st == 2).sum().item())))
+        if "doc_lengths" in w:
+            exp = sum(L * (L + 1) // 2 for L in w["doc_lengths"]) * w["B"] * w["Hq"]
+            assert exp == nvis, (exp, nvis)
+            rec["doc_lengths"] = w["doc_lengths"]
+    del q, k, v, o, lse
+    return rec
+
+
+def cpu_baseline(synth, name, rows, heads):
+    """The float64 oracle on a bounded sample of the workload, same FLOP numerator."""
+    from oracle import attention as OA
+    from oracle import masks as OM
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    w = synth.workload(name)
+    q, k, v = synth.draw_qkv(w)
+    q = OA.bf16_bits_to_f64(q[:, :heads, :rows])
+    k = OA.bf16_bits_to_f64(k[:, :1])
+    v = OA.bf16_bits_to_f64(v[:, :1])
+    G = w["Hq"] // w["Hkv"]
+    heads = min(heads, G)
+    spec = w["mask"]
+    vf = OA.spec_vis_fn(spec)
+    t0 = time.perf_counter()
+    OA.attention_dense(q[:, :heads], k, v, vf, w["scale"])
+    dt = time.perf_counter() - t0
+    nvis = int(np.asarray(OM.dense_vis(spec, 0, 0, np.arange(rows))).sum()) * heads
+    return dict(value=4 * w["D"] * nvis / dt / 1e12, unit="effective TFLOP/s", cores=int(threads),
+                kind="oracle", seconds=dt,
+                sample=f"{name}: query heads 0..{heads - 1} (K/V head 0), rows 0..{rows - 1} of {w['Sq']}, "
+                       f"all {w['Skv']} keys, float64 dense masked softmax attention")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the 32K causal-document step (for profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=32768)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import mask_aware_block_amd as fm
+    import synth
+
+    fm.lib()
+    torch.cuda.set_device(0)
+    head = time_workload(torch, fm, synth, "causal_doc_32k", args.steps, args.warmup, headline=True)
+    others = []
+    if not args.headline_only:
+        for name in ("causal_doc_8k", "shared_question_32k", "band_32k", "band_neg_4k",
+                     "block_bitmap_16k", "tree_4k", "selected_key_128k"):
+            others.append(time_workload(torch, fm, synth, name, max(3, args.steps // 2), 2))
+            torch.cuda.empty_cache()
+
+    achieved = head["effective_flop"] / (head["attn_ms"] * 1e-3) / 1e12
+    out = {
+        "metric": "effective TFLOP/s (unmasked FLOPs) + fraction of bf16 MFMA peak, 8K-128K seq",
+        "value": head["effective_tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, seeded document lengths)",
+        "config": {"workload": "causal_document_32k", "batch": 1, "q_heads": 32, "kv_heads": 8,
+                   "seq_len": 32768, "head_dim": 128, "doc_lengths": head["doc_lengths"],
+                   "visible_pairs": head["visible_pairs"]},
+        "fraction_of_peak": head["effective_tflops"] / PEAK_BF16_TFLOPS,
+        "step_breakdown_ms": {"encode": head["encode_ms"], "classify": head["classify_ms"],
+                              "attention": head["attn_ms"]},
+        "roofline": {"bound": "mfma", "kernel": "k_attn_tile_bf16<128,4,intervals>",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "workloads": others,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(synth, "causal_doc_32k", args.cpu_rows, 1)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -246,11 +246,24 @@ class Encoding:
         return ls, cn
 
 
+class MaskInput:
+    """A mask description with its device-side inputs already uploaded."""
+
+    def __init__(self, spec, device="cuda"):
+        self.desc, self.keep = make_desc(spec, device)
+
+
 def encode(spec, device="cuda", stream=None):
-    """Run the mask encoder (fmask_encode) on the device."""
+    """Run the mask encoder (fmask_encode) on the device.
+
+    spec: a mask spec dict (see make_desc) or a MaskInput.
+    """
     torch = _torch()
     L = lib()
-    desc, keep = make_desc(spec, device)
+    if isinstance(spec, MaskInput):
+        desc, keep = spec.desc, [spec]
+    else:
+        desc, keep = make_desc(spec, device)
     nbytes = L.fmask_encode_bytes(ctypes.byref(desc))
     if nbytes == 0:
         _check(L.fmask_encode(ctypes.byref(desc), None, 0, ctypes.byref(Encoded()), None))

@@ -485,6 +485,11 @@ fmask_status fmask_attn_fwd(const fmask_attn_args* a, const void* q, const void*
   if (tiles->nqt != ceil_div(a->sq, bm) || tiles->nkt != ceil_div(a->skv, bn) ||
       tiles->batch != enc->batch || tiles->heads != enc->heads)
     return fail(FMASK_ERR_INVALID, "tile table does not match the encoding");
+  if (a->dtype == FMASK_BF16) {  // 32-bit buffer offsets inside one (batch, K/V head)
+    const int64_t lim = ((int64_t)1 << 31) - 1;
+    if ((a->skv + 64) * a->k_stride[2] * 2 > lim || (a->skv + 64) * a->v_stride[2] * 2 > lim)
+      return fail(FMASK_ERR_UNSUPPORTED, "one K/V head must span less than 2 GiB");
+  }
   TileAttnParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   memcpy(p.qs, a->q_stride, sizeof(p.qs));

@@ -36,6 +36,7 @@ namespace fmask {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -132,26 +133,40 @@ __global__ void __launch_bounds__(64 * NW, 2) k_attn_tile_bf16(TileAttnParams p,
   u32x4 vreg[C::VGROUPS][4];
   i32x4 ivreg = i32x4{0, 0, 0, 0};
 
+  // K/V of this (batch, K/V head) through buffer resources: 32-bit offsets and
+  // hardware range checking (rows at or past skv read as zero).
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)K, (short)0, (int)(((int64_t)(p.skv - 1) * ks2 + D) * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)V, (short)0, (int)(((int64_t)(p.skv - 1) * vs2 + D) * 2), 0x00020000);
+  int koff[C::KLOADS];
+#pragma unroll
+  for (int i = 0; i < C::KLOADS; ++i) {
+    int idx = tid + C::NT * i;
+    koff[i] = (int)((idx / C::KCH) * ks2 * 2 + (idx % C::KCH) * 16);
+  }
+  int voff[C::VGROUPS];
+#pragma unroll
+  for (int i = 0; i < C::VGROUPS; ++i) {
+    int g = tid + C::NT * i;
+    voff[i] = (int)((4 * (g % (BN / 4))) * vs2 * 2 + (g / (BN / 4)) * 16);
+  }
+  const int kstep = (int)(BN * ks2 * 2), vstep = (int)(BN * vs2 * 2), vrow = (int)(vs2 * 2);
+
   auto load_tile = [&](int kt) {
     const int key0 = kt * BN;
+    const int kb0 = kt * kstep, vb0 = kt * vstep;
 #pragma unroll
     for (int i = 0; i < C::KLOADS; ++i) {
-      int idx = tid + C::NT * i;
-      int key = idx / C::KCH, ch = idx % C::KCH;
-      u32x4 x = u32x4{0, 0, 0, 0};
-      if (idx < BN * C::KCH && key0 + key < p.skv) x = *(const u32x4*)(K + (key0 + key) * ks2 + ch * 8);
-      kreg[i] = x;
+      if ((BN * C::KCH) % C::NT == 0 || tid + C::NT * i < BN * C::KCH)
+        kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i] + kb0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < C::VGROUPS; ++i) {
-      int g = tid + C::NT * i;
-      int kg = g % (BN / 4), ch = g / (BN / 4);
+      if (((BN / 4) * C::KCH) % C::NT == 0 || tid + C::NT * i < (BN / 4) * C::KCH) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int key = key0 + 4 * kg + j;
-        u32x4 x = u32x4{0, 0, 0, 0};
-        if (g < (BN / 4) * C::KCH && key < p.skv) x = *(const u32x4*)(V + key * vs2 + ch * 8);
-        vreg[i][j] = x;
+        for (int j = 0; j < 4; ++j)
+          vreg[i][j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[i] + vb0 + j * vrow, 0, 0);
       }
     }
     if (KIND == FMASK_ENC_INTERVALS && tid < BN) {
@@ -270,11 +285,19 @@ __global__ void __launch_bounds__(64 * NW, 2) k_attn_tile_bf16(TileAttnParams p,
 #pragma unroll
       for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[kh][r]);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-    const float mneg = -m_new * c;
-    m_run = m_new;
-    float lsum = 0.f;
+    // Lazy rescale: the running max only moves when some row's max grows by
+    // more than 8 in the exp2 domain, so p = exp2(s c - m c) stays <= 2^8.
+    const float m_cand = fmaxf(m_run, mloc);
+    const bool grow = (m_cand - m_run) * c > 8.f;
+    if (__any(grow)) {
+      const float m_new = grow ? m_cand : m_run;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+    }
+    const float mneg = -m_run * c;
     bf16x8 pf[4];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
@@ -282,17 +305,21 @@ __global__ void __launch_bounds__(64 * NW, 2) k_attn_tile_bf16(TileAttnParams p,
       for (int tp = 0; tp < 2; ++tp) {
         f32x8 pv;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][8 * tp + j], c, mneg));
-          pv[j] = e;
-          lsum += e;
-        }
+        for (int j = 0; j < 8; ++j)
+          pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][8 * tp + j], c, mneg));
         pf[kh * 2 + tp] = __builtin_convertvector(pv, bf16x8);
       }
     }
-    l_run = l_run * alpha + lsum;
+    // Row sums of the bf16 probabilities actually multiplied into V.
+    const bf16x2 one2 = bf16x2{(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x2 pr = bf16x2{pf[ks][2 * j], pf[ks][2 * j + 1]};
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, l_run, false);
+      }
+    }
 
     // O^T += V^T P^T
 #pragma unroll

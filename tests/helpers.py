@@ -8,11 +8,13 @@ from oracle import masks as OM
 
 # Agreement targets: fp32 inputs max abs <= 1e-5; bf16 inputs with fp32
 # accumulation max abs <= 2e-2 and mean abs <= 1e-3 (against the float64 oracle
-# run on the same bf16-rounded inputs).  LSE: fp32 1e-5; bf16 2e-3 (scores are
-# exact products of bf16 values accumulated in fp32, |s| < ~60, so fp32
-# rounding of the running max and log-sum stays far below 1e-3).
+# run on the same bf16-rounded inputs).  LSE (no target is stated for it):
+# fp32 1e-5; bf16 2^-8 + 5e-4: the bf16 kernel sums the bf16-rounded
+# probabilities it multiplies into V (so O is normalised exactly by what it
+# accumulated), and a bf16 rounding moves each term by at most 2^-8 relative,
+# hence log(l) by at most 2^-8; fp32 score and log rounding add < 5e-4.
 TOL = {"f32": dict(max_abs=1e-5, mean_abs=1e-5, lse=1e-5),
-       "bf16": dict(max_abs=2e-2, mean_abs=1e-3, lse=2e-3)}
+       "bf16": dict(max_abs=2e-2, mean_abs=1e-3, lse=2.0 ** -8 + 5e-4)}
 
 
 def to_device(w, arrays, device="cuda"):

@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+COPY_PROBE_BYTES = 256 << 20
 
 
 def _bf16(torch, a):
@@ -73,7 +74,7 @@ def visible_pairs_bitmap(torch, enc):
     return n_full + part.reshape(e.batch, e.heads)
 
 
-def time_workload(torch, fm, synth, name, steps, warmup, headline=False):
+def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5):
     w = synth.workload(name)
     q, k, v = (_bf16(torch, a) if w["dtype"] == "bf16" else torch.from_numpy(a).cuda()
                for a in synth.draw_qkv(w))
@@ -97,8 +98,14 @@ def time_workload(torch, fm, synth, name, steps, warmup, headline=False):
             ev[3].record(stream)
         return enc, tiles
 
-    for _ in range(warmup):
+    # warm-up: at least `warmup` steps and half a second, so clocks have settled
+    t_w = time.perf_counter()
+    n_w = 0
+    while n_w < warmup or time.perf_counter() - t_w < min_warmup_s:
         enc, tiles = step()
+        n_w += 1
+        if n_w % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
@@ -144,6 +151,30 @@ def time_workload(torch, fm, synth, name, steps, warmup, headline=False):
     return rec
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_causal_doc_32k_hbm_bytes.txt")
+ATTN_SOURCE = os.path.join(ROOT, "mask_aware_block_amd", "csrc", "attn_bf16.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the attention kernel from the committed counter
+    summary, or None if the kernel source changed since the counters were taken."""
+    import hashlib
+    try:
+        fields = {}
+        with open(TRAFFIC_PROFILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith(" "):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        with open(ATTN_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if fields.get("kernel_source_sha256") != sha:
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(synth, name, rows, heads):
     """The float64 oracle on a bounded sample of the workload, same FLOP numerator."""
     from oracle import attention as OA
@@ -182,6 +213,10 @@ def main():
                     help="time only the 32K causal-document step (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=32768)
+    ap.add_argument("--min-warmup-s", type=float, default=0.5,
+                    help="warm up for at least this long (clocks settle); 0 for counter runs")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
@@ -194,12 +229,20 @@ def main():
 
     fm.lib()
     torch.cuda.set_device(0)
-    head = time_workload(torch, fm, synth, "causal_doc_32k", args.steps, args.warmup, headline=True)
+    if args.copy_probe:
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    head = time_workload(torch, fm, synth, "causal_doc_32k", args.steps, args.warmup, args.min_warmup_s)
     others = []
     if not args.headline_only:
         for name in ("causal_doc_8k", "shared_question_32k", "band_32k", "band_neg_4k",
                      "block_bitmap_16k", "tree_4k", "selected_key_128k"):
-            others.append(time_workload(torch, fm, synth, name, max(3, args.steps // 2), 2))
+            others.append(time_workload(torch, fm, synth, name, max(3, args.steps // 2), 2,
+                                        min(0.2, args.min_warmup_s)))
             torch.cuda.empty_cache()
 
     achieved = head["effective_flop"] / (head["attn_ms"] * 1e-3) / 1e12
@@ -224,7 +267,7 @@ def main():
                               "attention": head["attn_ms"]},
         "roofline": {"bound": "mfma", "kernel": "k_attn_tile_bf16<128,4,intervals>",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic()},
         "workloads": others,
     }
     if not args.no_cpu_baseline:

@@ -234,11 +234,12 @@ fmask_status fmask_classify(const fmask_encoded *enc, int32_t bm, int32_t bn, vo
  * and LSE_i = -inf.  SKIP tiles are never loaded, FULL tiles are computed
  * without per-element masking, PARTIAL tiles are masked element by element.
  * tiles must come from fmask_classify on the same encoding (NULL for the
- * SELECTED kind, whose kernel walks the lists directly).  The tile shape must be
- * one that fmask_preferred_tile can return for (dtype, d, kind).
+ * SELECTED kind, whose kernel walks the lists directly).  Tile shapes with a
+ * kernel: BF16 INTERVALS 128x64 (preferred), 256x64, 64x64; BF16 BITMAP 64x64
+ * (preferred), 128x64; F32 64x64.  Other shapes return FMASK_ERR_UNSUPPORTED.
  * Supported: BF16 with d in {64, 128} on INTERVALS / BITMAP; F32 with d in
- * {64, 128} on INTERVALS / BITMAP; BF16 with d == 256 and sel_cells == 32 on
- * SELECTED.                                                                     */
+ * {64, 128} on INTERVALS / BITMAP; BF16 with d in {128, 256}, sel_cells == 32
+ * and hq / hkv in {1, 2, 4, 8, 16} on SELECTED.                                 */
 fmask_status fmask_attn_fwd(const fmask_attn_args *args, const void *q, const void *k,
                             const void *v, void *o, float *lse, const fmask_encoded *enc,
                             const fmask_tiles *tiles, void *stream);

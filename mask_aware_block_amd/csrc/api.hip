@@ -220,6 +220,15 @@ TileLayout tile_layout(const fmask_encoded* e, int32_t bm, int32_t bn) {
   return T;
 }
 
+// Tile shapes with a kernel: bf16 intervals 256x64 (two ping-pong wave groups),
+// 128x64 and 64x64; bf16 bitmap 64x64 and 128x64; fp32 64x64.
+bool tile_supported(int32_t dtype, int32_t kind, int32_t bm, int32_t bn) {
+  if (bn != 64) return false;
+  if (dtype == FMASK_F32) return bm == 64;
+  if (kind == FMASK_ENC_INTERVALS) return bm == 256 || bm == 128 || bm == 64;
+  return bm == 64 || bm == 128;
+}
+
 void preferred(int32_t dtype, int32_t d, int32_t kind, int32_t* bm, int32_t* bn) {
   (void)d;
   *bn = 64;
@@ -479,9 +488,13 @@ fmask_status fmask_attn_fwd(const fmask_attn_args* a, const void* q, const void*
   int32_t bm = 0, bn = 0;
   if ((a->dtype != FMASK_BF16 && a->dtype != FMASK_F32) || (a->d != 64 && a->d != 128))
     return fail(FMASK_ERR_UNSUPPORTED, "tile kernels: d in {64, 128}");
-  preferred(a->dtype, a->d, enc->kind, &bm, &bn);
-  if (tiles->bm != bm || tiles->bn != bn)
-    return fail(FMASK_ERR_UNSUPPORTED, "tile table is %dx%d, the kernel needs %dx%d", tiles->bm, tiles->bn, bm, bn);
+  bm = tiles->bm;
+  bn = tiles->bn;
+  if (!tile_supported(a->dtype, enc->kind, bm, bn)) {
+    int32_t pbm = 0, pbn = 0;
+    preferred(a->dtype, a->d, enc->kind, &pbm, &pbn);
+    return fail(FMASK_ERR_UNSUPPORTED, "no kernel for %dx%d tiles here (preferred: %dx%d)", bm, bn, pbm, pbn);
+  }
   if (tiles->nqt != ceil_div(a->sq, bm) || tiles->nkt != ceil_div(a->skv, bn) ||
       tiles->batch != enc->batch || tiles->heads != enc->heads)
     return fail(FMASK_ERR_INVALID, "tile table does not match the encoding");
@@ -510,7 +523,10 @@ fmask_status fmask_attn_fwd(const fmask_attn_args* a, const void* q, const void*
   p.bstate = enc->blk_state; p.bindex = enc->blk_index; p.bbits = enc->blk_bits;
   p.nbq = (int32_t)enc->nbq; p.nbk = (int32_t)enc->nbk;
   if (a->sq == 0) return FMASK_OK;
-  hipError_t e = a->dtype == FMASK_BF16 ? launch_attn_tile_bf16(p, a->d, s) : launch_attn_tile_f32(p, a->d, s);
+  hipError_t e;
+  if (a->dtype == FMASK_F32) e = launch_attn_tile_f32(p, a->d, s);
+  else if (bm == 256) e = launch_attn_pp_bf16(p, a->d, s);
+  else e = launch_attn_tile_bf16(p, a->d, s);
   return hip_status(e, "attention kernel");
 }
 

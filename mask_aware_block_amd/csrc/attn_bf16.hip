@@ -7,7 +7,7 @@
 // by element from the interval or bitmap encoding.  SKIP tiles are never
 // loaded.  This is the behaviour the FlashMask rebuttal page and the Binary
 // Block Masking abstract ask of a mask-aware kernel; the register and LDS
-// layout below is our own, designed for CDNA4.
+// layout below is our own, designed for CDNA4 (gfx950).
 //
 // Per wave and key tile:
 //   S^T[64 keys x 32 rows] = K Q^T   v_mfma_f32_32x32x16_bf16, A = K rows from
@@ -16,51 +16,67 @@
 //                                     so row max / sum stay in-lane plus one
 //                                     exchange with lane l ^ 32.
 //   online softmax in the exp2 domain (scale * log2(e) folded into one FMA),
-//   running max starting at -FLT_MAX so exp(-inf - -inf) never happens.
-//   O^T[d x 32 rows] += V^T P^T       A = V^T from LDS, B = P^T straight from
-//                                     the S^T accumulators converted to bf16.
-// V is written to LDS transposed (d-major) with the keys of every 16-key group
-// permuted (bits 2 and 3 of the key index swapped) so that the 8 keys one lane
-// needs for a PV step are contiguous: one ds_read_b128 per MFMA operand.
-// K/V tiles are double-buffered in LDS; the next tile's global loads are in
-// flight while the current tile is computed.  Both LDS arrays are XOR-
-// swizzled in 16-byte chunks so the MFMA operand reads are conflict-free.
+//   running max from -FLT_MAX (exp(-inf - -inf) never happens), moved only
+//   when a row's max grows by more than 8 (exp2 units), so the O rescale is
+//   rare; row sums are taken over the bf16 probabilities fed to the MFMA.
+//   O^T[d x 32 rows] += V^T P^T       A = V^T fragments read from the row-major
+//                                     V tile with the gfx950 transposing LDS
+//                                     read (ds_read_b64_tr_b16), B = P^T taken
+//                                     straight from the S^T accumulators.
+// K and V tiles go from HBM to LDS with direct-to-LDS buffer loads (no VGPR
+// staging), double-buffered: the next tile's loads are in flight while the
+// current one is computed.  Buffer range checking turns rows past the end of
+// the sequence into zeros.  Both LDS tiles are XOR-swizzled in 16-byte chunks
+// (the swizzle is applied through the global addresses each lane loads), so
+// the MFMA operand reads are free of bank conflicts.
 //
 // GQA: query head h reads K/V head h / group; the group's heads of one query
 // tile are consecutive work items placed on the same XCD (L2 reuse of K/V).
 #include <float.h>
 
+#include "device_util.h"
 #include "internal.h"
 
 namespace fmask {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
+#define LDS_AS FMASK_LDS_AS
+
 constexpr int BN = 64;
+constexpr int kListLds = 2048;  // tile-list entries staged in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D, int NW>
 struct Cfg {
   static constexpr int BM = 32 * NW;
   static constexpr int NT = 64 * NW;
-  static constexpr int KCH = D / 8;                 // 16-byte chunks per K row
+  static constexpr int KCH = D / 8;                  // 16-byte chunks per row
   static constexpr int K_BYTES = BN * D * 2;
-  static constexpr int V_BYTES = D * BN * 2;
+  static constexpr int V_BYTES = BN * D * 2;
   static constexpr int IV_BYTES = BN * 16;
   static constexpr int STAGE = K_BYTES + V_BYTES + IV_BYTES;
-  static constexpr int KLOADS = (BN * KCH + NT - 1) / NT;        // 16-byte K chunks per thread
-  static constexpr int VGROUPS = ((BN / 4) * KCH + NT - 1) / NT;  // (4 keys x 16 bytes) per thread
+  static constexpr int CHUNKS = BN * KCH;            // 16-byte chunks per K (or V) tile
+  static constexpr int LOADS = CHUNKS / NT;          // direct-to-LDS loads per thread per tile
+  static_assert(CHUNKS % NT == 0, "tile must split evenly over the workgroup");
 };
 
-__device__ inline int swap23(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
-__device__ inline int vswz(int d) { return (d ^ (d >> 3)) & 7; }
+// Chunk swizzle of the K tile: conflict-free 16-byte reads of 32 rows.
+template <int KCH>
+__device__ inline int kswz(int key) { return key & (KCH - 1); }
+// Chunk swizzle of the V tile: the transposing reads of one instruction touch
+// 8 consecutive rows x 64 bytes; spread them over all banks.
+template <int KCH>
+__device__ inline int vswz(int key) {
+  return KCH == 16 ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
+}
 
 struct Item {
   int b, h, kvh, mb, mh, qt, row;
@@ -92,8 +108,9 @@ __device__ inline int logical_item(int gsz) {
 
 template <int D, int NW, int KIND>
 __global__ void __launch_bounds__(64 * NW, 2) k_attn_tile_bf16(TileAttnParams p, int gsz) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using C = Cfg<D, NW>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
 
   const int l = logical_item(gsz);
   if (l >= p.n_items) return;
@@ -111,6 +128,16 @@ __global__ void __launch_bounds__(64 * NW, 2) k_attn_tile_bf16(TileAttnParams p,
   const int cnt = p.count[it.row];
   const int64_t ks2 = p.ks[2], vs2 = p.vs[2];
 
+  // Rows past the end may be read (as zeros) but never hold stale NaN bits.
+  for (int i = tid; i < 2 * C::STAGE / 16; i += C::NT) ((i32x4*)smem)[i] = i32x4{0, 0, 0, 0};
+  // The tile list goes to LDS once (its entries are then read without any
+  // wait on the memory counters that the tile loads use).
+  __shared__ int32_t lst[kListLds];
+  for (int i = tid; i < min(cnt, kListLds); i += C::NT) lst[i] = list[i];
+  auto entry = [&](int i) -> int {
+    return i < kListLds ? __builtin_amdgcn_readfirstlane(lst[i]) : sload_wait(list + i);
+  };
+
   // Q^T as MFMA B operand: lane holds row qrow, d = 16 t + 8 half + 0..7.
   bf16x8 qf[D / 16];
 #pragma unroll
@@ -118,6 +145,10 @@ __global__ void __launch_bounds__(64 * NW, 2) k_attn_tile_bf16(TileAttnParams p,
     if (qrow < p.sq) qf[t] = *(const bf16x8*)(Q + qrow * p.qs[2] + 16 * t + 8 * half);
     else qf[t] = bf16x8{};
   }
+
+  // Nothing the compiler tracks may stay pending once untracked tile loads
+  // are in flight.
+  wait_all();
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -129,106 +160,77 @@ __global__ void __launch_bounds__(64 * NW, 2) k_attn_tile_bf16(TileAttnParams p,
   const int brow = (q0 + w * 32) / kBlk;
   const size_t bbase = ((size_t)it.mb * p.mh + it.mh) * p.nbq;
 
-  u32x4 kreg[C::KLOADS];
-  u32x4 vreg[C::VGROUPS][4];
+  // Buffer resources over this (batch, K/V head): 32-bit offsets, and rows at
+  // or past skv fall outside the range and read as zero.
+  const rsrc_t krs = make_rsrc(K, ((int64_t)(p.skv - 1) * ks2 + D) * 2);
+  const rsrc_t vrs = make_rsrc(V, ((int64_t)(p.skv - 1) * vs2 + D) * 2);
+
+  // Direct-to-LDS loads: instruction n of wave w fills LDS chunks
+  // P = (w * LOADS + n) * 64 + lane; chunk P holds row P / KCH, physical chunk
+  // P % KCH, i.e. logical chunk (P % KCH) ^ swizzle(row) of that row.
+  int kgo[C::LOADS], vgo[C::LOADS];
+#pragma unroll
+  for (int n = 0; n < C::LOADS; ++n) {
+    const int P = (w * C::LOADS + n) * 64 + lane;
+    const int key = P / C::KCH, pc = P % C::KCH;
+    kgo[n] = (int)(key * ks2 * 2 + ((pc ^ kswz<C::KCH>(key)) * 16));
+    vgo[n] = (int)(key * vs2 * 2 + ((pc ^ vswz<C::KCH>(key)) * 16));
+  }
+  const int kstep = (int)(BN * ks2 * 2), vstep = (int)(BN * vs2 * 2);
+
+  // PV operand: two transposing reads per MFMA.  Lane (group g = lane / 16,
+  // r = (lane % 16) / 4, c4 = lane % 4) addresses row base + 4 (g / 2) + r and
+  // the 8 bytes at d = 32 db + 16 (g % 2) + 4 c4; the read hands lane l the four
+  // rows at d = 32 db + (l % 32), i.e. the keys of its P^T slots.
+  const int tg = lane >> 4, tr = (lane >> 2) & 3, tc4 = lane & 3;
+  const int vrow_l = 4 * (tg >> 1) + tr;  // row offset of this lane inside a 16-key group
+  int vofs[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int ch = 4 * db + 2 * (tg & 1) + (tc4 >> 1);
+    vofs[db] = vrow_l * (D * 2) + ((ch ^ vswz<C::KCH>(vrow_l)) * 16) + (tc4 & 1) * 8;
+  }
+
   i32x4 ivreg = i32x4{0, 0, 0, 0};
 
-  // K/V of this (batch, K/V head) through buffer resources: 32-bit offsets and
-  // hardware range checking (rows at or past skv read as zero).
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)K, (short)0, (int)(((int64_t)(p.skv - 1) * ks2 + D) * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)V, (short)0, (int)(((int64_t)(p.skv - 1) * vs2 + D) * 2), 0x00020000);
-  int koff[C::KLOADS];
-#pragma unroll
-  for (int i = 0; i < C::KLOADS; ++i) {
-    int idx = tid + C::NT * i;
-    koff[i] = (int)((idx / C::KCH) * ks2 * 2 + (idx % C::KCH) * 16);
-  }
-  int voff[C::VGROUPS];
-#pragma unroll
-  for (int i = 0; i < C::VGROUPS; ++i) {
-    int g = tid + C::NT * i;
-    voff[i] = (int)((4 * (g % (BN / 4))) * vs2 * 2 + (g / (BN / 4)) * 16);
-  }
-  const int kstep = (int)(BN * ks2 * 2), vstep = (int)(BN * vs2 * 2), vrow = (int)(vs2 * 2);
-
-  auto load_tile = [&](int kt) {
-    const int key0 = kt * BN;
+  // LDS byte address where this wave's loads of stage 0 start (scalar)
+  const int lds_w = __builtin_amdgcn_readfirstlane(lds_addr(smem) + w * C::LOADS * 1024);
+  auto issue_tile = [&](int kt, int buf) {
+    const int kb = lds_w + buf * C::STAGE, vb = kb + C::K_BYTES;
     const int kb0 = kt * kstep, vb0 = kt * vstep;
 #pragma unroll
-    for (int i = 0; i < C::KLOADS; ++i) {
-      if ((BN * C::KCH) % C::NT == 0 || tid + C::NT * i < BN * C::KCH)
-        kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i] + kb0, 0, 0);
-    }
+    for (int n = 0; n < C::LOADS; ++n) dma16(krs, kgo[n] + kb0, kb + n * 1024);
 #pragma unroll
-    for (int i = 0; i < C::VGROUPS; ++i) {
-      if (((BN / 4) * C::KCH) % C::NT == 0 || tid + C::NT * i < (BN / 4) * C::KCH) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          vreg[i][j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[i] + vb0 + j * vrow, 0, 0);
-      }
-    }
+    for (int n = 0; n < C::LOADS; ++n) dma16(vrs, vgo[n] + vb0, vb + n * 1024);
     if (KIND == FMASK_ENC_INTERVALS && tid < BN) {
-      int key = key0 + tid;
+      const int key = kt * BN + tid;
       if (key < p.skv) {
         const int32_t* col = p.iv + ((size_t)it.mb * p.mh + it.mh) * 4 * (size_t)p.skv;
-        int32_t uts = col[key], ute = col[p.skv + key];
-        int32_t lts = col[2 * (size_t)p.skv + key], lte = col[3 * (size_t)p.skv + key];
-        ivreg = i32x4{uts, ute - uts, lts, lte - lts};
+        // raw values only: the loads stay in flight behind the tile's loads
+        ivreg = i32x4{col[key], col[p.skv + key], col[2 * (size_t)p.skv + key],
+                      col[3 * (size_t)p.skv + key]};
       } else {
-        ivreg = i32x4{0, 0x7fffffff, 0, 0};  // beyond the keys: masked for every row
+        ivreg = i32x4{0, 0x7fffffff, 0, 0};  // past the keys: masked for every row
       }
     }
   };
-
-  auto store_tile = [&](int buf) {
-    char* kb = smem + buf * C::STAGE;
-    char* vb = kb + C::K_BYTES;
-#pragma unroll
-    for (int i = 0; i < C::KLOADS; ++i) {
-      int idx = tid + C::NT * i;
-      if (idx < BN * C::KCH) {
-        int key = idx / C::KCH, ch = idx % C::KCH;
-        *(u32x4*)(kb + key * (D * 2) + ((ch ^ (key & (C::KCH - 1))) * 16)) = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::VGROUPS; ++i) {
-      int g = tid + C::NT * i;
-      if (g < (BN / 4) * C::KCH) {
-        int kg = g % (BN / 4), ch = g / (BN / 4);
-        int pos = swap23(4 * kg);
-        int pch = pos >> 3, pin = (pos & 7) * 2;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          int d = ch * 8 + e;
-          int m = e >> 1;
-          uint32_t a0 = vreg[i][0][m], a1 = vreg[i][1][m], a2 = vreg[i][2][m], a3 = vreg[i][3][m];
-          u32x2 out;
-          if (e & 1) {
-            out[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-            out[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-          } else {
-            out[0] = (a0 & 0xffffu) | (a1 << 16);
-            out[1] = (a2 & 0xffffu) | (a3 << 16);
-          }
-          *(u32x2*)(vb + d * (BN * 2) + ((pch ^ vswz(d)) * 16) + pin) = out;
-        }
-      }
-    }
-    if (KIND == FMASK_ENC_INTERVALS && tid < BN) *(i32x4*)(vb + C::V_BYTES + tid * 16) = ivreg;
+  // intervals to LDS as (start, length) pairs, after the tile's compute
+  auto store_iv = [&](int buf) {
+    if (KIND == FMASK_ENC_INTERVALS && tid < BN)
+      *(i32x4*)(smem + buf * C::STAGE + C::K_BYTES + C::V_BYTES + tid * 16) =
+          i32x4{ivreg[0], ivreg[1] - ivreg[0], ivreg[2], ivreg[3] - ivreg[2]};
   };
 
   auto compute_tile = [&](int buf, int kt, bool full) {
     const char* kb = smem + buf * C::STAGE;
     const char* vb = kb + C::K_BYTES;
+    const char* ivb = vb + C::V_BYTES;
     const bool ragged = (kt + 1) * BN > p.skv;
 
-    if (q0 + w * 32 >= p.sq) return;  // every row of this wave lies past the end
     bool need_mask = !full || ragged;
     uint64_t word = ~0ull;
     if (KIND == FMASK_ENC_BITMAP) {
+      if (q0 + w * 32 >= p.sq) return;  // every row of this wave lies past the end
       uint8_t st = p.bstate[(bbase + brow) * p.nbk + kt];
       if (st == FMASK_SKIP) return;  // nothing visible in this wave's rows
       if (st == FMASK_PARTIAL) {
@@ -250,8 +252,8 @@ __global__ void __launch_bounds__(64 * NW, 2) k_attn_tile_bf16(TileAttnParams p,
       const int key = kh * 32 + l32;
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
-        int ch = 2 * t + half;
-        bf16x8 a = *(const bf16x8*)(kb + key * (D * 2) + ((ch ^ (key & (C::KCH - 1))) * 16));
+        const int ch = 2 * t + half;
+        bf16x8 a = *(const bf16x8*)(kb + key * (D * 2) + ((ch ^ kswz<C::KCH>(key)) * 16));
         s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kh], 0, 0, 0);
       }
     }
@@ -263,10 +265,10 @@ __global__ void __launch_bounds__(64 * NW, 2) k_attn_tile_bf16(TileAttnParams p,
         for (int rg = 0; rg < 4; ++rg) {
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            int key = kh * 32 + 8 * rg + 4 * half + r4;  // key index inside the tile
+            const int key = kh * 32 + 8 * rg + 4 * half + r4;  // key index inside the tile
             bool masked;
             if (KIND == FMASK_ENC_INTERVALS) {
-              i32x4 iv = *(const i32x4*)(vb + C::V_BYTES + key * 16);
+              i32x4 iv = *(const i32x4*)(ivb + key * 16);
               masked = ((uint32_t)(qrow - iv[0]) < (uint32_t)iv[1]) ||
                        ((uint32_t)(qrow - iv[2]) < (uint32_t)iv[3]);
             } else {
@@ -285,8 +287,6 @@ __global__ void __launch_bounds__(64 * NW, 2) k_attn_tile_bf16(TileAttnParams p,
 #pragma unroll
       for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[kh][r]);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    // Lazy rescale: the running max only moves when some row's max grows by
-    // more than 8 in the exp2 domain, so p = exp2(s c - m c) stays <= 2^8.
     const float m_cand = fmaxf(m_run, mloc);
     const bool grow = (m_cand - m_run) * c > 8.f;
     if (__any(grow)) {
@@ -321,35 +321,46 @@ __global__ void __launch_bounds__(64 * NW, 2) k_attn_tile_bf16(TileAttnParams p,
       }
     }
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T; P^T step ks covers keys 16 ks .. 16 ks + 15.
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const int d = db * 32 + l32;
-      const char* vrow = vb + d * (BN * 2);
-      const int sw = vswz(d);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        int ch = 2 * ks + half;  // = 4 kh + 2 tp + half
-        bf16x8 a = *(const bf16x8*)(vrow + ((ch ^ sw) * 16));
+        const char* a0 = vb + vofs[db] + (16 * ks) * (D * 2);
+        bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)a0);
+        bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(a0 + 8 * (D * 2)));
+        bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], acc[db], 0, 0, 0);
       }
     }
   };
 
+  __syncthreads();  // LDS cleared and the list staged before any tile load lands
+  int e_cur = 0, e_next = 0;
   if (cnt > 0) {
-    load_tile(list[0] & 0x7fffffff);
-    store_tile(0);
+    e_cur = entry(0);
+    if (cnt > 1) e_next = entry(1);
+    issue_tile(e_cur & 0x7fffffff, 0);
+    wait_all();  // tile 0 and its intervals
+    store_iv(0);
   }
+  wait_all();
   __syncthreads();
   for (int i = 0; i < cnt; ++i) {
-    const uint32_t e = (uint32_t)list[i];
-    const int kt = (int)(e & 0x7fffffffu);
-    const bool full = (e & FMASK_LIST_FULL_BIT) != 0;
+    const int kt = e_cur & 0x7fffffff;
+    const bool full = (e_cur & (int)FMASK_LIST_FULL_BIT) != 0;
     const bool more = i + 1 < cnt;
-    if (more) load_tile(list[i + 1] & 0x7fffffff);
+    int e_after = 0;
+    if (more) {
+      if (i + 2 < cnt) e_after = entry(i + 2);
+      issue_tile(e_next & 0x7fffffff, (i + 1) & 1);
+    }
     compute_tile(i & 1, kt, full);
-    if (more) store_tile((i + 1) & 1);
-    __syncthreads();
+    if (more) store_iv((i + 1) & 1);
+    wait_all();  // tile i+1 landed, its intervals written
+    barrier();
+    e_cur = e_next;
+    e_next = e_after;
   }
 
   // Epilogue: O = O / l, zero rows for l = 0, LSE in natural log.
@@ -361,9 +372,7 @@ __global__ void __launch_bounds__(64 * NW, 2) k_attn_tile_bf16(TileAttnParams p,
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        int d0 = db * 32 + 8 * rg + 4 * half;
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const int d0 = db * 32 + 8 * rg + 4 * half;
         f32x4 x = f32x4{acc[db][4 * rg], acc[db][4 * rg + 1], acc[db][4 * rg + 2],
                         acc[db][4 * rg + 3]} * inv;
         *(bf16x4*)(O + d0) = __builtin_convertvector(x, bf16x4);
@@ -374,6 +383,7 @@ __global__ void __launch_bounds__(64 * NW, 2) k_attn_tile_bf16(TileAttnParams p,
       p.lse[((int64_t)it.b * p.hq + it.h) * p.sq + qrow] = lse;
     }
   }
+#endif
 }
 
 template <int D, int NW>

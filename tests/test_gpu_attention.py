@@ -104,6 +104,25 @@ def test_small_bitmap_and_raw_intervals(dtype):
     _dense_check(w, spec, "raw intervals per head")
 
 
+@pytest.mark.parametrize("bm", [256, 128, 64])
+def test_interval_tile_shapes(bm):
+    """Every bf16 interval kernel (256-row ping-pong, 128-row, 64-row) on ragged shapes."""
+    for S, K, spec in [(333, 333, dict(family="causal_document", sq=333, skv=333,
+                                       cu_seg=np.array([0, 70, 200, 333], dtype=np.int32))),
+                       (700, 700, dict(family="band", sq=700, skv=700, pre=100, next=5)),
+                       (300, 520, dict(family="causal_bottom_right", sq=300, skv=520))]:
+        w = _small("bf16", 128, S, K, Hq=8, Hkv=2, B=2)
+        arrays = synth.draw_qkv(w)
+        q, k, v = to_device(w, arrays)
+        enc = fm.encode(spec)
+        tiles = fm.classify(enc, bm, 64)
+        o, lse = fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"])
+        torch.cuda.synchronize()
+        qq, kk, vv = (to_f64(w, a) for a in arrays)
+        ro, rl = OA.attention_dense(qq, kk, vv, OA.spec_vis_fn(spec), w["scale"])
+        compare(w, o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"bm {bm} {spec['family']}")
+
+
 def test_gqa_groups_and_batch():
     for Hq, Hkv in [(8, 1), (8, 8), (6, 2)]:
         w = _small("bf16", 128, 257, 257, Hq=Hq, Hkv=Hkv, B=2)

@@ -152,7 +152,8 @@ def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5):
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_causal_doc_32k_hbm_bytes.txt")
-ATTN_SOURCE = os.path.join(ROOT, "mask_aware_block_amd", "csrc", "attn_bf16.hip")
+ATTN_SOURCES = [os.path.join(ROOT, "mask_aware_block_amd", "csrc", f)
+                for f in ("attn_bf16.hip", "device_util.h")]
 
 
 def measured_traffic():
@@ -166,8 +167,11 @@ def measured_traffic():
                 if ":" in line and not line.startswith(" "):
                     k, v = line.split(":", 1)
                     fields[k.strip()] = v.strip()
-        with open(ATTN_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        h = hashlib.sha256()
+        for path in ATTN_SOURCES:
+            with open(path, "rb") as f:
+                h.update(f.read())
+        sha = h.hexdigest()
         if fields.get("kernel_source_sha256") != sha:
             return None
         return float(fields["hbm_bytes_per_launch"])

@@ -1,0 +1,140 @@
+"""C-ABI checks that need no GPU: libfmask.so loads, exports every function
+include/fmask.h declares, its structs have the layout the binding assumes, and
+host-detectable errors come back as status codes before anything is launched."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import mask_aware_block_amd as fm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fmask.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_]\w*\s*\**\s*(fmask_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for must in ("fmask_encode", "fmask_classify", "fmask_attn_fwd", "fmask_encode_bytes",
+                 "fmask_classify_bytes"):
+        assert must in names
+    assert set(names) == set(fm.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = fm.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", fm.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "sizes.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "fmask.h"\n'
+        "int main(void) {\n"
+        '  printf("%zu %zu %zu %zu\\n", sizeof(fmask_mask_desc), sizeof(fmask_encoded),'
+        " sizeof(fmask_tiles), sizeof(fmask_attn_args));\n"
+        '  printf("%zu %zu %zu %zu\\n", offsetof(fmask_mask_desc, raw_intervals),'
+        " offsetof(fmask_encoded, sel_n), offsetof(fmask_tiles, order), offsetof(fmask_attn_args, scale));\n"
+        "  return 0;\n}\n")
+    exe = tmp_path / "sizes"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src),
+                    "-o", str(exe)], check=True)
+    lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    sizes = [int(x) for x in lines[0].split()]
+    offs = [int(x) for x in lines[1].split()]
+    assert sizes == [ctypes.sizeof(fm.MaskDesc), ctypes.sizeof(fm.Encoded), ctypes.sizeof(fm.Tiles),
+                     ctypes.sizeof(fm.AttnArgs)]
+    assert offs == [fm.MaskDesc.raw_intervals.offset, fm.Encoded.sel_n.offset, fm.Tiles.order.offset,
+                    fm.AttnArgs.scale.offset]
+
+
+def test_status_strings_and_preferred_tiles():
+    L = fm.lib()
+    for s in (fm.OK, fm.ERR_INVALID, fm.ERR_UNSUPPORTED, fm.ERR_CAPACITY, fm.ERR_HIP):
+        assert L.fmask_status_str(s)
+    assert fm.preferred_tile("bf16", 128, fm.ENC_INTERVALS) == (128, 64)
+    assert fm.preferred_tile("bf16", 128, fm.ENC_BITMAP) == (64, 64)
+    assert fm.preferred_tile("f32", 64, fm.ENC_INTERVALS) == (64, 64)
+    bm, bn = ctypes.c_int32(), ctypes.c_int32()
+    assert L.fmask_preferred_tile(1, 96, fm.ENC_INTERVALS, ctypes.byref(bm), ctypes.byref(bn)) == fm.ERR_UNSUPPORTED
+    assert L.fmask_preferred_tile(1, 128, fm.ENC_SELECTED, ctypes.byref(bm), ctypes.byref(bn)) == fm.ERR_INVALID
+
+
+def _desc(**kw):
+    d = fm.MaskDesc()
+    d.family, d.batch, d.heads = kw.pop("family"), kw.pop("batch", 1), kw.pop("heads", 1)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_encode_bytes_and_host_validation():
+    L = fm.lib()
+    ok = _desc(family=1, sq=1000, skv=1000)
+    assert L.fmask_encode_bytes(ctypes.byref(ok)) >= 4 * 1000 * 4
+    bad_sizes = _desc(family=1, sq=-1, skv=10)
+    assert L.fmask_encode_bytes(ctypes.byref(bad_sizes)) == 0
+    cu = np.array([0, 64, 32, 256], dtype=np.int32)  # not increasing
+    doc = _desc(family=3, sq=256, skv=256, cu_seg=cu.ctypes.data, n_seg=3)
+    assert L.fmask_encode_bytes(ctypes.byref(doc)) == 0
+    enc = fm.Encoded()
+    st = L.fmask_encode(ctypes.byref(doc), None, 0, ctypes.byref(enc), None)
+    assert st == fm.ERR_INVALID and L.fmask_last_error()
+    cu_short = np.array([0, 64, 200], dtype=np.int32)  # last offset != sq
+    doc2 = _desc(family=3, sq=256, skv=256, cu_seg=cu_short.ctypes.data, n_seg=2)
+    assert L.fmask_encode(ctypes.byref(doc2), None, 0, ctypes.byref(enc), None) == fm.ERR_INVALID
+    par = np.array([-1, 0, 2], dtype=np.int32)  # parent not before child
+    tree = _desc(family=6, sq=67, skv=67, tree_parent=par.ctypes.data, tree_prefix=64, tree_n=3)
+    assert L.fmask_encode(ctypes.byref(tree), None, 0, ctypes.byref(enc), None) == fm.ERR_INVALID
+    unknown = _desc(family=42, sq=8, skv=8)
+    assert L.fmask_encode(ctypes.byref(unknown), None, 0, ctypes.byref(enc), None) == fm.ERR_INVALID
+    # valid description, but no output buffer / too small: rejected before any launch
+    assert L.fmask_encode(ctypes.byref(ok), None, 0, ctypes.byref(enc), None) == fm.ERR_INVALID
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: the size check fails first
+    assert L.fmask_encode(ctypes.byref(ok), fake, 16, ctypes.byref(enc), None) == fm.ERR_CAPACITY
+
+
+def test_classify_and_attn_host_validation():
+    L = fm.lib()
+    enc = fm.Encoded()
+    enc.kind, enc.batch, enc.heads, enc.sq, enc.skv = fm.ENC_INTERVALS, 1, 1, 512, 512
+    enc.intervals = 1 << 20
+    assert L.fmask_classify_bytes(ctypes.byref(enc), 128, 64) > 0
+    assert L.fmask_classify_bytes(ctypes.byref(enc), 100, 64) == 0  # not a multiple of 16
+    assert L.fmask_classify_bytes(ctypes.byref(enc), 512, 64) == 0  # above 256
+    tiles = fm.Tiles()
+    fake = ctypes.c_void_p(1 << 20)
+    assert L.fmask_classify(ctypes.byref(enc), 128, 64, fake, 16, ctypes.byref(tiles), None) == fm.ERR_CAPACITY
+    enc_b = fm.Encoded()
+    enc_b.kind, enc_b.batch, enc_b.heads, enc_b.sq, enc_b.skv = fm.ENC_BITMAP, 1, 1, 512, 512
+    assert L.fmask_classify_bytes(ctypes.byref(enc_b), 96, 64) == 0  # bitmap tiles: multiples of 64
+
+    a = fm.AttnArgs()
+    a.dtype, a.b, a.hq, a.hkv, a.sq, a.skv, a.d, a.scale = 1, 1, 6, 4, 512, 512, 128, 0.08
+    p = ctypes.c_void_p(1 << 20)
+    assert L.fmask_attn_fwd(ctypes.byref(a), p, p, p, p, None, ctypes.byref(enc), ctypes.byref(tiles),
+                            None) == fm.ERR_INVALID  # hq % hkv != 0
+    a.hq = 8
+    a.sq = 256
+    assert L.fmask_attn_fwd(ctypes.byref(a), p, p, p, p, None, ctypes.byref(enc), ctypes.byref(tiles),
+                            None) == fm.ERR_INVALID  # differs from the encoding
+    a.sq, a.dtype = 512, 7
+    assert L.fmask_attn_fwd(ctypes.byref(a), p, p, p, p, None, ctypes.byref(enc), ctypes.byref(tiles),
+                            None) == fm.ERR_UNSUPPORTED
+    a.dtype = 1
+    assert L.fmask_attn_fwd(ctypes.byref(a), None, p, p, p, None, ctypes.byref(enc), ctypes.byref(tiles),
+                            None) == fm.ERR_INVALID  # null tensor

@@ -153,7 +153,7 @@ def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5):
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_causal_doc_32k_hbm_bytes.txt")
 ATTN_SOURCES = [os.path.join(ROOT, "mask_aware_block_amd", "csrc", f)
-                for f in ("attn_bf16.hip", "device_util.h")]
+                for f in ("attn_bf16_o3.hip", "device_util.h")]
 
 
 def measured_traffic():
@@ -269,7 +269,7 @@ def main():
         "fraction_of_peak": head["effective_tflops"] / PEAK_BF16_TFLOPS,
         "step_breakdown_ms": {"encode": head["encode_ms"], "classify": head["classify_ms"],
                               "attention": head["attn_ms"]},
-        "roofline": {"bound": "mfma", "kernel": "k_attn_tile_bf16<128,4,intervals>",
+        "roofline": {"bound": "mfma", "kernel": "k_attn_o3<128> (128x64 tiles, intervals)",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic()},
         "workloads": others,

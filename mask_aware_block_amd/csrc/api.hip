@@ -525,7 +525,7 @@ fmask_status fmask_attn_fwd(const fmask_attn_args* a, const void* q, const void*
   if (a->sq == 0) return FMASK_OK;
   hipError_t e;
   if (a->dtype == FMASK_F32) e = launch_attn_tile_f32(p, a->d, s);
-  else if (bm == 256) e = launch_attn_pp_bf16(p, a->d, s);
+  else if (bm == 128 && enc->kind == FMASK_ENC_INTERVALS) e = launch_attn_o3_bf16(p, a->d, s);
   else e = launch_attn_tile_bf16(p, a->d, s);
   return hip_status(e, "attention kernel");
 }

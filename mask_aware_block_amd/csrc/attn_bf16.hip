@@ -78,6 +78,10 @@ __device__ inline int vswz(int key) {
   return KCH == 16 ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
 }
 
+__device__ inline int overlap(int a0, int a1, int b0, int b1) {
+  return max(0, min(a1, b1) - max(a0, b0));
+}
+
 struct Item {
   int b, h, kvh, mb, mh, qt, row;
 };
@@ -244,6 +248,17 @@ __global__ void __launch_bounds__(64 * NW, 2) k_attn_tile_bf16(TileAttnParams p,
       }
     }
 
+    if (KIND == FMASK_ENC_INTERVALS && need_mask) {
+      // This wave's own state for the tile (lane = key column): its 32 rows
+      // may see nothing (skip the tile) or everything (no element mask).
+      // Keys past skv carry an all-rows interval and count as masked.
+      const i32x4 iv = *(const i32x4*)(ivb + lane * 16);
+      const int a0 = q0 + w * 32, a1 = min(a0 + 32, p.sq), n = max(0, a1 - a0);
+      const int cm = overlap(a0, a1, iv[0], iv[0] + iv[1]) + overlap(a0, a1, iv[2], iv[2] + iv[3]);
+      if (__ballot(cm == n) == ~0ull) return;
+      if (__ballot(cm != 0) == 0ull) need_mask = false;
+    }
+
     // S^T = K Q^T for the two 32-key halves of the tile.
     f32x16 s[2];
 #pragma unroll
@@ -405,8 +420,10 @@ hipError_t launch_dn(const TileAttnParams& p, hipStream_t s) {
 
 hipError_t launch_attn_tile_bf16(const TileAttnParams& p, int32_t d, hipStream_t s) {
   if (p.bn != BN) return hipErrorInvalidValue;
+  if (d == 128 && p.bm == 256) return launch_dn<128, 8>(p, s);
   if (d == 128 && p.bm == 128) return launch_dn<128, 4>(p, s);
   if (d == 128 && p.bm == 64) return launch_dn<128, 2>(p, s);
+  if (d == 64 && p.bm == 256) return launch_dn<64, 8>(p, s);
   if (d == 64 && p.bm == 128) return launch_dn<64, 4>(p, s);
   if (d == 64 && p.bm == 64) return launch_dn<64, 2>(p, s);
   return hipErrorInvalidValue;

@@ -1,0 +1,379 @@
+// Masked attention forward, bf16 inputs, fp32 accumulation, gfx950 MFMA:
+// 128-row query tiles of four 32-row waves, interval encoding, three
+// workgroups per CU (three waves per SIMD).
+//
+// Same arithmetic and register layout as the 128-row kernel of
+// attn_bf16.hip (S^T = K Q^T per wave with one query row per lane, online
+// softmax in the exp2 domain with a lazy running max, O^T += V^T P^T through
+// the transposing LDS read); the difference is the memory plan, which trades
+// double-buffered V for occupancy.  LDS per workgroup is 52 KB:
+//   K tiles     2 x 16 KB   tile i + 1 streams in while tile i is computed
+//   V tile      1 x 16 KB   V(i) streams in behind QK(i) and the softmax
+//   intervals   2 x  1 KB   raw [4][64] int32, one field per wave
+//   row masks   4 x 256 B   per wave, for PARTIAL tiles
+//   tile list       1 KB
+// so three workgroups (12 waves) share a CU, and the MFMA work of one wave
+// overlaps the VALU work and load waits of the others.  Per tile:
+//   issue V(i), K(i+1), intervals(i+1)   (direct-to-LDS buffer loads)
+//   wave state of tile i (SKIP / FULL / PARTIAL for its 32 rows); QK; mask; softmax
+//   wait V(i); barrier; PV(i)
+//   wait for everything; barrier
+#include <float.h>
+
+#include "device_util.h"
+#include "internal.h"
+
+namespace fmask {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS FMASK_LDS_AS
+#define INLINE __attribute__((always_inline))
+
+constexpr int BN = 64;
+constexpr int NW = 4;
+constexpr int NT = 64 * NW;
+constexpr int BM = 32 * NW;
+constexpr int kList = 256;  // tile-list entries staged in LDS
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kQkAhead = 4;  // K fragments read ahead of their MFMA
+constexpr int kPvAhead = 3;  // V^T fragments read ahead of their MFMA
+
+template <int D>
+struct Geo {
+  static constexpr int KCH = D / 8;
+  static constexpr int TILE = BN * D * 2;
+  static constexpr int K0 = 0;               // K buffers 0, 1
+  static constexpr int V0 = 2 * TILE;        // V buffer
+  static constexpr int IV0 = 3 * TILE;       // raw interval buffers 0, 1: [4][BN] int32
+  static constexpr int IVB = 4 * BN * 4;
+  static constexpr int RM0 = IV0 + 2 * IVB;  // per-wave row masks: [NW][BN] uint32
+  static constexpr int END = RM0 + NW * BN * 4;
+  static constexpr int LOADS = BN * KCH / NT;
+  static_assert(BN * KCH % NT == 0, "tile must split evenly over the workgroup");
+};
+
+template <int KCH>
+__device__ inline int kswz(int key) { return key & (KCH - 1); }
+template <int KCH>
+__device__ inline int vswz(int key) {
+  return KCH == 16 ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
+}
+
+__device__ inline int overlap(int a0, int a1, int b0, int b1) {
+  return max(0, min(a1, b1) - max(a0, b0));
+}
+
+struct Item {
+  int b, h, kvh, mb, mh, qt, row;
+};
+
+__device__ inline Item decode_item(const TileAttnParams& p, int l) {
+  Item it;
+  int r = p.order[l / p.expand];
+  int e = l % p.expand;
+  it.row = r;
+  it.qt = r % p.nqt;
+  it.mh = (r / p.nqt) % p.mh;
+  it.mb = r / (p.nqt * p.mh);
+  if (p.mb == 1 && p.mh == 1) { it.b = e / p.hq; it.h = e % p.hq; }
+  else if (p.mb == 1) { it.b = e; it.h = it.mh; }
+  else if (p.mh == 1) { it.b = it.mb; it.h = e; }
+  else { it.b = it.mb; it.h = it.mh; }
+  it.kvh = it.h / p.group;
+  return it;
+}
+
+// XCD-aware remap: groups of `gsz` consecutive logical items land on one XCD
+// while the longest-first order is kept across XCDs.
+__device__ inline int logical_item(int gsz) {
+  int p = blockIdx.x;
+  int xcd = p % kXcds, k = p / kXcds;
+  return ((k / gsz) * kXcds + xcd) * gsz + (k % gsz);
+}
+
+template <int D>
+__global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  using G = Geo<D>;
+  constexpr int DB = D / 32;
+  constexpr int KT = D / 16;
+  __shared__ __attribute__((aligned(1024))) char smem[G::END];
+  __shared__ int32_t lst[kList];
+
+  const int l = logical_item(gsz);
+  if (l >= p.n_items) return;
+  const Item it = decode_item(p, l);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  const int r0 = it.qt * BM + w * 32;  // first row of this wave
+  const int qrow = r0 + l32;
+
+  const __bf16* Q = (const __bf16*)p.q + it.b * p.qs[0] + it.h * p.qs[1];
+  const __bf16* K = (const __bf16*)p.k + it.b * p.ks[0] + it.kvh * p.ks[1];
+  const __bf16* V = (const __bf16*)p.v + it.b * p.vs[0] + it.kvh * p.vs[1];
+  const int32_t* list = p.list + (int64_t)it.row * p.nkt;
+  const int cnt = p.count[it.row];
+  const int64_t ks2 = p.ks[2], vs2 = p.vs[2];
+  const int32_t* ivcol = p.iv + ((size_t)it.mb * p.mh + it.mh) * 4 * (size_t)p.skv;
+
+  for (int i = tid; i < G::END / 16; i += NT) ((i32x4*)smem)[i] = i32x4{0, 0, 0, 0};
+  for (int i = tid; i < min(cnt, kList); i += NT) lst[i] = list[i];
+  auto entry = [&](int i) INLINE -> int {
+    return i < kList ? __builtin_amdgcn_readfirstlane(lst[i]) : sload_wait(list + i);
+  };
+
+  bf16x8 qf[KT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    if (qrow < p.sq) qf[t] = *(const bf16x8*)(Q + qrow * p.qs[2] + 16 * t + 8 * half);
+    else qf[t] = bf16x8{};
+  }
+  wait_all();  // nothing tracked may stay pending once untracked loads fly
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+  float m_run = -FLT_MAX, l_run = 0.f;
+  const float c = p.scale * kLog2e;
+
+  const rsrc_t krs = make_rsrc(K, ((int64_t)(p.skv - 1) * ks2 + D) * 2);
+  const rsrc_t vrs = make_rsrc(V, ((int64_t)(p.skv - 1) * vs2 + D) * 2);
+  const rsrc_t irs = make_rsrc(ivcol, (int64_t)4 * p.skv * 4);
+  // Direct-to-LDS loads: instruction n of wave w fills LDS chunks
+  // P = (w * LOADS + n) * 64 + lane, i.e. row P / KCH, physical chunk P % KCH
+  // holding logical chunk (P % KCH) ^ swizzle(row).
+  // The V swizzle does not depend on n (rows advance by a multiple of 4 per
+  // instruction), so one lane offset serves all of V's loads; the rest is a
+  // scalar offset.
+  int kgo[G::LOADS];
+#pragma unroll
+  for (int n = 0; n < G::LOADS; ++n) {
+    const int P = (w * G::LOADS + n) * 64 + lane;
+    const int key = P / G::KCH, pc = P % G::KCH;
+    kgo[n] = (int)(key * ks2 * 2 + ((pc ^ kswz<G::KCH>(key)) * 16));
+  }
+  int vgo;
+  {
+    const int P = w * G::LOADS * 64 + lane;
+    const int key = P / G::KCH, pc = P % G::KCH;
+    vgo = (int)(key * vs2 * 2 + ((pc ^ vswz<G::KCH>(key)) * 16));
+  }
+  const int kstep = (int)(BN * ks2 * 2), vstep = (int)(BN * vs2 * 2);
+  const int vrow = (int)((64 / G::KCH) * vs2 * 2);  // bytes of the rows one instruction covers
+  const int lds_w = __builtin_amdgcn_readfirstlane(lds_addr(smem) + w * G::LOADS * 1024);
+  const int lds_iv = __builtin_amdgcn_readfirstlane(lds_addr(smem) + G::IV0 + w * BN * 4);
+
+  const int tg = lane >> 4, tr = (lane >> 2) & 3, tc4 = lane & 3;
+  const int vrow_l = 4 * (tg >> 1) + tr;
+  int vofs[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int ch = 4 * db + 2 * (tg & 1) + (tc4 >> 1);
+    vofs[db] = vrow_l * (D * 2) + ((ch ^ vswz<G::KCH>(vrow_l)) * 16) + (tc4 & 1) * 8;
+  }
+
+  // K tile kt and its raw intervals (wave w loads field w): LOADS + 1 loads.
+  auto issue_k = [&](int kt, int buf) INLINE {
+    const int base = lds_w + G::K0 + buf * G::TILE, g0 = kt * kstep;
+#pragma unroll
+    for (int n = 0; n < G::LOADS; ++n) dma16(krs, kgo[n] + g0, base + n * 1024);
+    dma4(irs, (w * p.skv + kt * BN + lane) * 4, lds_iv + buf * G::IVB);
+  };
+  // V tile kt: LOADS loads.
+  auto issue_v = [&](int kt) INLINE {
+    const int base = lds_w + G::V0, g0 = kt * vstep;
+#pragma unroll
+    for (int n = 0; n < G::LOADS; ++n) dma16s(vrs, vgo, g0 + n * vrow, base + n * 1024);
+  };
+
+  __syncthreads();  // LDS cleared and the list staged before any tile load lands
+  if (cnt > 0) {
+    int e_cur = entry(0);
+    issue_k(e_cur & 0x7fffffff, 0);
+    wait_all();
+    barrier();
+    for (int i = 0; i < cnt; ++i) {
+      const bool more = i + 1 < cnt;
+      const int b = i & 1;
+      const int kt = e_cur & 0x7fffffff;
+      const int e_next = more ? entry(i + 1) : 0;
+      issue_v(kt);
+      if (more) issue_k(e_next & 0x7fffffff, b ^ 1);
+
+      const char* kb = smem + G::K0 + b * G::TILE;
+      const char* vb = smem + G::V0;
+      const int32_t* raw = (const int32_t*)(smem + G::IV0 + b * G::IVB);
+      const bool ragged = (kt + 1) * BN > p.skv;
+      bool need_mask = !(e_cur & (int)FMASK_LIST_FULL_BIT) || ragged;
+      bool skip = false;
+      uint32_t* rmask = (uint32_t*)(smem + G::RM0) + w * BN;
+      if (need_mask) {
+        // This wave's 32-bit row mask of each key column (lane = key; bit r set
+        // iff row r0 + r is masked; keys past skv are masked for every row),
+        // and from it the wave's state for the tile.
+        const int key = kt * BN + lane;
+        int us = raw[lane], ue = raw[BN + lane], ls = raw[2 * BN + lane], le = raw[3 * BN + lane];
+        if (key >= p.skv) { us = 0; ue = 0x7fffffff; ls = 0; le = 0; }
+        auto bits = [&](int a, int e) INLINE -> uint32_t {
+          const int lo = min(max(a - r0, 0), 32), hi = min(max(e - r0, 0), 32);
+          return (uint32_t)(((1ull << hi) - 1ull) & ~((1ull << lo) - 1ull));
+        };
+        const uint32_t mk = bits(us, ue) | bits(ls, le);
+        rmask[lane] = mk;
+        const int n = min(max(p.sq - r0, 0), 32);
+        const uint32_t valid = (uint32_t)((1ull << n) - 1ull);
+        skip = __ballot((mk & valid) == valid) == ~0ull;
+        need_mask = __ballot((mk & valid) != 0u) != 0ull;
+      }
+
+      bf16x8 pf[4];
+      if (!skip) {
+        f32x16 s[2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          s[kh] = f32x16{};
+          const int key = kh * 32 + l32;
+#pragma unroll
+          for (int t = 0; t < KT; ++t) {
+            const int ch = 2 * t + half;
+            bf16x8 a = *(const bf16x8*)(kb + key * (D * 2) + ((ch ^ kswz<G::KCH>(key)) * 16));
+            s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kh], 0, 0, 0);
+          }
+        }
+        // Keep kQkAhead K reads in flight ahead of the MFMAs that consume them
+        // (sched_group_barrier masks: 0x8 MFMA, 0x100 LDS read).
+        __builtin_amdgcn_sched_group_barrier(0x100, kQkAhead, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * KT - kQkAhead; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kQkAhead, 0);
+        if (need_mask) {
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int kl = kh * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+              if ((rmask[kl] >> l32) & 1u) s[kh][r] = -INFINITY;
+            }
+          }
+        }
+        // Online softmax (the other 32 keys of the row sit in lane ^ 32).
+        float mloc = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, fmaxf(s[0][r], s[1][r]));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        const float m_cand = fmaxf(m_run, mloc);
+        const bool grow = (m_cand - m_run) * c > 8.f;
+        if (__any(grow)) {
+          const float m_new = grow ? m_cand : m_run;
+          const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+        }
+        const float mneg = -m_run * c;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+          for (int tp = 0; tp < 2; ++tp) {
+            f32x8 pv;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][8 * tp + j], c, mneg));
+            pf[kh * 2 + tp] = __builtin_convertvector(pv, bf16x8);
+          }
+        }
+        const bf16x2 one2 = bf16x2{(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][2 * j], pf[ks][2 * j + 1]}, one2,
+                                                    l_run, false);
+      }
+      // V(i) landed (K(i+1) and its intervals may still be in flight).
+      if (more) wait_vmcnt<G::LOADS + 1>();
+      else wait_all();
+      barrier();
+      if (!skip) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const char* a0 = vb + vofs[db] + (16 * ks) * (D * 2);
+            bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)a0);
+            bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(a0 + 8 * (D * 2)));
+            bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], acc[db], 0, 0, 0);
+          }
+        }
+        // Same for the V^T fragments (two transposing reads per MFMA).
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvAhead, 0);
+#pragma unroll
+        for (int i = 0; i < 4 * DB - kPvAhead; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kPvAhead, 0);
+      }
+      // K(i+1) and its intervals landed; every wave is done with V(i) and K(i).
+      wait_all();
+      barrier();
+      e_cur = e_next;
+    }
+  }
+
+  // Epilogue: O = O / l, zero rows for l = 0, LSE in natural log.
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < p.sq) {
+    __bf16* O = (__bf16*)p.o + it.b * p.os[0] + it.h * p.os[1] + qrow * p.os[2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = db * 32 + 8 * rg + 4 * half;
+        f32x4 x = f32x4{acc[db][4 * rg], acc[db][4 * rg + 1], acc[db][4 * rg + 2], acc[db][4 * rg + 3]} * inv;
+        *(bf16x4*)(O + d0) = __builtin_convertvector(x, bf16x4);
+      }
+    }
+    if (p.lse && half == 0) {
+      const float lse = l_tot > 0.f ? m_run * p.scale + logf(l_tot) : -INFINITY;
+      p.lse[((int64_t)it.b * p.hq + it.h) * p.sq + qrow] = lse;
+    }
+  }
+#endif
+}
+
+template <int D>
+hipError_t launch_d(const TileAttnParams& p, hipStream_t s) {
+  const int gsz = (p.mh == 1) ? p.group : 1;
+  if (p.n_items <= 0) return hipSuccess;
+  const int64_t unit = (int64_t)kXcds * gsz;
+  const int64_t npad = (p.n_items + unit - 1) / unit * unit;
+  hipLaunchKernelGGL((k_attn_o3<D>), dim3((unsigned)npad), dim3(NT), 0, s, p, gsz);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_o3_bf16(const TileAttnParams& p, int32_t d, hipStream_t s) {
+  if (p.bn != BN || p.bm != BM || p.kind != FMASK_ENC_INTERVALS) return hipErrorInvalidValue;
+  if (d == 128) return launch_d<128>(p, s);
+  if (d == 64) return launch_d<64>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fmask

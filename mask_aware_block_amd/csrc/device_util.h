@@ -38,6 +38,13 @@ __device__ inline void dma16(rsrc_t r, int voff, int lds) {
                : "s"(lds), "v"(voff), "s"(r)
                : "memory", "m0");
 }
+// Same, with a wave-uniform byte offset added through the scalar offset field.
+__device__ inline void dma16s(rsrc_t r, int voff, int soff, int lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(r), "s"(soff)
+               : "memory", "m0");
+}
 __device__ inline void dma4(rsrc_t r, int voff, int lds) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :

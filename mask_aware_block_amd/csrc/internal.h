@@ -101,7 +101,7 @@ struct TileAttnParams {
 
 hipError_t launch_attn_tile_bf16(const TileAttnParams& p, int32_t d, hipStream_t s);
 hipError_t launch_attn_tile_f32(const TileAttnParams& p, int32_t d, hipStream_t s);
-hipError_t launch_attn_pp_bf16(const TileAttnParams& p, int32_t d, hipStream_t s);
+hipError_t launch_attn_o3_bf16(const TileAttnParams& p, int32_t d, hipStream_t s);
 
 struct SelAttnParams {
   const void* q;

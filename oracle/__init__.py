@@ -15,8 +15,8 @@ Modules:
                 exact tile states, compact tile lists and the longest-first order
   attention  -- dense masked softmax attention in float64 (vectorised per row
                 chunk), a per-row sampler, a pure-Python brute force for tiny
-                shapes, and attention over exactly the listed cells for the
-                selected-key family
+                shapes, attention over exactly the listed cells for the
+                selected-key family, and the analytic gradient (dQ, dK, dV)
 
 Every function in this package has a pin in tests/test_oracle_*.py (values the
 pages fix, closed forms, invariants, library reductions, brute force); none is

@@ -160,3 +160,48 @@ def attention_listed_cells(q, k, v, sel, cells, scale, samples, decode=None):
         outs.append((p @ vv) / l)
         lses.append(m + math.log(l))
     return np.array(outs), np.array(lses)
+
+
+def attention_backward_dense(q, k, v, do, vis_fn, scale, row_chunk=512):
+    """Gradients (dQ, dK, dV) of the masked attention above w.r.t. Q, K and V,
+    given the output gradient dO [B,Hq,Sq,Dv] (all float64).
+
+    The analytic gradient of softmax attention, written per (b, h) over the
+    materialised mask (rows with no visible key have P = 0 and contribute
+    nothing, consistent with O_i = 0 there):
+        P_ij   = exp(s_ij - LSE_i) on visible cells, 0 elsewhere
+        dV_g  += P^T dO                       (summed over the heads of group g)
+        dP     = dO V_g^T
+        D_i    = sum_j P_ij dP_ij             (= sum_d dO_id O_id)
+        dS     = P * (dP - D)
+        dQ     = scale dS K_g
+        dK_g  += scale dS^T Q
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, Hq, Sq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for r0 in range(0, Sq, row_chunk):
+                rows = np.arange(r0, min(Sq, r0 + row_chunk))
+                vis = np.asarray(vis_fn(b, h, rows), dtype=bool)
+                s = scale * (q[b, h, rows] @ k[b, g].T)
+                _, lse = _softmax_rows(s, vis, v[b, g])
+                nonempty = np.isfinite(lse)
+                p = np.where(vis & nonempty[:, None], np.exp(s - np.where(nonempty, lse, 0.0)[:, None]), 0.0)
+                dor = do[b, h, rows]
+                dv[b, g] += p.T @ dor
+                dp = dor @ v[b, g].T
+                delta = (p * dp).sum(axis=1)
+                ds = p * (dp - delta[:, None])
+                dq[b, h, rows] = scale * (ds @ k[b, g])
+                dk[b, g] += scale * (ds.T @ q[b, h, rows])
+    return dq, dk, dv

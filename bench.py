@@ -151,6 +151,39 @@ def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5):
     return rec
 
 
+def time_backward(torch, fm, synth, name, steps, warmup):
+    """Backward pass (fmask_attn_bwd) of a workload: attention-gradient launch time
+    and effective TFLOP/s over 10 D flops per visible pair (QK^T, dO V^T, P^T dO,
+    dS K, dS^T Q; the recomputation both gradient kernels do is not counted)."""
+    w = synth.workload(name)
+    q, k, v = (_bf16(torch, a) for a in synth.draw_qkv(w))
+    do = _bf16(torch, synth.draw_dout(w))
+    enc = fm.encode(w["mask"])
+    tiles = fm.classify(enc, 128, 64)
+    o, lse = fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"])
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(q.shape[0] * q.shape[1] * q.shape[2] * 8, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    run = lambda: fm.attn_bwd(q, k, v, o, lse, do, enc, tiles, scale=w["scale"], dq=dq, dk=dk, dv=dv,
+                              workspace=ws)
+    for _ in range(max(warmup, 3)):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / steps
+    nvis = int(visible_pairs(torch, enc).sum().item()) * w["B"] * w["Hq"]
+    flops = 10 * w["D"] * nvis
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    return dict(workload=name + "_backward", B=w["B"], Hq=w["Hq"], Hkv=w["Hkv"], Sq=w["Sq"], Skv=w["Skv"],
+                D=w["D"], dtype="bf16", bwd_ms=t, visible_pairs=nvis, effective_flop=flops,
+                effective_tflops=flops / (t * 1e-3) / 1e12)
+
+
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_causal_doc_32k_hbm_bytes.txt")
 ATTN_SOURCES = [os.path.join(ROOT, "mask_aware_block_amd", "csrc", f)
                 for f in ("attn_bf16_o3.hip", "device_util.h")]
@@ -221,6 +254,9 @@ def main():
                     help="warm up for at least this long (clocks settle); 0 for counter runs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (calibrates HBM byte counters)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the backward pass of the 32K causal-document workload "
+                         "(for profiling runs); prints its own JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
@@ -240,6 +276,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.backward_only:
+        print(json.dumps(time_backward(torch, fm, synth, "causal_doc_32k", args.steps, args.warmup)))
+        return
     head = time_workload(torch, fm, synth, "causal_doc_32k", args.steps, args.warmup, args.min_warmup_s)
     others = []
     if not args.headline_only:
@@ -247,6 +286,8 @@ def main():
                      "block_bitmap_16k", "tree_4k", "selected_key_128k"):
             others.append(time_workload(torch, fm, synth, name, max(3, args.steps // 2), 2,
                                         min(0.2, args.min_warmup_s)))
+        for name in ("causal_doc_8k", "causal_doc_32k"):
+            others.append(time_backward(torch, fm, synth, name, max(3, args.steps // 4), 2))
             torch.cuda.empty_cache()
 
     achieved = head["effective_flop"] / (head["attn_ms"] * 1e-3) / 1e12

@@ -192,6 +192,13 @@ typedef struct fmask_tiles {
   const int32_t *list;             /* [batch][heads][nqt][nkt]                  */
   const int32_t *count;            /* [batch][heads][nqt]                       */
   const int32_t *order;            /* [batch*heads*nqt]                         */
+  /* The same table by key-tile column (used by the backward pass):
+   * col_list[b][h][kt][0..col_count) holds the non-SKIP qt in ascending
+   * order (FMASK_LIST_FULL_BIT set for FULL tiles); col_order lists the
+   * batch*heads*nkt columns by decreasing count, ties by index.                */
+  const int32_t *col_list;         /* [batch][heads][nkt][nqt]                  */
+  const int32_t *col_count;        /* [batch][heads][nkt]                       */
+  const int32_t *col_order;        /* [batch*heads*nkt]                         */
 } fmask_tiles;
 
 /* Attention problem.  Q [b][hq][sq][d], K and V [b][hkv][skv][d], O like Q, in
@@ -242,6 +249,29 @@ fmask_status fmask_classify(const fmask_encoded *enc, int32_t bm, int32_t bn, vo
  * and hq / hkv in {1, 2, 4, 8, 16} on SELECTED.                                 */
 fmask_status fmask_attn_fwd(const fmask_attn_args *args, const void *q, const void *k,
                             const void *v, void *o, float *lse, const fmask_encoded *enc,
+                            const fmask_tiles *tiles, void *stream);
+
+/* Bytes of device workspace fmask_attn_bwd needs (one float per (batch, q
+ * head, query row)); 0 if args is invalid.                                    */
+size_t fmask_attn_bwd_workspace_bytes(const fmask_attn_args *args);
+
+/* Gradient of fmask_attn_fwd (same args, encoding and tile table): given the
+ * forward's output O and log-sum-exp LSE and the output gradient dO, writes
+ * dQ, dK and dV.  With P_ij = exp(s_ij - LSE_i) on visible cells (0 elsewhere,
+ * and for rows with LSE = -inf), D_i = sum_d dO_id O_id and
+ * dS = P * (dO V^T - D):  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO,
+ * dK and dV summed over the query heads that share a K/V head.  This is the
+ * analytic gradient of the forward's definition; training with packed or
+ * structured masks is what the FlashMask rebuttal page builds the forward for.
+ * Layouts: dQ like Q (q_stride), dK like K (k_stride), dV like V (v_stride),
+ * O and dO share o_stride; LSE float [b][hq][sq] contiguous, as the forward
+ * writes it.  workspace: device buffer of fmask_attn_bwd_workspace_bytes
+ * bytes.  Supported: BF16, d in {64, 128}, INTERVALS encoding, the tile table
+ * at 128 x 64 (fmask_preferred_tile); otherwise FMASK_ERR_UNSUPPORTED.         */
+fmask_status fmask_attn_bwd(const fmask_attn_args *args, const void *q, const void *k,
+                            const void *v, const void *o, const float *lse, const void *dout,
+                            void *dq, void *dk, void *dv, void *workspace,
+                            size_t workspace_bytes, const fmask_encoded *enc,
                             const fmask_tiles *tiles, void *stream);
 
 /* Tile shape the attention kernel for (dtype, d, encoding kind) uses. */

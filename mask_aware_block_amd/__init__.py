@@ -67,6 +67,7 @@ class Tiles(ctypes.Structure):
         ("nkt", ctypes.c_int32), ("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
         ("reserved0", ctypes.c_int32), ("reserved1", ctypes.c_int32),
         ("state", _vp), ("list", _vp), ("count", _vp), ("order", _vp),
+        ("col_list", _vp), ("col_count", _vp), ("col_order", _vp),
     ]
 
 
@@ -82,7 +83,8 @@ class AttnArgs(ctypes.Structure):
 
 
 EXPORTS = ("fmask_encode_bytes", "fmask_encode", "fmask_classify_bytes", "fmask_classify",
-           "fmask_attn_fwd", "fmask_preferred_tile", "fmask_status_str", "fmask_last_error")
+           "fmask_attn_fwd", "fmask_attn_bwd_workspace_bytes", "fmask_attn_bwd",
+           "fmask_preferred_tile", "fmask_status_str", "fmask_last_error")
 
 _lib = None
 
@@ -114,6 +116,11 @@ def lib():
         L.fmask_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), _vp, _vp, _vp, _vp, _vp,
                                      ctypes.POINTER(Encoded), ctypes.POINTER(Tiles), _vp]
         L.fmask_attn_fwd.restype = ctypes.c_int32
+        L.fmask_attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs)]
+        L.fmask_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.fmask_attn_bwd.argtypes = [ctypes.POINTER(AttnArgs)] + [_vp] * 10 + [
+            ctypes.c_size_t, ctypes.POINTER(Encoded), ctypes.POINTER(Tiles), _vp]
+        L.fmask_attn_bwd.restype = ctypes.c_int32
         L.fmask_preferred_tile.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                            _c_i32p, _c_i32p]
         L.fmask_preferred_tile.restype = ctypes.c_int32
@@ -300,6 +307,16 @@ class TileTable:
         od = self._view(t.order, 4 * rows, torch.int32, (rows,))
         return st, ls, cn, od
 
+    def columns(self):
+        """(col_list [b][h][nkt][nqt], col_count [b][h][nkt], col_order [b*h*nkt])."""
+        torch = _torch()
+        t = self.struct
+        cols = t.batch * t.heads * t.nkt
+        ls = self._view(t.col_list, 4 * cols * t.nqt, torch.int32, (t.batch, t.heads, t.nkt, t.nqt))
+        cn = self._view(t.col_count, 4 * cols, torch.int32, (t.batch, t.heads, t.nkt))
+        od = self._view(t.col_order, 4 * cols, torch.int32, (cols,))
+        return ls, cn, od
+
 
 def classify(enc, bm=None, bn=None, dtype="bf16", d=128, stream=None):
     """Run the tile classifier (fmask_classify) at bm x bn (default: the kernel's tile)."""
@@ -355,3 +372,32 @@ def attn_fwd(q, k, v, enc, tiles=None, scale=None, out=None, lse=None, want_lse=
                           _stream_handle(stream))
     _check(st)
     return out, lse
+
+
+def attn_bwd(q, k, v, out, lse, dout, enc, tiles, scale=None, dq=None, dk=None, dv=None,
+             workspace=None, stream=None):
+    """Gradient of the masked attention forward (fmask_attn_bwd).
+
+    q, k, v, the forward's out and lse, and the output gradient dout (laid out
+    like out).  Returns (dq, dk, dv) shaped like q, k, v.
+    """
+    torch = _torch()
+    L = lib()
+    if scale is None:
+        scale = 1.0 / float(q.shape[-1]) ** 0.5
+    if dout.stride() != out.stride():
+        raise ValueError("dout must be laid out like out")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
+        raise ValueError("dq, dk, dv must be laid out like q, k, v")
+    a = attn_args(q, k, v, out, scale)
+    nbytes = L.fmask_attn_bwd_workspace_bytes(ctypes.byref(a))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = L.fmask_attn_bwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                          ctypes.byref(enc.struct), ctypes.byref(tiles.struct), _stream_handle(stream))
+    _check(st)
+    return dq, dk, dv

@@ -189,8 +189,9 @@ T* at(void* base, size_t off) {
 }
 
 struct TileLayout {
-  size_t state = 0, list = 0, count = 0, order = 0, total = 0;
-  int64_t nqt = 0, nkt = 0, rows = 0;
+  size_t state = 0, list = 0, count = 0, order = 0, col_list = 0, col_count = 0, col_order = 0,
+         total = 0;
+  int64_t nqt = 0, nkt = 0, rows = 0, cols = 0;
 };
 
 fmask_status check_tiles_args(const fmask_encoded* e, int32_t bm, int32_t bn) {
@@ -216,12 +217,16 @@ TileLayout tile_layout(const fmask_encoded* e, int32_t bm, int32_t bn) {
   T.list = c.take((size_t)T.rows * T.nkt * sizeof(int32_t));
   T.count = c.take((size_t)T.rows * sizeof(int32_t));
   T.order = c.take((size_t)T.rows * sizeof(int32_t));
+  T.cols = (int64_t)e->batch * e->heads * T.nkt;
+  T.col_list = c.take((size_t)T.cols * T.nqt * sizeof(int32_t));
+  T.col_count = c.take((size_t)T.cols * sizeof(int32_t));
+  T.col_order = c.take((size_t)T.cols * sizeof(int32_t));
   T.total = std::max<size_t>(c.off, kAlign);
   return T;
 }
 
-// Tile shapes with a kernel: bf16 intervals 256x64 (two ping-pong wave groups),
-// 128x64 and 64x64; bf16 bitmap 64x64 and 128x64; fp32 64x64.
+// Tile shapes with a kernel: bf16 intervals 256x64, 128x64 and 64x64; bf16
+// bitmap 64x64 and 128x64; fp32 64x64.
 bool tile_supported(int32_t dtype, int32_t kind, int32_t bm, int32_t bn) {
   if (bn != 64) return false;
   if (dtype == FMASK_F32) return bm == 64;
@@ -406,7 +411,7 @@ fmask_status fmask_classify(const fmask_encoded* enc, int32_t bm, int32_t bn, vo
   if (!out || ((uintptr_t)out % kAlign)) return fail(FMASK_ERR_INVALID, "out must be 256-byte aligned");
   const TileLayout T = tile_layout(enc, bm, bn);
   if (out_bytes < T.total) return fail(FMASK_ERR_CAPACITY, "out has %zu bytes, %zu needed", out_bytes, T.total);
-  if (T.rows > INT32_MAX || T.rows * T.nkt > ((int64_t)1 << 40))
+  if (T.rows > INT32_MAX || T.cols > INT32_MAX || T.rows * T.nkt > ((int64_t)1 << 40))
     return fail(FMASK_ERR_UNSUPPORTED, "tile table too large");
   hipStream_t s = (hipStream_t)stream;
   memset(tiles, 0, sizeof(*tiles));
@@ -436,7 +441,17 @@ fmask_status fmask_classify(const fmask_encoded* enc, int32_t bm, int32_t bn, vo
   e = launch_tile_lists(state, (int32_t)T.rows, (int32_t)T.nkt, list, count, s);
   if (e != hipSuccess) return hip_status(e, "tile list kernel");
   e = launch_tile_order(count, (int32_t)T.rows, order, s);
-  return hip_status(e, "tile order kernel");
+  if (e != hipSuccess) return hip_status(e, "tile order kernel");
+  int32_t* col_list = at<int32_t>(out, T.col_list);
+  int32_t* col_count = at<int32_t>(out, T.col_count);
+  int32_t* col_order = at<int32_t>(out, T.col_order);
+  tiles->col_list = col_list;
+  tiles->col_count = col_count;
+  tiles->col_order = col_order;
+  e = launch_tile_cols(state, nmask, (int32_t)T.nqt, (int32_t)T.nkt, col_list, col_count, s);
+  if (e != hipSuccess) return hip_status(e, "tile column kernel");
+  e = launch_tile_order(col_count, (int32_t)T.cols, col_order, s);
+  return hip_status(e, "tile column order kernel");
 }
 
 fmask_status fmask_attn_fwd(const fmask_attn_args* a, const void* q, const void* k, const void* v, void* o,
@@ -528,6 +543,70 @@ fmask_status fmask_attn_fwd(const fmask_attn_args* a, const void* q, const void*
   else if (bm == 128 && enc->kind == FMASK_ENC_INTERVALS) e = launch_attn_o3_bf16(p, a->d, s);
   else e = launch_attn_tile_bf16(p, a->d, s);
   return hip_status(e, "attention kernel");
+}
+
+size_t fmask_attn_bwd_workspace_bytes(const fmask_attn_args* a) {
+  if (!a || a->b < 1 || a->hq < 1 || a->sq < 0 || a->sq > kMaxSeq) return 0;
+  return std::max<size_t>((size_t)a->b * a->hq * a->sq * 2 * sizeof(float), kAlign);
+}
+
+fmask_status fmask_attn_bwd(const fmask_attn_args* a, const void* q, const void* k, const void* v,
+                            const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                            void* dv, void* workspace, size_t workspace_bytes, const fmask_encoded* enc,
+                            const fmask_tiles* tiles, void* stream) {
+  g_err[0] = 0;
+  if (!a || !enc || !tiles) return fail(FMASK_ERR_INVALID, "null args, encoding or tile table");
+  if (a->dtype != FMASK_BF16) return fail(FMASK_ERR_UNSUPPORTED, "backward: bf16 only");
+  if (a->d != 64 && a->d != 128) return fail(FMASK_ERR_UNSUPPORTED, "backward: d in {64, 128}");
+  if (enc->kind != FMASK_ENC_INTERVALS) return fail(FMASK_ERR_UNSUPPORTED, "backward: INTERVALS encoding only");
+  if (a->b < 1 || a->hq < 1 || a->hkv < 1 || a->hq % a->hkv)
+    return fail(FMASK_ERR_INVALID, "need b, hq, hkv >= 1 and hq %% hkv == 0");
+  if (a->sq < 0 || a->skv < 0 || a->sq > kMaxSeq || a->skv > kMaxSeq)
+    return fail(FMASK_ERR_INVALID, "sq / skv out of range");
+  if (a->sq != enc->sq || a->skv != enc->skv) return fail(FMASK_ERR_INVALID, "sq / skv differ from the encoding");
+  if (!(enc->batch == 1 || enc->batch == a->b)) return fail(FMASK_ERR_INVALID, "encoding batch must be 1 or b");
+  if (!(enc->heads == 1 || enc->heads == a->hq)) return fail(FMASK_ERR_INVALID, "encoding heads must be 1 or hq");
+  if (tiles->bm != 128 || tiles->bn != 64)
+    return fail(FMASK_ERR_UNSUPPORTED, "backward: tile table at 128 x 64 (have %d x %d)", tiles->bm, tiles->bn);
+  if (tiles->nqt != ceil_div(a->sq, 128) || tiles->nkt != ceil_div(a->skv, 64) ||
+      tiles->batch != enc->batch || tiles->heads != enc->heads || !tiles->col_list)
+    return fail(FMASK_ERR_INVALID, "tile table does not match the encoding");
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return fail(FMASK_ERR_INVALID, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(FMASK_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
+  for (int i = 0; i < 3; ++i) {
+    if (a->q_stride[i] % 8 || a->k_stride[i] % 8 || a->v_stride[i] % 8 || a->o_stride[i] % 8)
+      return fail(FMASK_ERR_UNSUPPORTED, "strides must be multiples of 8 elements");
+    if (a->q_stride[i] < 0 || a->k_stride[i] < 0 || a->v_stride[i] < 0 || a->o_stride[i] < 0)
+      return fail(FMASK_ERR_INVALID, "negative stride");
+  }
+  const size_t need = fmask_attn_bwd_workspace_bytes(a);
+  if (!workspace || ((uintptr_t)workspace % 16)) return fail(FMASK_ERR_INVALID, "workspace must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(FMASK_ERR_CAPACITY, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  const int64_t lim = ((int64_t)1 << 31) - 1;  // 32-bit buffer offsets inside one head
+  if ((a->skv + 64) * a->k_stride[2] * 2 > lim || (a->skv + 64) * a->v_stride[2] * 2 > lim ||
+      (a->sq + 128) * a->q_stride[2] * 2 > lim || (a->sq + 128) * a->o_stride[2] * 2 > lim)
+    return fail(FMASK_ERR_UNSUPPORTED, "one head must span less than 2 GiB");
+  if ((int64_t)a->b * a->hq * a->sq > INT32_MAX / 4) return fail(FMASK_ERR_UNSUPPORTED, "problem too large");
+  BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
+  p.dq = dq; p.dk = dk; p.dv = dv; p.ws = (float*)workspace;
+  memcpy(p.qs, a->q_stride, sizeof(p.qs));
+  memcpy(p.ks, a->k_stride, sizeof(p.ks));
+  memcpy(p.vs, a->v_stride, sizeof(p.vs));
+  memcpy(p.os, a->o_stride, sizeof(p.os));
+  p.b = a->b; p.hq = a->hq; p.hkv = a->hkv; p.group = a->hq / a->hkv;
+  p.sq = (int32_t)a->sq; p.skv = (int32_t)a->skv; p.scale = a->scale;
+  p.list = tiles->list; p.count = tiles->count; p.order = tiles->order;
+  p.col_list = tiles->col_list; p.col_count = tiles->col_count; p.col_order = tiles->col_order;
+  p.nqt = tiles->nqt; p.nkt = tiles->nkt; p.bm = tiles->bm; p.bn = tiles->bn;
+  p.mb = enc->batch; p.mh = enc->heads;
+  p.iv = enc->intervals;
+  hipStream_t s = (hipStream_t)stream;
+  return hip_status(launch_attn_bwd_bf16(p, a->d, s), "attention backward kernels");
 }
 
 }  // extern "C"

@@ -1,0 +1,637 @@
+// Backward pass of the masked attention forward, bf16 inputs, fp32
+// accumulation, gfx950 MFMA (interval encoding, 128 x 64 tile table).
+//
+// With P_ij = exp(s_ij - LSE_i) on visible cells, D_i = sum_d dO_id O_id and
+// dS = P * (dO V^T - D):  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
+// Three launches, no atomics:
+//   k_bwd_rows   D_i and LSE_i log2(e) per row (+inf for rows with no visible
+//                key, so that their P is exactly 0).
+//   k_bwd_dq     one 128-row query tile per workgroup (four 32-row waves)
+//                walking the tile row's compact list of 64-key tiles, as in
+//                the forward: S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, then
+//                dQ^T += K^T dS^T.
+//   k_bwd_dkdv   one 64-key tile per workgroup walking its column list of
+//                128-row query tiles, for every query head of the K/V head:
+//                S = Q K^T and dP = dO V^T with K, V in registers, then
+//                dV^T += dO^T P and dK^T += Q^T dS.  Waves split the keys (2 x
+//                32) and the rows of each query tile (2 x 64); the two row
+//                halves are summed through LDS at the end.  Query tiles are
+//                double-buffered in LDS.
+// Tiles whose rows and keys a wave does not see at all are skipped per wave;
+// FULL tiles run without element masks.  Operand fragments that are read
+// both row-wise (16-byte reads) and transposed (ds_read_b64_tr_b16) live in
+// LDS under a swizzle that keeps both access patterns free of bank conflicts.
+#include <float.h>
+
+#include "device_util.h"
+#include "internal.h"
+
+namespace fmask {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS FMASK_LDS_AS
+#define INLINE __attribute__((always_inline))
+
+constexpr int BN = 64;    // keys per tile
+constexpr int BM = 128;   // query rows per tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 16-byte chunk swizzle serving both access patterns: 16 consecutive rows
+// read at one logical chunk hit 16 distinct (bank) positions, and the four
+// rows of a transposing read group hit distinct chunk pairs.
+template <int KCH>
+__device__ inline int sw(int row) {
+  if (KCH == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);  // KCH == 8
+}
+
+// Byte offset (inside a [rows][D] bf16 tile) of logical chunk ch of row r.
+template <int D>
+__device__ inline int chunk_off(int r, int ch) {
+  return r * (D * 2) + ((ch ^ sw<D / 8>(r)) * 16);
+}
+
+// Transposing-read offsets: lane (g = lane / 16, rr = (lane % 16) / 4,
+// c4 = lane % 4) addresses row 4 (g / 2) + rr and the 8 bytes at
+// d = 32 db + 16 (g % 2) + 4 c4 of a group of 16 rows; the read hands lane l
+// four rows at d = 32 db + (l % 32), which become the MFMA operand slots
+// 8 (j / 4) + 4 (l / 32) + j % 4 of a 16-row step (the slot order the score
+// accumulators produce).
+// (hi selects rows 8 .. 15 of the group.)
+template <int D>
+__device__ inline int tr_off(int lane, int db, int hi) {
+  const int tg = lane >> 4, rr = (lane >> 2) & 3, tc4 = lane & 3;
+  const int row = 8 * hi + 4 * (tg >> 1) + rr;
+  const int ch = 4 * db + 2 * (tg & 1) + (tc4 >> 1);
+  return chunk_off<D>(row, ch) + (tc4 & 1) * 8;
+}
+
+// A 32 x 16 operand fragment (32 values of d, k = 16 rows of the tile) read
+// transposed from a swizzled [rows][D] tile, rows r0 .. r0 + 15 (r0 % 16 == 0;
+// the swizzle depends on row % 16 only, so the offsets of rows 0 .. 15 serve).
+template <int D>
+__device__ inline bf16x8 tr_frag(const char* tile, int r0, int off_lo, int off_hi) {
+  const char* t = tile + r0 * (D * 2);
+  bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(t + off_lo));
+  bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(t + off_hi));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ inline int overlap(int a0, int a1, int b0, int b1) {
+  return max(0, min(a1, b1) - max(a0, b0));
+}
+
+__device__ inline int logical_item(int gsz) {
+  int p = blockIdx.x;
+  int xcd = p % kXcds, k = p / kXcds;
+  return ((k / gsz) * kXcds + xcd) * gsz + (k % gsz);
+}
+
+// ------------------------------------------------------------------ rows
+// One 16-lane (D = 128) or 8-lane (D = 64) group per row.
+template <int D>
+__global__ void __launch_bounds__(256) k_bwd_rows(BwdParams p, int64_t rows) {
+  constexpr int LPR = D / 8;          // lanes per row, 8 values each
+  constexpr int RPB = 256 / LPR;      // rows per block
+  const int64_t g = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int sub = threadIdx.x % LPR;
+  float acc = 0.f;
+  int64_t b = 0, h = 0, i = 0;
+  const bool ok = g < rows;
+  if (ok) {
+    i = g % p.sq;
+    h = (g / p.sq) % p.hq;
+    b = g / ((int64_t)p.sq * p.hq);
+    const __bf16* O = (const __bf16*)p.o + b * p.os[0] + h * p.os[1] + i * p.os[2];
+    const __bf16* dO = (const __bf16*)p.dout + b * p.os[0] + h * p.os[1] + i * p.os[2];
+    const bf16x8 x = *(const bf16x8*)(O + 8 * sub), y = *(const bf16x8*)(dO + 8 * sub);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += (float)x[j] * (float)y[j];
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (ok && sub == 0) {
+    const float lse = p.lse[(b * p.hq + h) * p.sq + i];
+    p.ws[2 * g] = acc;
+    p.ws[2 * g + 1] = lse == -INFINITY ? INFINITY : lse * kLog2e;
+  }
+}
+
+// ------------------------------------------------------------------ dQ
+template <int D>
+struct GeoQ {
+  static constexpr int KCH = D / 8;
+  static constexpr int TILE = BN * D * 2;
+  static constexpr int STAGE = 2 * TILE + 4 * BN * 4;  // K, V, raw intervals [4][BN]
+  static constexpr int RM0 = 2 * STAGE;                // per-wave row masks [4][BN]
+  static constexpr int END = RM0 + 4 * BN * 4;
+  static constexpr int LOADS = BN * KCH / 256;
+};
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdParams p, int expand, int n_items, int gsz) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  using G = GeoQ<D>;
+  constexpr int DB = D / 32, KT = D / 16;
+  __shared__ __attribute__((aligned(1024))) char smem[G::END];
+
+  const int l = logical_item(gsz);
+  if (l >= n_items) return;
+  // item -> (mask row, batch, head), as the forward orders them
+  const int row = p.order[l / expand], e = l % expand;
+  const int qt = row % p.nqt, mh = (row / p.nqt) % p.mh, mb = row / (p.nqt * p.mh);
+  int b, h;
+  if (p.mb == 1 && p.mh == 1) { b = e / p.hq; h = e % p.hq; }
+  else if (p.mb == 1) { b = e; h = mh; }
+  else if (p.mh == 1) { b = mb; h = e; }
+  else { b = mb; h = mh; }
+  const int kvh = h / p.group;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  const int r0 = qt * BM + w * 32;
+  const int qrow = r0 + l32;
+  const int32_t* list = p.list + (int64_t)row * p.nkt;
+  const int cnt = p.count[row];
+  const int64_t ks2 = p.ks[2], vs2 = p.vs[2];
+  const int32_t* ivcol = p.iv + ((size_t)mb * p.mh + mh) * 4 * (size_t)p.skv;
+  const __bf16* Q = (const __bf16*)p.q + b * p.qs[0] + h * p.qs[1];
+  const __bf16* dO = (const __bf16*)p.dout + b * p.os[0] + h * p.os[1];
+  const __bf16* K = (const __bf16*)p.k + b * p.ks[0] + kvh * p.ks[1];
+  const __bf16* V = (const __bf16*)p.v + b * p.vs[0] + kvh * p.vs[1];
+
+  for (int i = tid; i < G::END / 16; i += 256) ((i32x4*)smem)[i] = i32x4{0, 0, 0, 0};
+
+  // Q^T and dO^T as MFMA B operands (lane: row qrow, d = 16 t + 8 half + 0..7)
+  bf16x8 qf[KT], df[KT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    if (qrow < p.sq) {
+      qf[t] = *(const bf16x8*)(Q + qrow * p.qs[2] + 16 * t + 8 * half);
+      df[t] = *(const bf16x8*)(dO + qrow * p.os[2] + 16 * t + 8 * half);
+    } else {
+      qf[t] = bf16x8{};
+      df[t] = bf16x8{};
+    }
+  }
+  float dlt = 0.f, lse2 = INFINITY;
+  if (qrow < p.sq) {
+    const int64_t g = ((int64_t)b * p.hq + h) * p.sq + qrow;
+    dlt = p.ws[2 * g];
+    lse2 = p.ws[2 * g + 1];
+  }
+  wait_all();  // nothing tracked may stay pending once untracked loads fly
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+  const float c = p.scale * kLog2e;
+
+  const rsrc_t krs = make_rsrc(K, ((int64_t)(p.skv - 1) * ks2 + D) * 2);
+  const rsrc_t vrs = make_rsrc(V, ((int64_t)(p.skv - 1) * vs2 + D) * 2);
+  const rsrc_t irs = make_rsrc(ivcol, (int64_t)4 * p.skv * 4);
+  int kgo[G::LOADS], vgo[G::LOADS];
+#pragma unroll
+  for (int n = 0; n < G::LOADS; ++n) {
+    const int P = (w * G::LOADS + n) * 64 + lane;
+    const int key = P / G::KCH, pc = P % G::KCH;
+    kgo[n] = (int)(key * ks2 * 2 + ((pc ^ sw<G::KCH>(key)) * 16));
+    vgo[n] = (int)(key * vs2 * 2 + ((pc ^ sw<G::KCH>(key)) * 16));
+  }
+  const int kstep = (int)(BN * ks2 * 2), vstep = (int)(BN * vs2 * 2);
+  const int lds_w = __builtin_amdgcn_readfirstlane(lds_addr(smem) + w * G::LOADS * 1024);
+  const int lds_iv = __builtin_amdgcn_readfirstlane(lds_addr(smem) + 2 * G::TILE + w * BN * 4);
+  int tlo[DB], thi[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    tlo[db] = tr_off<D>(lane, db, 0);
+    thi[db] = tr_off<D>(lane, db, 1);
+  }
+
+  auto issue = [&](int kt, int buf) INLINE {
+    const int base = lds_w + buf * G::STAGE;
+#pragma unroll
+    for (int n = 0; n < G::LOADS; ++n) dma16(krs, kgo[n] + kt * kstep, base + n * 1024);
+#pragma unroll
+    for (int n = 0; n < G::LOADS; ++n) dma16(vrs, vgo[n] + kt * vstep, base + G::TILE + n * 1024);
+    dma4(irs, (w * p.skv + kt * BN + lane) * 4, lds_iv + buf * G::STAGE);
+  };
+
+  uint32_t* rmask = (uint32_t*)(smem + G::RM0) + w * BN;
+  __syncthreads();
+  if (cnt > 0) {
+    int e_cur = list[0];
+    issue(e_cur & 0x7fffffff, 0);
+    wait_all();
+    barrier();
+    for (int i = 0; i < cnt; ++i) {
+      const bool more = i + 1 < cnt;
+      const int e_next = more ? list[i + 1] : 0;
+      if (more) issue(e_next & 0x7fffffff, (i + 1) & 1);
+      const int kt = e_cur & 0x7fffffff;
+      const char* kb = smem + (i & 1) * G::STAGE;
+      const char* vb = kb + G::TILE;
+      const int32_t* raw = (const int32_t*)(kb + 2 * G::TILE);
+      const bool ragged = (kt + 1) * BN > p.skv;
+      bool need_mask = !(e_cur & (int)FMASK_LIST_FULL_BIT) || ragged;
+      bool skip = false;
+      if (need_mask) {
+        const int key = kt * BN + lane;
+        int us = raw[lane], ue = raw[BN + lane], ls = raw[2 * BN + lane], le = raw[3 * BN + lane];
+        if (key >= p.skv) { us = 0; ue = 0x7fffffff; ls = 0; le = 0; }
+        auto bits = [&](int a, int z) INLINE -> uint32_t {
+          const int lo = min(max(a - r0, 0), 32), hi = min(max(z - r0, 0), 32);
+          return (uint32_t)(((1ull << hi) - 1ull) & ~((1ull << lo) - 1ull));
+        };
+        const uint32_t mk = bits(us, ue) | bits(ls, le);
+        rmask[lane] = mk;
+        const int n = min(max(p.sq - r0, 0), 32);
+        const uint32_t valid = (uint32_t)((1ull << n) - 1ull);
+        skip = __ballot((mk & valid) == valid) == ~0ull;
+        need_mask = __ballot((mk & valid) != 0u) != 0ull;
+      }
+      if (!skip) {
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          s[kh] = f32x16{};
+          dp[kh] = f32x16{};
+          const int key = kh * 32 + l32;
+#pragma unroll
+          for (int t = 0; t < KT; ++t) {
+            const bf16x8 a = *(const bf16x8*)(kb + chunk_off<D>(key, 2 * t + half));
+            s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kh], 0, 0, 0);
+          }
+#pragma unroll
+          for (int t = 0; t < KT; ++t) {
+            const bf16x8 a = *(const bf16x8*)(vb + chunk_off<D>(key, 2 * t + half));
+            dp[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, df[t], dp[kh], 0, 0, 0);
+          }
+        }
+        // P^T and dS^T (key slots in the order the PV-style operand expects)
+        bf16x8 dsf[4];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+          for (int tp = 0; tp < 2; ++tp) {
+            f32x8 x;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int r = 8 * tp + j;
+              float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][r], c, -lse2));
+              if (need_mask) {
+                const int kl = kh * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                if ((rmask[kl] >> l32) & 1u) pr = 0.f;
+              }
+              x[j] = pr * (dp[kh][r] - dlt);
+            }
+            dsf[kh * 2 + tp] = __builtin_convertvector(x, bf16x8);
+          }
+        }
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 a = tr_frag<D>(kb, 16 * ks, tlo[db], thi[db]);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[ks], acc[db], 0, 0, 0);
+          }
+        }
+      }
+      wait_all();  // tile i+1 landed; every wave is done with tile i
+      barrier();
+      e_cur = e_next;
+    }
+  }
+
+  if (qrow < p.sq) {
+    __bf16* dQ = (__bf16*)p.dq + b * p.qs[0] + h * p.qs[1] + qrow * p.qs[2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = db * 32 + 8 * rg + 4 * half;
+        f32x4 x = f32x4{acc[db][4 * rg], acc[db][4 * rg + 1], acc[db][4 * rg + 2], acc[db][4 * rg + 3]} *
+                  p.scale;
+        *(bf16x4*)(dQ + d0) = __builtin_convertvector(x, bf16x4);
+      }
+    }
+  }
+#endif
+}
+
+// ------------------------------------------------------------------ dK, dV
+template <int D>
+struct GeoKV {
+  static constexpr int KCH = D / 8;
+  static constexpr int TILE = BM * D * 2;        // one [128 rows][D] bf16 tile
+  static constexpr int Q0 = 0, DO0 = TILE;       // Q tile, dO tile
+  static constexpr int RW0 = 2 * TILE;           // [128 rows] x {D_i, LSE2_i}
+  static constexpr int STAGE = RW0 + BM * 8;     // two stages (double-buffered)
+  static constexpr int END = 2 * STAGE;
+  static constexpr int LOADS = BM * KCH / 256;
+};
+
+template <int D>
+__global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, int n_items) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  using G = GeoKV<D>;
+  constexpr int DB = D / 32, KT = D / 16;
+  __shared__ __attribute__((aligned(1024))) char smem[G::END];
+
+  const int l = blockIdx.x;
+  if (l >= n_items) return;
+  // item -> (mask column, batch, K/V head)
+  int col, b, g;
+  if (p.mh == 1) {
+    col = p.col_order[l / expand];
+    const int e = l % expand;  // (batch if the mask is shared along it) x K/V head
+    const int mbm = col / p.nkt;
+    if (p.mb == 1) { b = e / p.hkv; g = e % p.hkv; }
+    else { b = mbm; g = e; }
+  } else {
+    // per-head masks: items are (batch, K/V head, key tile) in natural order
+    const int kt0 = l % p.nkt;
+    g = (l / p.nkt) % p.hkv;
+    b = l / (p.nkt * p.hkv);
+    col = ((p.mb == 1 ? 0 : b) * p.mh) * p.nkt + kt0;  // column of the first head (fixed below)
+  }
+  const int kt = col % p.nkt;
+  const int mb = (p.mb == 1) ? 0 : b;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = w & 1, rw = w >> 1;  // key half (32 keys), 64-row half of each query tile
+  const int half = lane >> 5, l32 = lane & 31;
+  const int key = kt * BN + kw * 32 + l32;  // this lane's key (as MFMA column)
+
+  const __bf16* K = (const __bf16*)p.k + b * p.ks[0] + g * p.ks[1];
+  const __bf16* V = (const __bf16*)p.v + b * p.vs[0] + g * p.vs[1];
+
+  for (int i = tid; i < G::END / 16; i += 256) ((i32x4*)smem)[i] = i32x4{0, 0, 0, 0};
+
+  // K and V as B operands of S = Q K^T and dP = dO V^T (lane: key, 8 d)
+  bf16x8 kf[KT], vf[KT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    if (key < p.skv) {
+      kf[t] = *(const bf16x8*)(K + key * p.ks[2] + 16 * t + 8 * half);
+      vf[t] = *(const bf16x8*)(V + key * p.vs[2] + 16 * t + 8 * half);
+    } else {
+      kf[t] = bf16x8{};
+      vf[t] = bf16x8{};
+    }
+  }
+  wait_all();
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dk[i] = dv[i] = f32x16{};
+  const float c = p.scale * kLog2e;
+  int tlo[DB], thi[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    tlo[db] = tr_off<D>(lane, db, 0);
+    thi[db] = tr_off<D>(lane, db, 1);
+  }
+  const int lds_w = __builtin_amdgcn_readfirstlane(lds_addr(smem) + w * G::LOADS * 1024);
+  const int lds_rw = __builtin_amdgcn_readfirstlane(lds_addr(smem) + G::RW0);
+  // Tile loads: instruction n of wave w fills chunks P = (w LOADS + n) 64 + lane,
+  // row r = P / KCH (RPI rows per instruction).  The swizzle repeats every PER
+  // instructions, so the lane part is one of PER (row, chunk) pairs and the
+  // rest is a scalar row offset.
+  constexpr int RPI = 64 / G::KCH;
+  constexpr int PER = 16 / RPI;
+
+  // The (query head, query tile) pairs of this key tile, flattened; pair
+  // n + 1 is staged into the other buffer while pair n is computed.
+  auto col_of = [&](int hi) INLINE -> int {
+    return (mb * p.mh + (p.mh == 1 ? 0 : g * p.group + hi)) * p.nkt + kt;
+  };
+  auto count_of = [&](int hi) INLINE -> int { return p.col_count[col_of(hi)]; };
+  auto stage = [&](int hi, int i, int buf) INLINE {
+    const int h = g * p.group + hi;
+    const int qt = p.col_list[(int64_t)col_of(hi) * p.nqt + i] & 0x7fffffff;
+    const __bf16* Q = (const __bf16*)p.q + b * p.qs[0] + h * p.qs[1];
+    const __bf16* dO = (const __bf16*)p.dout + b * p.os[0] + h * p.os[1];
+    const float* ws = p.ws + ((int64_t)b * p.hq + h) * p.sq * 2;
+    const rsrc_t qrs = make_rsrc(Q, ((int64_t)(p.sq - 1) * p.qs[2] + D) * 2);
+    const rsrc_t ors = make_rsrc(dO, ((int64_t)(p.sq - 1) * p.os[2] + D) * 2);
+    const rsrc_t wrs = make_rsrc(ws, (int64_t)p.sq * 8);
+    const int base = lds_w + buf * G::STAGE;
+#pragma unroll
+    for (int n = 0; n < G::LOADS; ++n) {
+      // scalar part: rows of whole swizzle periods (a multiple of 16) + tile base;
+      // lane part: row tr (< 16) and its swizzled chunk
+      const int rs = qt * BM + (w * G::LOADS + n - n % PER) * RPI;
+      const int tr = (n % PER) * RPI + lane / G::KCH;
+      const int tc = ((lane % G::KCH) ^ sw<G::KCH>(tr)) * 16;
+      dma16s(qrs, (int)(tr * p.qs[2] * 2) + tc, (int)(rs * p.qs[2] * 2), base + G::Q0 + n * 1024);
+      dma16s(ors, (int)(tr * p.os[2] * 2) + tc, (int)(rs * p.os[2] * 2), base + G::DO0 + n * 1024);
+    }
+    // 128 rows x 8 bytes = 1 KB of row values, one 16-byte load per lane of wave 0
+    if (w == 0) dma16(wrs, (qt * BM * 2 + lane * 4) * 4, lds_rw + buf * G::STAGE);
+  };
+
+  int hi = 0;
+  while (hi < p.group && count_of(hi) == 0) ++hi;
+  int us = 0, ue = 0x7fffffff, ls = 0, le = 0;  // this lane's key column (past skv: all masked)
+  int iv_head = -1;
+  if (hi < p.group) {
+    int i = 0, buf = 0;
+    stage(hi, i, 0);
+    wait_all();
+    barrier();
+    while (true) {
+      int nh = hi, ni = i + 1;
+      while (nh < p.group && ni >= count_of(nh)) { ++nh; ni = 0; }
+      const bool more = nh < p.group;
+      // intervals of this lane's key for the current head's mask (loaded
+      // before the next stage's loads are in flight)
+      const int mhh = p.mh == 1 ? 0 : g * p.group + hi;
+      if (mhh != iv_head) {
+        iv_head = mhh;
+        if (key < p.skv) {
+          const int32_t* ivcol = p.iv + ((size_t)mb * p.mh + mhh) * 4 * (size_t)p.skv;
+          us = ivcol[key];
+          ue = ivcol[p.skv + key];
+          ls = ivcol[2 * (size_t)p.skv + key];
+          le = ivcol[3 * (size_t)p.skv + key];
+        }
+        wait_all();
+      }
+      const int e = p.col_list[(int64_t)col_of(hi) * p.nqt + i];
+      if (more) stage(nh, ni, buf ^ 1);
+      const int qt = e & 0x7fffffff;
+
+      const char* qb = smem + buf * G::STAGE + G::Q0;
+      const char* ob = smem + buf * G::STAGE + G::DO0;
+      const float* rv = (const float*)(smem + buf * G::STAGE + G::RW0);
+      // this wave: keys key (lane), rows qt*BM + rw*64 + [0, 64)
+      const int ra = qt * BM + rw * 64;
+      const int na = min(max(p.sq - ra, 0), 64);
+      const int cm = overlap(ra, ra + na, us, ue) + overlap(ra, ra + na, ls, le);
+      const bool wskip = __ballot(!(key < p.skv) || cm == na) == ~0ull;
+      const bool full = (e & (int)FMASK_LIST_FULL_BIT) && (kt + 1) * BN <= p.skv && na == 64;
+      if (!wskip) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int lr0 = rw * 64 + rb * 32;  // first tile row of this block
+          f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+          for (int t = 0; t < KT; ++t) {
+            const bf16x8 aq = *(const bf16x8*)(qb + chunk_off<D>(lr0 + l32, 2 * t + half));
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[t], s, 0, 0, 0);
+          }
+#pragma unroll
+          for (int t = 0; t < KT; ++t) {
+            const bf16x8 ao = *(const bf16x8*)(ob + chunk_off<D>(lr0 + l32, 2 * t + half));
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[t], dp, 0, 0, 0);
+          }
+          // P, dS: lane = key, rows lr0 + 8 (r / 4) + 4 half + r % 4
+          bf16x8 pb[2], sb[2];
+#pragma unroll
+          for (int tp = 0; tp < 2; ++tp) {
+            f32x8 xp, xs;
+#pragma unroll
+            for (int j4 = 0; j4 < 2; ++j4) {
+              const int rl = lr0 + 8 * (2 * tp + j4) + 4 * half;  // 4 consecutive rows
+              const f32x4 d4 = *(const f32x4*)(rv + 2 * rl);       // {D, LSE2} x 2
+              const f32x4 d5 = *(const f32x4*)(rv + 2 * rl + 4);
+              const float dl[4] = {d4[0], d4[2], d5[0], d5[2]};
+              const float ll[4] = {d4[1], d4[3], d5[1], d5[3]};
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4) {
+                const int r = 8 * tp + 4 * j4 + q4;
+                float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -ll[q4]));
+                if (!full) {
+                  const int grow = qt * BM + rl + q4;
+                  const bool masked = ((uint32_t)(grow - us) < (uint32_t)(ue - us)) ||
+                                      ((uint32_t)(grow - ls) < (uint32_t)(le - ls)) || grow >= p.sq;
+                  if (masked) pr = 0.f;
+                }
+                xp[4 * j4 + q4] = pr;
+                xs[4 * j4 + q4] = pr * (dp[r] - dl[q4]);
+              }
+            }
+            pb[tp] = __builtin_convertvector(xp, bf16x8);
+            sb[tp] = __builtin_convertvector(xs, bf16x8);
+          }
+          // dV^T += dO^T P,  dK^T += Q^T dS  (contraction over the 32 rows)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+              const bf16x8 ao = tr_frag<D>(ob, lr0 + 16 * ks, tlo[db], thi[db]);
+              dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb[ks], dv[db], 0, 0, 0);
+              const bf16x8 aq = tr_frag<D>(qb, lr0 + 16 * ks, tlo[db], thi[db]);
+              dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb[ks], dk[db], 0, 0, 0);
+            }
+          }
+        }
+      }
+      wait_all();  // the next pair landed; every wave is done with this one
+      barrier();
+      if (!more) break;
+      hi = nh;
+      i = ni;
+      buf ^= 1;
+    }
+  }
+
+  // Sum the two row halves (waves kw and kw + 2) through LDS, then write.
+  float* red = (float*)smem;  // [2 kw][2 tensors][DB][16][64] floats
+  auto slot = [&](int t, int db, int r) INLINE -> float& {
+    return red[(((kw * 2 + t) * DB + db) * 16 + r) * 64 + lane];
+  };
+  __syncthreads();
+  if (rw == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        slot(0, db, r) = dk[db][r];
+        slot(1, db, r) = dv[db][r];
+      }
+  }
+  __syncthreads();
+  if (rw == 0 && key < p.skv) {
+    __bf16* dK = (__bf16*)p.dk + b * p.ks[0] + g * p.ks[1] + key * p.ks[2];
+    __bf16* dV = (__bf16*)p.dv + b * p.vs[0] + g * p.vs[1] + key * p.vs[2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        f32x4 xk, xv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * rg + j;
+          xk[j] = (dk[db][r] + slot(0, db, r)) * p.scale;
+          xv[j] = dv[db][r] + slot(1, db, r);
+        }
+        const int d0 = db * 32 + 8 * rg + 4 * half;
+        *(bf16x4*)(dK + d0) = __builtin_convertvector(xk, bf16x4);
+        *(bf16x4*)(dV + d0) = __builtin_convertvector(xv, bf16x4);
+      }
+    }
+  }
+#endif
+}
+
+template <int D>
+hipError_t launch_d(const BwdParams& p, hipStream_t s) {
+  // (With no query row the dK / dV kernel still runs: its empty column lists
+  // write zeros.  With no key the dQ kernel's empty lists do the same.)
+  const int64_t rows = (int64_t)p.b * p.hq * p.sq;
+  constexpr int RPB = 256 / (D / 8);
+  if (rows > 0)
+    hipLaunchKernelGGL((k_bwd_rows<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // dQ: items like the forward (tile rows x (batch, head) expansion)
+  {
+    const int expand = (p.mb == 1 ? p.b : 1) * (p.mh == 1 ? p.hq : 1);
+    const int64_t n = (int64_t)p.mb * p.mh * p.nqt * expand;
+    const int gsz = (p.mh == 1) ? p.group : 1;
+    const int64_t unit = (int64_t)kXcds * gsz;
+    const int64_t npad = (n + unit - 1) / unit * unit;
+    if (n > 0)
+      hipLaunchKernelGGL((k_bwd_dq<D>), dim3((unsigned)npad), dim3(256), 0, s, p, expand, (int)n, gsz);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // dK, dV: one item per (key tile column, batch, K/V head)
+  {
+    int expand;
+    int64_t n;
+    if (p.mh == 1) {
+      expand = (p.mb == 1 ? p.b : 1) * p.hkv;
+      n = (int64_t)p.mb * p.nkt * expand;
+    } else {
+      expand = 1;
+      n = (int64_t)p.b * p.hkv * p.nkt;
+    }
+    if (n > 0) hipLaunchKernelGGL((k_bwd_dkdv<D>), dim3((unsigned)n), dim3(256), 0, s, p, expand, (int)n);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const BwdParams& p, int32_t d, hipStream_t s) {
+  if (p.bm != BM || p.bn != BN) return hipErrorInvalidValue;
+  if (d == 128) return launch_d<128>(p, s);
+  if (d == 64) return launch_d<64>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fmask

@@ -96,6 +96,30 @@ __global__ void __launch_bounds__(256) k_tile_lists(const uint8_t* state, int32_
   if (lane == 0) count[row] = running;
 }
 
+// One wave per tile column (mask m, key tile kt): compaction of the non-SKIP
+// query tiles of that column, read from the row-major state table.
+__global__ void __launch_bounds__(256) k_tile_cols(const uint8_t* state, int32_t cols, int32_t nqt,
+                                                   int32_t nkt, int32_t* list, int32_t* count) {
+  int col = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int lane = threadIdx.x & 63;
+  if (col >= cols) return;
+  const int m = col / nkt, kt = col % nkt;
+  const uint8_t* st = state + (int64_t)m * nqt * nkt + kt;
+  int32_t* out = list + (int64_t)col * nqt;
+  int running = 0;
+  for (int base = 0; base < nqt; base += 64) {
+    int qt = base + lane;
+    uint8_t s = qt < nqt ? st[(int64_t)qt * nkt] : (uint8_t)FMASK_SKIP;
+    bool keep = s != FMASK_SKIP;
+    uint64_t bal = __ballot(keep);
+    int rank = running + __popcll(bal & ((1ull << lane) - 1ull));
+    if (keep) out[rank] = (int32_t)((uint32_t)qt | (s == FMASK_FULL ? FMASK_LIST_FULL_BIT : 0u));
+    running += __popcll(bal);
+  }
+  for (int i = running + lane; i < nqt; i += 64) out[i] = 0;
+  if (lane == 0) count[col] = running;
+}
+
 // Rank of every tile row under (count descending, index ascending); the rank
 // is unique, so order[rank] = row is a permutation.
 __global__ void __launch_bounds__(256) k_tile_order(const int32_t* count, int32_t rows,
@@ -153,6 +177,15 @@ hipError_t launch_tile_lists(const uint8_t* state, int32_t rows, int32_t nkt, in
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_tile_lists, dim3((rows + 3) / 4), dim3(256), 0, s, state, rows, nkt, list,
                      count);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_cols(const uint8_t* state, int32_t nmask, int32_t nqt, int32_t nkt,
+                            int32_t* list, int32_t* count, hipStream_t s) {
+  const int64_t cols = (int64_t)nmask * nkt;
+  if (cols <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_tile_cols, dim3((unsigned)((cols + 3) / 4)), dim3(256), 0, s, state,
+                     (int32_t)cols, nqt, nkt, list, count);
   return hipGetLastError();
 }
 

@@ -69,6 +69,8 @@ hipError_t launch_classify_bitmap(const uint8_t* bstate, int32_t nmask, int32_t 
                                   uint8_t* state, hipStream_t s);
 hipError_t launch_tile_lists(const uint8_t* state, int32_t rows, int32_t nkt, int32_t* list,
                              int32_t* count, hipStream_t s);
+hipError_t launch_tile_cols(const uint8_t* state, int32_t nmask, int32_t nqt, int32_t nkt,
+                            int32_t* list, int32_t* count, hipStream_t s);
 hipError_t launch_tile_order(const int32_t* count, int32_t rows, int32_t* order, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
@@ -102,6 +104,34 @@ struct TileAttnParams {
 hipError_t launch_attn_tile_bf16(const TileAttnParams& p, int32_t d, hipStream_t s);
 hipError_t launch_attn_tile_f32(const TileAttnParams& p, int32_t d, hipStream_t s);
 hipError_t launch_attn_o3_bf16(const TileAttnParams& p, int32_t d, hipStream_t s);
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* ws;           // [b][hq][sq] x {D_i, LSE_i log2(e) (+inf for empty rows)}
+  int64_t qs[3], ks[3], vs[3], os[3];
+  int32_t b, hq, hkv, group;
+  int32_t sq, skv;
+  float scale;
+  const int32_t* list;
+  const int32_t* count;
+  const int32_t* order;
+  const int32_t* col_list;
+  const int32_t* col_count;
+  const int32_t* col_order;
+  int32_t nqt, nkt, bm, bn;
+  int32_t mb, mh;
+  const int32_t* iv;   // [mb][mh][4][skv]
+};
+
+hipError_t launch_attn_bwd_bf16(const BwdParams& p, int32_t d, hipStream_t s);
 
 struct SelAttnParams {
   const void* q;

@@ -45,6 +45,11 @@ def streams(k):
     return [np.random.Generator(np.random.PCG64(s)) for s in seqs]
 
 
+def grad_stream(k):
+    """A fifth independent generator (output gradient dO) for workload number k."""
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(1000 * k).spawn(5)[4]))
+
+
 def _f32_to_bf16_bits(x):
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     rounding = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
@@ -245,3 +250,9 @@ def draw_qkv(w):
     ks = (w["B"], w["Hkv"], w["Skv"], w["D"])
     gen = normal_bf16 if w["dtype"] == "bf16" else normal_f32
     return gen(rq, qs), gen(rk, ks), gen(rv, ks)
+
+
+def draw_dout(w):
+    """Output gradient dO of workload w, shaped like Q: N(0, 1) as bf16 bits or float32."""
+    gen = normal_bf16 if w["dtype"] == "bf16" else normal_f32
+    return gen(grad_stream(w["seed"]), (w["B"], w["Hq"], w["Sq"], w["D"]))

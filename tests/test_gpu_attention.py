@@ -106,7 +106,7 @@ def test_small_bitmap_and_raw_intervals(dtype):
 
 @pytest.mark.parametrize("bm", [256, 128, 64])
 def test_interval_tile_shapes(bm):
-    """Every bf16 interval kernel (256-row ping-pong, 128-row, 64-row) on ragged shapes."""
+    """Every bf16 interval kernel (256-, 128- and 64-row tiles) on ragged shapes."""
     for S, K, spec in [(333, 333, dict(family="causal_document", sq=333, skv=333,
                                        cu_seg=np.array([0, 70, 200, 333], dtype=np.int32))),
                        (700, 700, dict(family="band", sq=700, skv=700, pre=100, next=5)),

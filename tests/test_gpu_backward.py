@@ -1,0 +1,114 @@
+"""GPU attention backward (fmask_attn_bwd, through the C ABI) vs the float64
+oracle gradient (oracle.attention.attention_backward_dense).
+
+The forward output O and LSE the backward consumes come from the GPU forward
+(they are inputs of the operation, like dO); the reference gradient is the
+oracle's, computed from the same bf16 Q, K, V and dO alone.  Small shapes span
+several tiles with ragged tails, GQA and per-head masks; the 8K causal-document
+workload is checked on one K/V head group at its full size.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import attention as OA
+from tests.helpers import to_device, to_f64
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+fm = pytest.importorskip("mask_aware_block_amd")
+
+# bf16 gradients with fp32 accumulation.  Relative to the largest reference
+# magnitude of each tensor: every product P dO, dS Q, dS K enters the MFMA
+# with P or dS rounded to bf16 (2^-9 relative) and the result is rounded to
+# bf16 once more (2^-9), D_i comes from the bf16-rounded forward output.
+GRAD_TOL = dict(max_rel=2e-2, mean_rel=2e-3)
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _grad_check(w, spec, what, heads=None):
+    arrays = synth.draw_qkv(w)
+    do_bits = synth.draw_dout(w)
+    q, k, v = to_device(w, arrays)
+    do = torch.from_numpy(do_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    enc = fm.encode(spec)
+    tiles = fm.classify(enc, 128, 64)
+    o, lse = fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"])
+    dq, dk, dv = fm.attn_bwd(q, k, v, o, lse, do, enc, tiles, scale=w["scale"])
+    torch.cuda.synchronize()
+    qq, kk, vv, dd = (to_f64(w, a) for a in (*arrays, do_bits))
+    hq0, hq1 = heads or (0, w["Hq"])
+    G = w["Hq"] // w["Hkv"]
+    sl_q = slice(hq0, hq1)
+    sl_k = slice(hq0 // G, hq1 // G)
+    vis = OA.spec_vis_fn(spec)
+    fn = (lambda b, h, rows: vis(b, h + hq0, rows))
+    rq, rk, rv = OA.attention_backward_dense(qq[:, sl_q], kk[:, sl_k], vv[:, sl_k], dd[:, sl_q], fn, w["scale"])
+    out = {}
+    for name, got, ref in (("dq", dq[:, sl_q], rq), ("dk", dk[:, sl_k], rk), ("dv", dv[:, sl_k], rv)):
+        g = got.float().cpu().numpy().astype(np.float64)
+        assert np.isfinite(g).all(), f"{what}: {name} not finite"
+        scale = max(np.abs(ref).max(), 1e-6)
+        err = np.abs(g - ref)
+        out[name] = (err.max() / scale, err.mean() / scale)
+        assert err.max() <= GRAD_TOL["max_rel"] * scale, f"{what}: {name} max err {err.max():.3e} (ref max {scale:.3e})"
+        assert err.mean() <= GRAD_TOL["mean_rel"] * scale, f"{what}: {name} mean err {err.mean():.3e}"
+    print(what, {k: (f"{a:.2e}", f"{b:.2e}") for k, (a, b) in out.items()}, flush=True)
+    return out
+
+
+def _small(D, S, K, Hq=4, Hkv=2, B=1, seed=21):
+    return dict(name="small", seed=seed, B=B, Hq=Hq, Hkv=Hkv, Sq=S, Skv=K, D=D, dtype="bf16",
+                scale=1 / math.sqrt(D))
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("S,K", [(333, 333), (200, 461)])
+def test_small_families(D, S, K):
+    w = _small(D, S, K)
+    rng = np.random.default_rng(S + K)
+    specs = [dict(family="causal", sq=S, skv=K), dict(family="band", sq=S, skv=K, pre=40, next=3),
+             dict(family="band", sq=S, skv=K, pre=9, next=-3)]
+    if S == K:
+        cu = np.unique(np.concatenate(([0, S], rng.integers(1, S, 6)))).astype(np.int32)
+        specs += [dict(family="causal_document", sq=S, skv=K, cu_seg=cu),
+                  dict(family="shared_question", sq=S, skv=K, cu_seg=cu),
+                  dict(family="document", sq=S, skv=K, cu_seg=cu)]
+    else:
+        specs += [dict(family="causal_bottom_right", sq=S, skv=K)]
+    for spec in specs:
+        _grad_check(w, spec, f"{spec['family']} d{D} {S}x{K}")
+
+
+def test_gqa_batch_and_per_head_masks():
+    S, K = 300, 260
+    w = _small(128, S, K, Hq=4, Hkv=2, B=2, seed=22)
+    rng = np.random.default_rng(5)
+    raw = rng.integers(-10, S + 10, size=(2, 4, 4, K)).astype(np.int32)
+    _grad_check(w, dict(family="intervals", sq=S, skv=K, batch=2, heads=4, raw_intervals=raw),
+                "raw intervals per (batch, head)")
+    w8 = _small(128, 257, 257, Hq=8, Hkv=1, B=2, seed=23)
+    _grad_check(w8, dict(family="causal", sq=257, skv=257), "gqa 8/1")
+
+
+def test_full_size_causal_doc_8k_one_group():
+    w = synth.workload("causal_doc_8k")
+    _grad_check(w, w["mask"], "causal_doc_8k heads 0..3", heads=(0, 4))
+
+
+def test_unsupported_combinations_are_refused():
+    w = _small(128, 64, 64)
+    q, k, v = to_device(w, synth.draw_qkv(w))
+    enc = fm.encode(dict(family="causal", sq=64, skv=64))
+    t64 = fm.classify(enc, 64, 64)
+    o, lse = fm.attn_fwd(q, k, v, enc, fm.classify(enc, 128, 64), scale=w["scale"])
+    with pytest.raises(fm.FmaskError) as ei:
+        fm.attn_bwd(q, k, v, o, lse, torch.zeros_like(o), enc, t64)
+    assert ei.value.status == fm.ERR_UNSUPPORTED

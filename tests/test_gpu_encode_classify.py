@@ -196,6 +196,8 @@ def test_full_size_tables(name):
     bm, bn = fm.preferred_tile(w["dtype"], w["D"], enc.kind)
     t = fm.classify(enc, bm, bn)
     st, ls, cn, od = [x.cpu().numpy() for x in t.arrays()]
+    col_ls, col_cn, col_od = [x.cpu().numpy() for x in t.columns()]
+    allcc = []
     S = w["Sq"]
     rng = np.random.default_rng(0)
     nb = spec.get("batch", 1)
@@ -217,6 +219,12 @@ def test_full_size_tables(name):
         np.testing.assert_array_equal(ls[b, 0], el)
         np.testing.assert_array_equal(cn[b, 0], ec)
         allc.append(ec)
+        # the same table by key-tile column
+        cl, cc = OE.tile_lists(exp_st.T)
+        np.testing.assert_array_equal(col_ls[b, 0], cl)
+        np.testing.assert_array_equal(col_cn[b, 0], cc)
+        allcc.append(cc)
     np.testing.assert_array_equal(od, OE.tile_order(np.concatenate(allc)))
+    np.testing.assert_array_equal(col_od, OE.tile_order(np.concatenate(allcc)))
     if enc.kind == fm.ENC_INTERVALS:
         np.testing.assert_array_equal(got_iv, OE.intervals_from_dense(colvis))

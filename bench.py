@@ -151,6 +151,43 @@ def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5):
     return rec
 
 
+def time_decode(torch, fm, synth, name, steps, warmup):
+    """Few-query selected-key attention: the one-pass kernel (one workgroup per
+    query and K/V head) against the split form (lists split over workgroups,
+    partial states merged), launch latency and gathered K/V bytes per second."""
+    w = synth.workload(name)
+    q, k, v = (_bf16(torch, a) for a in synth.draw_qkv(w))
+    enc = fm.encode(w["mask"])
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, 64 << 20), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(max(warmup, 5)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    t1 = timed(lambda: fm.attn_fwd(q, k, v, enc, None, scale=w["scale"], out=o, lse=lse))
+    ts = timed(lambda: fm.attn_fwd_split(q, k, v, enc, splits=0, scale=w["scale"], out=o, lse=lse,
+                                         workspace=ws))
+    ls, cn = enc.lists()
+    cells = int(cn.sum().item()) * w["mask"]["sel_cells"]
+    gathered = cells * w["Hkv"] * 2 * w["D"] * 2
+    del q, k, v, o, lse, ws
+    return dict(workload=name, B=w["B"], Hq=w["Hq"], Hkv=w["Hkv"], Sq=w["Sq"], Skv=w["Skv"], D=w["D"],
+                dtype="bf16", one_pass_us=t1 * 1e3, split_us=ts * 1e3, gathered_bytes=int(gathered),
+                split_gathered_gbs=gathered / (ts * 1e-3) / 1e9,
+                one_pass_gathered_gbs=gathered / (t1 * 1e-3) / 1e9)
+
+
 def time_backward(torch, fm, synth, name, steps, warmup):
     """Backward pass (fmask_attn_bwd) of a workload: attention-gradient launch time
     and effective TFLOP/s over 10 D flops per visible pair (QK^T, dO V^T, P^T dO,
@@ -288,6 +325,8 @@ def main():
                                         min(0.2, args.min_warmup_s)))
         for name in ("causal_doc_8k", "causal_doc_32k"):
             others.append(time_backward(torch, fm, synth, name, max(3, args.steps // 4), 2))
+        for name in ("selected_key_decode_128k", "selected_key_decode16_128k"):
+            others.append(time_decode(torch, fm, synth, name, max(20, args.steps), 5))
             torch.cuda.empty_cache()
 
     achieved = head["effective_flop"] / (head["attn_ms"] * 1e-3) / 1e12

@@ -246,10 +246,28 @@ fmask_status fmask_classify(const fmask_encoded *enc, int32_t bm, int32_t bn, vo
  * (preferred), 128x64; F32 64x64.  Other shapes return FMASK_ERR_UNSUPPORTED.
  * Supported: BF16 with d in {64, 128} on INTERVALS / BITMAP; F32 with d in
  * {64, 128} on INTERVALS / BITMAP; BF16 with d in {128, 256}, sel_cells == 32
- * and hq / hkv in {1, 2, 4, 8, 16} on SELECTED.                                 */
+ * and hq / hkv in {1, 2, 4, 8, 12, 16} on SELECTED.                             */
 fmask_status fmask_attn_fwd(const fmask_attn_args *args, const void *q, const void *k,
                             const void *v, void *o, float *lse, const fmask_encoded *enc,
                             const fmask_tiles *tiles, void *stream);
+
+/* Few-query (decode) form of fmask_attn_fwd for the SELECTED kind: each
+ * query's list is split over `splits` workgroups (0 = automatic: enough to
+ * cover the chip, at most one split per 4 entries), whose partial states
+ * (running max m, sum l, unnormalised O per query head) go to `workspace` and
+ * are merged by a second kernel with the split-K rule of the selected-key PR
+ * (factors exp(m_s - max_s m_s); a split that sees no valid entry carries
+ * m = -FLT_MAX, l = 0 and contributes nothing).  Same result as
+ * fmask_attn_fwd up to rounding order; meant for a handful of queries, where
+ * one workgroup per (query, K/V head) leaves the chip idle.  workspace: device
+ * buffer of fmask_attn_split_workspace_bytes(args, enc, splits) bytes (unused
+ * when the split count is 1).                                                  */
+size_t fmask_attn_split_workspace_bytes(const fmask_attn_args *args, const fmask_encoded *enc,
+                                        int32_t splits);
+fmask_status fmask_attn_fwd_split(const fmask_attn_args *args, const void *q, const void *k,
+                                  const void *v, void *o, float *lse, const fmask_encoded *enc,
+                                  int32_t splits, void *workspace, size_t workspace_bytes,
+                                  void *stream);
 
 /* Bytes of device workspace fmask_attn_bwd needs (one float per (batch, q
  * head, query row)); 0 if args is invalid.                                    */

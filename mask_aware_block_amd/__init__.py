@@ -83,7 +83,8 @@ class AttnArgs(ctypes.Structure):
 
 
 EXPORTS = ("fmask_encode_bytes", "fmask_encode", "fmask_classify_bytes", "fmask_classify",
-           "fmask_attn_fwd", "fmask_attn_bwd_workspace_bytes", "fmask_attn_bwd",
+           "fmask_attn_fwd", "fmask_attn_split_workspace_bytes", "fmask_attn_fwd_split",
+           "fmask_attn_bwd_workspace_bytes", "fmask_attn_bwd",
            "fmask_preferred_tile", "fmask_status_str", "fmask_last_error")
 
 _lib = None
@@ -116,6 +117,12 @@ def lib():
         L.fmask_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), _vp, _vp, _vp, _vp, _vp,
                                      ctypes.POINTER(Encoded), ctypes.POINTER(Tiles), _vp]
         L.fmask_attn_fwd.restype = ctypes.c_int32
+        L.fmask_attn_split_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(Encoded),
+                                                       ctypes.c_int32]
+        L.fmask_attn_split_workspace_bytes.restype = ctypes.c_size_t
+        L.fmask_attn_fwd_split.argtypes = [ctypes.POINTER(AttnArgs), _vp, _vp, _vp, _vp, _vp,
+                                           ctypes.POINTER(Encoded), ctypes.c_int32, _vp, ctypes.c_size_t, _vp]
+        L.fmask_attn_fwd_split.restype = ctypes.c_int32
         L.fmask_attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs)]
         L.fmask_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.fmask_attn_bwd.argtypes = [ctypes.POINTER(AttnArgs)] + [_vp] * 10 + [
@@ -370,6 +377,28 @@ def attn_fwd(q, k, v, enc, tiles=None, scale=None, out=None, lse=None, want_lse=
                           ctypes.byref(enc.struct),
                           ctypes.byref(tiles.struct) if tiles is not None else None,
                           _stream_handle(stream))
+    _check(st)
+    return out, lse
+
+
+def attn_fwd_split(q, k, v, enc, splits=0, scale=None, out=None, lse=None, workspace=None, stream=None):
+    """Few-query form of attn_fwd for selected-key lists (fmask_attn_fwd_split):
+    each list is split over `splits` workgroups (0 = automatic) and merged."""
+    torch = _torch()
+    L = lib()
+    if scale is None:
+        scale = 1.0 / float(q.shape[-1]) ** 0.5
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    a = attn_args(q, k, v, out, scale)
+    nbytes = L.fmask_attn_split_workspace_bytes(ctypes.byref(a), ctypes.byref(enc.struct), int(splits))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = L.fmask_attn_fwd_split(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                ctypes.byref(enc.struct), int(splits), _ptr(workspace), workspace.numel(),
+                                _stream_handle(stream))
     _check(st)
     return out, lse
 

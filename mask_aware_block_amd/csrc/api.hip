@@ -243,6 +243,39 @@ void preferred(int32_t dtype, int32_t d, int32_t kind, int32_t* bm, int32_t* bn)
 
 }  // namespace
 
+// Checks and parameters of the selected-key kernels (shared by the one-pass
+// and the split forms).
+fmask_status selected_params(const fmask_attn_args* a, const void* q, const void* k, const void* v,
+                             void* o, float* lse, const fmask_encoded* enc, SelAttnParams* p) {
+  const int32_t group = a->hq / a->hkv;
+  if (a->dtype != FMASK_BF16 || (a->d != 256 && a->d != 128) || enc->blk != 32 ||
+      !selected_group_supported(group))
+    return fail(FMASK_ERR_UNSUPPORTED, "selected-key kernel: bf16, d in {128, 256}, 32-cell blocks, "
+                                       "hq/hkv in {1,2,4,8,12,16}");
+  if (enc->heads != 1) return fail(FMASK_ERR_INVALID, "selected-key lists are shared by all heads");
+  p->q = q; p->k = k; p->v = v; p->o = o; p->lse = lse;
+  memcpy(p->qs, a->q_stride, sizeof(p->qs));
+  memcpy(p->ks, a->k_stride, sizeof(p->ks));
+  memcpy(p->vs, a->v_stride, sizeof(p->vs));
+  memcpy(p->os, a->o_stride, sizeof(p->os));
+  p->b = a->b; p->hq = a->hq; p->hkv = a->hkv; p->group = group;
+  p->sq = (int32_t)a->sq; p->skv = (int32_t)a->skv; p->scale = a->scale;
+  p->list = enc->sel_list; p->count = enc->sel_count;
+  p->n = enc->sel_n; p->cells = enc->blk; p->mb = enc->batch;
+  if ((int64_t)a->hkv * a->b * a->sq * 16 > INT32_MAX) return fail(FMASK_ERR_UNSUPPORTED, "grid too large");
+  return FMASK_OK;
+}
+
+// Splits per list for the split form: enough workgroups to cover the chip
+// twice (256 CUs), at least 4 entries (one per wave) per split.
+int32_t auto_splits(const fmask_attn_args* a, int32_t sel_n) {
+  const int64_t items = (int64_t)a->hkv * a->b * a->sq;
+  if (items <= 0) return 1;
+  int64_t sp = (2 * 256 + items - 1) / items;
+  const int64_t cap = std::max<int64_t>(1, (sel_n + 3) / 4);
+  return (int32_t)std::min<int64_t>(std::max<int64_t>(sp, 1), cap);
+}
+
 extern "C" {
 
 const char* fmask_status_str(fmask_status s) {
@@ -480,23 +513,10 @@ fmask_status fmask_attn_fwd(const fmask_attn_args* a, const void* q, const void*
   const int32_t group = a->hq / a->hkv;
 
   if (enc->kind == FMASK_ENC_SELECTED) {
-    if (a->dtype != FMASK_BF16 || (a->d != 256 && a->d != 128) || enc->blk != 32 ||
-        !(group == 1 || group == 2 || group == 4 || group == 8 || group == 16))
-      return fail(FMASK_ERR_UNSUPPORTED, "selected-key kernel: bf16, d in {128, 256}, 32-cell blocks, "
-                                         "hq/hkv in {1,2,4,8,16}");
-    if (enc->heads != 1) return fail(FMASK_ERR_INVALID, "selected-key lists are shared by all heads");
     SelAttnParams p{};
-    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
-    memcpy(p.qs, a->q_stride, sizeof(p.qs));
-    memcpy(p.ks, a->k_stride, sizeof(p.ks));
-    memcpy(p.vs, a->v_stride, sizeof(p.vs));
-    memcpy(p.os, a->o_stride, sizeof(p.os));
-    p.b = a->b; p.hq = a->hq; p.hkv = a->hkv; p.group = group;
-    p.sq = (int32_t)a->sq; p.skv = (int32_t)a->skv; p.scale = a->scale;
-    p.list = enc->sel_list; p.count = enc->sel_count;
-    p.n = enc->sel_n; p.cells = enc->blk; p.mb = enc->batch;
-    if ((int64_t)a->hkv * a->b * a->sq > INT32_MAX) return fail(FMASK_ERR_UNSUPPORTED, "grid too large");
-    return hip_status(launch_attn_selected_bf16(p, a->d, s), "selected-key attention kernel");
+    const fmask_status st = selected_params(a, q, k, v, o, lse, enc, &p);
+    if (st != FMASK_OK) return st;
+    return hip_status(launch_attn_selected_bf16(p, a->d, 1, nullptr, s), "selected-key attention kernel");
   }
 
   if (!tiles) return fail(FMASK_ERR_INVALID, "tile table required for this encoding");
@@ -543,6 +563,51 @@ fmask_status fmask_attn_fwd(const fmask_attn_args* a, const void* q, const void*
   else if (bm == 128 && enc->kind == FMASK_ENC_INTERVALS) e = launch_attn_o3_bf16(p, a->d, s);
   else e = launch_attn_tile_bf16(p, a->d, s);
   return hip_status(e, "attention kernel");
+}
+
+size_t fmask_attn_split_workspace_bytes(const fmask_attn_args* a, const fmask_encoded* enc, int32_t splits) {
+  if (!a || !enc || enc->kind != FMASK_ENC_SELECTED || splits < 0 || a->b < 1 || a->hkv < 1 ||
+      a->hq < 1 || a->hq % a->hkv || a->sq < 0 || a->sq > kMaxSeq)
+    return 0;
+  const int32_t ns = splits == 0 ? auto_splits(a, enc->sel_n) : splits;
+  const size_t floats = (size_t)a->hkv * a->b * a->sq * ns * (size_t)(a->hq / a->hkv) * (a->d + 2);
+  return std::max<size_t>(floats * sizeof(float), kAlign);
+}
+
+fmask_status fmask_attn_fwd_split(const fmask_attn_args* a, const void* q, const void* k, const void* v,
+                                  void* o, float* lse, const fmask_encoded* enc, int32_t splits,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!a || !enc) return fail(FMASK_ERR_INVALID, "null args or encoding");
+  if (enc->kind != FMASK_ENC_SELECTED) return fail(FMASK_ERR_UNSUPPORTED, "split form: SELECTED encoding only");
+  if (splits < 0 || splits > 64) return fail(FMASK_ERR_INVALID, "splits must be in [0, 64] (0 = automatic)");
+  if (a->b < 1 || a->hq < 1 || a->hkv < 1 || a->hq % a->hkv)
+    return fail(FMASK_ERR_INVALID, "need b, hq, hkv >= 1 and hq %% hkv == 0");
+  if (a->sq < 0 || a->skv < 0 || a->sq > kMaxSeq || a->skv > kMaxSeq)
+    return fail(FMASK_ERR_INVALID, "sq / skv out of range");
+  if (a->sq != enc->sq || a->skv != enc->skv) return fail(FMASK_ERR_INVALID, "sq / skv differ from the encoding");
+  if (!(enc->batch == 1 || enc->batch == a->b)) return fail(FMASK_ERR_INVALID, "encoding batch must be 1 or b");
+  if (!q || !k || !v || !o) return fail(FMASK_ERR_INVALID, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(FMASK_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
+  for (int i = 0; i < 3; ++i) {
+    if (a->q_stride[i] % 8 || a->k_stride[i] % 8 || a->v_stride[i] % 8 || a->o_stride[i] % 8)
+      return fail(FMASK_ERR_UNSUPPORTED, "strides must be multiples of 8 elements");
+    if (a->q_stride[i] < 0 || a->k_stride[i] < 0 || a->v_stride[i] < 0 || a->o_stride[i] < 0)
+      return fail(FMASK_ERR_INVALID, "negative stride");
+  }
+  SelAttnParams p{};
+  const fmask_status st = selected_params(a, q, k, v, o, lse, enc, &p);
+  if (st != FMASK_OK) return st;
+  const int32_t ns = splits == 0 ? auto_splits(a, enc->sel_n) : splits;
+  const size_t need = fmask_attn_split_workspace_bytes(a, enc, ns);
+  if (ns > 1) {
+    if (!workspace || ((uintptr_t)workspace % 16)) return fail(FMASK_ERR_INVALID, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FMASK_ERR_CAPACITY, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  return hip_status(launch_attn_selected_bf16(p, a->d, ns, (float*)workspace, (hipStream_t)stream),
+                    "selected-key split kernels");
 }
 
 size_t fmask_attn_bwd_workspace_bytes(const fmask_attn_args* a) {

@@ -35,8 +35,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ inline float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ inline float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
+// With nsplit > 1 (few-query / decode path) workgroup (item, s) takes only
+// list entries [s * per, (s + 1) * per) and writes its partial state (running
+// max M, sum L, unnormalised O per head) to the workspace instead of O / LSE;
+// k_selected_combine merges the splits.
 template <int D, int G>
-__global__ void __launch_bounds__(256) k_attn_selected(SelAttnParams p) {
+__global__ void __launch_bounds__(256) k_attn_selected(SelAttnParams p, int nsplit, float* ws) {
   constexpr int DPL = D / 64;  // output columns per lane
   __shared__ float Pl[4][CELLS][16];
   __shared__ float Al[4][16];
@@ -44,7 +48,8 @@ __global__ void __launch_bounds__(256) k_attn_selected(SelAttnParams p) {
   __shared__ float Co[4][G][D];
 
   const int64_t nq = (int64_t)p.b * p.sq;
-  const int64_t item = blockIdx.x;
+  const int64_t item = blockIdx.x / nsplit;
+  const int split = (int)(blockIdx.x % nsplit);
   const int kvh = (int)(item / nq);
   const int64_t rem = item % nq;
   const int b = (int)(rem / p.sq);
@@ -76,7 +81,9 @@ __global__ void __launch_bounds__(256) k_attn_selected(SelAttnParams p) {
     for (int j = 0; j < DPL; ++j) acc[g][j] = 0.f;
   float m_run = -FLT_MAX, l_run = 0.f;  // per column (head) lane
 
-  for (int e = w; e < cnt; e += 4) {
+  const int per = (cnt + nsplit - 1) / nsplit;
+  const int e0 = split * per, e1 = min(cnt, e0 + per);
+  for (int e = e0 + w; e < e1; e += 4) {
     const int64_t kbase = (int64_t)lst[e] * CELLS;
     // Gather: K rows as MFMA A operands, V rows for the VALU accumulation.
     bf16x8 ka[2][D / 32];
@@ -178,6 +185,9 @@ __global__ void __launch_bounds__(256) k_attn_selected(SelAttnParams p) {
   __syncthreads();
   for (int x = tid; x < G * D; x += 256) {
     const int g = x / D, d = x % D;
+    // A wave that saw no entry keeps m = -FLT_MAX and l = 0: its factor is
+    // exp2 of a large negative number (0), or 1 when every wave is empty, and
+    // either way it adds nothing.
     float M = fmaxf(fmaxf(Cm[0][g], Cm[1][g]), fmaxf(Cm[2][g], Cm[3][g]));
     float L = 0.f, acc_o = 0.f;
 #pragma unroll
@@ -185,6 +195,15 @@ __global__ void __launch_bounds__(256) k_attn_selected(SelAttnParams p) {
       float f = __builtin_amdgcn_exp2f((Cm[ww][g] - M) * c);
       L += Cl[ww][g] * f;
       acc_o += Co[ww][g][d] * f;
+    }
+    if (nsplit > 1) {
+      float* part = ws + (item * nsplit + split) * (size_t)(G * (D + 2));
+      part[2 * G + g * D + d] = acc_o;
+      if (d == 0) {
+        part[g] = M;
+        part[G + g] = L;
+      }
+      continue;
     }
     const int h = kvh * G + g;
     __bf16* O = (__bf16*)p.o + b * p.os[0] + h * p.os[1] + i * p.os[2];
@@ -194,28 +213,79 @@ __global__ void __launch_bounds__(256) k_attn_selected(SelAttnParams p) {
   }
 }
 
+// Merge of the split partial states: one workgroup per (item, head), one
+// thread per output column.  The combine rule is the one the split-K decode
+// path of the selected-key PR uses: factors exp(m_s - M) against the largest
+// partial max, with empty splits (m = -FLT_MAX, l = 0) contributing nothing.
+template <int D, int G>
+__global__ void __launch_bounds__(D) k_selected_combine(SelAttnParams p, int nsplit, const float* ws) {
+  const int64_t item = blockIdx.x / G;
+  const int g = (int)(blockIdx.x % G);
+  const int d = threadIdx.x;
+  const int64_t nq = (int64_t)p.b * p.sq;
+  const int kvh = (int)(item / nq);
+  const int64_t rem = item % nq;
+  const int b = (int)(rem / p.sq);
+  const int i = (int)(rem % p.sq);
+  const float c = p.scale * kLog2e;
+  const size_t stride = (size_t)G * (D + 2);
+  const float* base = ws + item * nsplit * stride;
+  float M = -FLT_MAX;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[s * stride + g]);
+  float L = 0.f, acc_o = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float f = __builtin_amdgcn_exp2f((base[s * stride + g] - M) * c);
+    L += base[s * stride + G + g] * f;
+    acc_o += base[s * stride + 2 * G + g * D + d] * f;
+  }
+  const int h = kvh * G + g;
+  __bf16* O = (__bf16*)p.o + b * p.os[0] + h * p.os[1] + i * p.os[2];
+  O[d] = (__bf16)(L > 0.f ? acc_o / L : 0.f);
+  if (d == 0 && p.lse)
+    p.lse[((int64_t)b * p.hq + h) * p.sq + i] = L > 0.f ? M * p.scale + logf(L) : -INFINITY;
+}
+
+template <int D, int G>
+hipError_t launch_dg(const SelAttnParams& p, int nsplit, float* ws, hipStream_t s) {
+  const int64_t items = (int64_t)p.hkv * p.b * p.sq;
+  hipLaunchKernelGGL((k_attn_selected<D, G>), dim3((unsigned)(items * nsplit)), dim3(256), 0, s, p, nsplit,
+                     ws);
+  if (nsplit > 1)
+    hipLaunchKernelGGL((k_selected_combine<D, G>), dim3((unsigned)(items * G)), dim3(D), 0, s, p, nsplit,
+                       (const float*)ws);
+  return hipGetLastError();
+}
+
 template <int D>
-hipError_t launch_d(const SelAttnParams& p, hipStream_t s) {
-  int64_t items = (int64_t)p.hkv * p.b * p.sq;
+hipError_t launch_d(const SelAttnParams& p, int nsplit, float* ws, hipStream_t s) {
+  const int64_t items = (int64_t)p.hkv * p.b * p.sq;
   if (items <= 0) return hipSuccess;
-  dim3 grid((unsigned)items), block(256);
   switch (p.group) {
-    case 1: hipLaunchKernelGGL((k_attn_selected<D, 1>), grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((k_attn_selected<D, 2>), grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((k_attn_selected<D, 4>), grid, block, 0, s, p); break;
-    case 8: hipLaunchKernelGGL((k_attn_selected<D, 8>), grid, block, 0, s, p); break;
-    case 16: hipLaunchKernelGGL((k_attn_selected<D, 16>), grid, block, 0, s, p); break;
+    case 1: return launch_dg<D, 1>(p, nsplit, ws, s);
+    case 2: return launch_dg<D, 2>(p, nsplit, ws, s);
+    case 4: return launch_dg<D, 4>(p, nsplit, ws, s);
+    case 8: return launch_dg<D, 8>(p, nsplit, ws, s);
+    case 12: return launch_dg<D, 12>(p, nsplit, ws, s);
+    case 16: return launch_dg<D, 16>(p, nsplit, ws, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_selected_bf16(const SelAttnParams& p, int32_t d, hipStream_t s) {
-  if (p.cells != CELLS) return hipErrorInvalidValue;
-  if (d == 256) return launch_d<256>(p, s);
-  if (d == 128) return launch_d<128>(p, s);
+bool selected_group_supported(int32_t group) {
+  return group == 1 || group == 2 || group == 4 || group == 8 || group == 12 || group == 16;
+}
+
+size_t selected_split_ws_floats(const SelAttnParams& p, int32_t d, int32_t nsplit) {
+  return (size_t)p.hkv * p.b * p.sq * nsplit * (size_t)p.group * (d + 2);
+}
+
+hipError_t launch_attn_selected_bf16(const SelAttnParams& p, int32_t d, int32_t nsplit, float* ws,
+                                     hipStream_t s) {
+  if (p.cells != CELLS || nsplit < 1 || (nsplit > 1 && !ws)) return hipErrorInvalidValue;
+  if (d == 256) return launch_d<256>(p, nsplit, ws, s);
+  if (d == 128) return launch_d<128>(p, nsplit, ws, s);
   return hipErrorInvalidValue;
 }
 

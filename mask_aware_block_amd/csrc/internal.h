@@ -148,6 +148,11 @@ struct SelAttnParams {
   int32_t n, cells, mb;
 };
 
-hipError_t launch_attn_selected_bf16(const SelAttnParams& p, int32_t d, hipStream_t s);
+// nsplit > 1: each query's list is split over nsplit workgroups whose partial
+// states go to ws (selected_split_ws_floats floats) and are merged afterwards.
+hipError_t launch_attn_selected_bf16(const SelAttnParams& p, int32_t d, int32_t nsplit, float* ws,
+                                     hipStream_t s);
+bool selected_group_supported(int32_t group);
+size_t selected_split_ws_floats(const SelAttnParams& p, int32_t d, int32_t nsplit);
 
 }  // namespace fmask

@@ -134,10 +134,14 @@ def block_pattern(rng, nbq, nbk, p_full=0.10, p_partial=0.05, blk=64):
     return state, index, bits
 
 
-def selected_lists(rng, sq, nblk, n=64, p_invalid=1 / 8):
-    """Per-query block lists int32 [sq][n] with duplicates, -1 entries and edge rows."""
+def selected_lists(rng, sq, nblk, n=64, p_invalid=1 / 8, edge_rows=True):
+    """Per-query block lists int32 [sq][n] with duplicates, -1 entries and (unless
+    edge_rows is false) the edge rows: query 0 all -1, query 1 one block
+    repeated, query 2 distinct blocks."""
     sel = rng.integers(0, nblk, size=(sq, n), dtype=np.int64)
     sel[rng.random((sq, n)) < p_invalid] = -1
+    if not edge_rows:
+        return sel.astype(np.int32)
     if sq > 0:
         sel[0] = -1
     if sq > 1:
@@ -235,12 +239,24 @@ def workload(name, **over):
         w["mask"] = dict(family="selected_key", sq=w["Sq"], skv=w["Skv"], batch=1,
                          sel=selected_lists(rng, w["Sq"], nblk)[None], sel_cells=cells)
         return w
+    if name in ("selected_key_decode_128k", "selected_key_decode16_128k"):
+        # few-query (decode) form: 1 or 16 queries at the end of a 128K context,
+        # ordinary lists (no forced edge rows)
+        sq = 1 if name == "selected_key_decode_128k" else 16
+        w = _base(name, 11 if sq == 1 else 12, 1, 32, 8, sq, 131072, 256, "bf16")
+        w.update(over)
+        cells = 32
+        rng = streams(w["seed"])[3]
+        nblk = -(-w["Skv"] // cells)
+        w["mask"] = dict(family="selected_key", sq=w["Sq"], skv=w["Skv"], batch=1,
+                         sel=selected_lists(rng, w["Sq"], nblk, edge_rows=False)[None], sel_cells=cells)
+        return w
     raise KeyError(name)
 
 
 WORKLOADS = ("tiny_causal_doc", "causal_doc_8k", "causal_doc_32k", "shared_question_32k",
              "band_32k", "band_neg_4k", "block_bitmap_16k", "tree_4k", "tree_4k_dfs",
-             "selected_key_128k")
+             "selected_key_128k", "selected_key_decode_128k", "selected_key_decode16_128k")
 
 
 def draw_qkv(w):

@@ -38,11 +38,19 @@ selected_key          per query a list of block indices of `sel_cells` cells;
                       duplicate entries skipped; 32-cell blocks).
 intervals             raw per-column masked intervals: masked iff
                       UTS_c <= r < UTE_c or LTS_c <= r < LTE_c.
+varlen                packed batch of segments (cumulative query lengths cu_q,
+                      key lengths cu_k): row r of segment s sees only columns of
+                      segment s; with ii, jj the positions inside the segment and
+                      off = K_s - Q_s, mode "full" sees all, "causal" jj <= ii,
+                      "causal_bottom_right" jj <= ii + off, "band" rr - pre <= jj
+                      <= rr + next (rr = ii + off), "prefix" jj < prefix_s or
+                      jj <= ii + off.  Ascend sparseMode page (actual_seq_qlen /
+                      actual_seq_kvlen, modes 2, 3, 4, 5, 7, 8).
 
 Spec keys: sq, skv and, per family, cu_seg (cumulative boundaries, first 0, last
 Sq), pre, next, tree_prefix, tree_parent, blk_state [B][H][nbq][nbk],
 blk_index (same shape), blk_bits [pool][64] (uint64), force_diag, sel [B][Sq][n],
-sel_cells, raw_intervals [B][H][4][Skv].
+sel_cells, raw_intervals [B][H][4][Skv], cu_q, cu_k, seg_mode, seg_prefix.
 """
 
 import numpy as np
@@ -139,6 +147,40 @@ def dense_vis(spec, b=0, h=0, rows=None):
         rr = np.broadcast_to(np.arange(lists.shape[0])[:, None], lists.shape)
         blockvis[rr[valid], lists[valid]] = True
         return blockvis[:, c[0] // cells]
+    if fam == "varlen":
+        # Packed variable-length batch (Ascend sparseMode page, actual_seq_qlen /
+        # actual_seq_kvlen): row i of query segment s sees only the key columns
+        # of segment s, under that segment's mode, with positions taken inside
+        # the segment and the causal / band anchor at the segment's lower right
+        # corner (upper left for "causal").
+        cq = np.asarray(spec["cu_q"], dtype=np.int64)
+        ck = np.asarray(spec["cu_k"], dtype=np.int64)
+        modes = list(spec["seg_mode"])
+        prefix = spec.get("seg_prefix")
+        vis = np.zeros((r.shape[0], skv), dtype=bool)
+        for s in range(len(modes)):
+            rows_s = (r[:, 0] >= cq[s]) & (r[:, 0] < cq[s + 1])
+            if not rows_s.any() or ck[s + 1] == ck[s]:
+                continue
+            ii = r[rows_s] - cq[s]                    # [R_s, 1]
+            jj = np.arange(ck[s + 1] - ck[s])[None, :]  # [1, K_s]
+            off = (ck[s + 1] - ck[s]) - (cq[s + 1] - cq[s])
+            m = modes[s]
+            if m == "full":
+                v = np.ones((ii.shape[0], jj.shape[1]), dtype=bool)
+            elif m == "causal":
+                v = jj <= ii
+            elif m == "causal_bottom_right":
+                v = jj <= ii + off
+            elif m == "band":
+                rr = ii + off
+                v = (jj >= rr - int(spec["pre"])) & (jj <= rr + int(spec["next"]))
+            elif m == "prefix":
+                v = (jj < int(prefix[s])) | (jj <= ii + off)
+            else:
+                raise ValueError(f"unknown varlen mode {m!r}")
+            vis[np.nonzero(rows_s)[0], ck[s]:ck[s + 1]] = np.broadcast_to(v, (ii.shape[0], jj.shape[1]))
+        return vis
     if fam == "intervals":
         raw = np.asarray(spec["raw_intervals"], dtype=np.int64)[bm, hm]
         uts, ute, lts, lte = raw[0][None, :], raw[1][None, :], raw[2][None, :], raw[3][None, :]

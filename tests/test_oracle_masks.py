@@ -278,3 +278,65 @@ def test_canonical_lists():
     assert lists[0, 0].tolist() == [3, 5, -1, -1, -1, -1]
     assert lists[0, 1].tolist() == [-1] * 6 and counts[0, 1] == 0
     assert lists[0, 2].tolist() == [0, 1, 2, 7, -1, -1] and counts[0, 2] == 4
+
+
+def test_varlen_single_segment_reduces_to_the_families():
+    for sq, skv in [(7, 7), (5, 9), (9, 4)]:
+        one = lambda mode, **kw: dict(family="varlen", sq=sq, skv=skv, cu_q=[0, sq], cu_k=[0, skv],
+                                      seg_mode=[mode], **kw)
+        np.testing.assert_array_equal(dense(one("full")), np.ones((sq, skv), dtype=bool))
+        np.testing.assert_array_equal(dense(one("causal")), dense(dict(family="causal", sq=sq, skv=skv)))
+        np.testing.assert_array_equal(dense(one("causal_bottom_right")),
+                                      dense(dict(family="causal_bottom_right", sq=sq, skv=skv)))
+        np.testing.assert_array_equal(dense(one("band", pre=2, next=1)),
+                                      dense(dict(family="band", sq=sq, skv=skv, pre=2, next=1)))
+        # prefix 0 is bottom-right causal; a prefix as wide as the keys is full
+        np.testing.assert_array_equal(dense(one("prefix", seg_prefix=[0])),
+                                      dense(dict(family="causal_bottom_right", sq=sq, skv=skv)))
+        np.testing.assert_array_equal(dense(one("prefix", seg_prefix=[skv])), np.ones((sq, skv), dtype=bool))
+
+
+def test_varlen_reproduces_the_ascend_split_examples():
+    """The packed masks of the Ascend varlen split examples: the named batch's
+    block equals the page's printed rows, every other batch follows its own
+    mode, and nothing crosses segments."""
+    with open(os.path.join(GOLDEN, "ascend_varlen_split.json")) as f:
+        gold = json.load(f)
+    # mode of the other batches on the same card: mode 7 comes from
+    # rightDownCausal, mode 8 from leftUpCausal (the page's notes)
+    base = {"mode7": "causal_bottom_right", "mode8": "causal"}
+    fam_to_mode = {"band": "band", "causal": "causal", "causal_bottom_right": "causal_bottom_right"}
+    for case in gold["cases"]:
+        cq, ck = [0] + case["actual_seq_qlen"], [0] + case["actual_seq_kvlen"]
+        n = len(cq) - 1
+        modes = [base[case["name"][:5]]] * n
+        modes[case["batch"]] = fam_to_mode[case["family"]]
+        spec = dict(family="varlen", sq=cq[-1], skv=ck[-1], cu_q=cq, cu_k=ck, seg_mode=modes,
+                    pre=case.get("pre", 0), next=case.get("next", 0))
+        vis = dense(spec)
+        b = case["batch"]
+        block = vis[cq[b]:cq[b + 1], ck[b]:ck[b + 1]]
+        np.testing.assert_array_equal(block.astype(int), np.array(case["expected"]), err_msg=case["name"])
+        for s in range(n):  # nothing outside the diagonal blocks
+            outside = np.ones(ck[-1], dtype=bool)
+            outside[ck[s]:ck[s + 1]] = False
+            assert not vis[cq[s]:cq[s + 1], outside].any(), case["name"]
+
+
+def test_varlen_intervals_round_trip():
+    rng = np.random.default_rng(9)
+    for _ in range(20):
+        n = int(rng.integers(1, 6))
+        ql = rng.integers(0, 9, n)
+        kl = rng.integers(0, 9, n)
+        cq = np.concatenate(([0], np.cumsum(ql))).tolist()
+        ck = np.concatenate(([0], np.cumsum(kl))).tolist()
+        modes = [str(m) for m in rng.choice(["full", "causal", "causal_bottom_right", "band", "prefix"], n)]
+        spec = dict(family="varlen", sq=cq[-1], skv=ck[-1], cu_q=cq, cu_k=ck, seg_mode=modes,
+                    pre=int(rng.integers(-2, 6)), next=int(rng.integers(-2, 4)),
+                    seg_prefix=rng.integers(0, 5, n).tolist())
+        vis = dense(spec)
+        if vis.size == 0:
+            continue
+        iv = E.intervals_from_dense(vis)  # every column stays within two masked runs
+        np.testing.assert_array_equal(E.dense_from_intervals(iv, vis.shape[0]), vis)

@@ -319,7 +319,7 @@ def main():
     head = time_workload(torch, fm, synth, "causal_doc_32k", args.steps, args.warmup, args.min_warmup_s)
     others = []
     if not args.headline_only:
-        for name in ("causal_doc_8k", "shared_question_32k", "band_32k", "band_neg_4k",
+        for name in ("causal_doc_8k", "shared_question_32k", "band_32k", "band_neg_4k", "varlen_prefill_32k",
                      "block_bitmap_16k", "tree_4k", "selected_key_128k"):
             others.append(time_workload(torch, fm, synth, name, max(3, args.steps // 2), 2,
                                         min(0.2, args.min_warmup_s)))

@@ -86,7 +86,22 @@ enum fmask_family {
    * UTS_j <= i < UTE_j or LTS_j <= i < LTE_j.                                   */
   FMASK_INTERVALS = 9,
   /* j <= i + skv - sq (anchored at the lower right corner, "rightDownCausal"). */
-  FMASK_CAUSAL_BOTTOM_RIGHT = 10
+  FMASK_CAUSAL_BOTTOM_RIGHT = 10,
+  /* Packed variable-length batch (Ascend "actual_seq_qlen / actual_seq_kvlen"):
+   * query rows [cu_seg[s], cu_seg[s+1]) attend only to key columns
+   * [cu_seg_k[s], cu_seg_k[s+1]) of the same segment s, under the segment's
+   * mode seg_mode[s] (fmask_varlen_mode), with ii, jj the row / column inside
+   * the segment and off = (segment keys) - (segment queries).               */
+  FMASK_VARLEN = 11
+};
+
+/* Per-segment modes of FMASK_VARLEN. */
+enum fmask_varlen_mode {
+  FMASK_VL_FULL = 0,                /* every (ii, jj)                                 */
+  FMASK_VL_CAUSAL = 1,              /* jj <= ii        (upper left, "leftUpCausal")   */
+  FMASK_VL_CAUSAL_BOTTOM_RIGHT = 2, /* jj <= ii + off  (lower right, "rightDownCausal") */
+  FMASK_VL_BAND = 3,                /* r - pre_tokens <= jj <= r + next_tokens, r = ii + off */
+  FMASK_VL_PREFIX = 4               /* jj < seg_prefix[s] or jj <= ii + off ("prefix") */
 };
 
 /* Kinds of canonical encoding written by fmask_encode. */
@@ -144,6 +159,14 @@ typedef struct fmask_mask_desc {
   /* raw intervals (device): int32 [batch][heads][4][skv] in the order
    * UTS, UTE, LTS, LTE.                                                         */
   const int32_t *raw_intervals;
+  /* varlen: (host) cu_seg holds the cumulative query lengths (n_seg + 1
+   * entries, from 0 to sq, non-decreasing), cu_seg_k the cumulative key
+   * lengths (from 0 to skv), seg_mode[n_seg] the modes, seg_prefix[n_seg] the
+   * prefix widths (read for FMASK_VL_PREFIX segments only; may be NULL if
+   * there is none); pre_tokens / next_tokens serve FMASK_VL_BAND segments.      */
+  const int32_t *cu_seg_k;
+  const int32_t *seg_mode;
+  const int32_t *seg_prefix;
 } fmask_mask_desc;
 
 /* Canonical encoding (host struct filled by fmask_encode; device views into the

@@ -25,8 +25,9 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_HIP = 0, -1, -2, -3, -4
 FAMILIES = {
     "causal": 1, "document": 2, "causal_document": 3, "shared_question": 4, "band": 5,
     "tree": 6, "block_bitmap": 7, "selected_key": 8, "intervals": 9,
-    "causal_bottom_right": 10,
+    "causal_bottom_right": 10, "varlen": 11,
 }
+VARLEN_MODES = {"full": 0, "causal": 1, "causal_bottom_right": 2, "band": 3, "prefix": 4}
 ENC_INTERVALS, ENC_BITMAP, ENC_SELECTED = 1, 2, 3
 SKIP, PARTIAL, FULL = 0, 1, 2
 DTYPES = {"f32": 0, "bf16": 1}
@@ -46,7 +47,7 @@ class MaskDesc(ctypes.Structure):
         ("blk_state", _vp), ("blk_index", _vp), ("blk_bits", _vp), ("blk_pool_n", ctypes.c_int64),
         ("force_diag", ctypes.c_int32), ("reserved2", ctypes.c_int32),
         ("sel", _vp), ("sel_n", ctypes.c_int32), ("sel_cells", ctypes.c_int32),
-        ("raw_intervals", _vp),
+        ("raw_intervals", _vp), ("cu_seg_k", _vp), ("seg_mode", _vp), ("seg_prefix", _vp),
     ]
 
 
@@ -211,6 +212,18 @@ def make_desc(spec, device="cuda"):
         d.sel = sel.data_ptr()
         d.sel_n = sel.shape[-1]
         d.sel_cells = int(spec.get("sel_cells", 32))
+    if spec["family"] == "varlen":
+        cq = np.ascontiguousarray(np.asarray(spec["cu_q"], dtype=np.int32))
+        ck = np.ascontiguousarray(np.asarray(spec["cu_k"], dtype=np.int32))
+        md = np.ascontiguousarray(np.asarray([VARLEN_MODES[m] if isinstance(m, str) else int(m)
+                                              for m in spec["seg_mode"]], dtype=np.int32))
+        keep += [cq, ck, md]
+        d.cu_seg, d.n_seg = cq.ctypes.data, cq.size - 1
+        d.cu_seg_k, d.seg_mode = ck.ctypes.data, md.ctypes.data
+        if spec.get("seg_prefix") is not None:
+            pf = np.ascontiguousarray(np.asarray(spec["seg_prefix"], dtype=np.int32))
+            keep.append(pf)
+            d.seg_prefix = pf.ctypes.data
     if spec.get("raw_intervals") is not None:
         raw = _dev(spec["raw_intervals"], np.int32, device)
         keep.append(raw)

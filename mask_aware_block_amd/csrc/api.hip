@@ -52,7 +52,7 @@ bool is_segment_family(int f) {
 
 bool is_param_family(int f) {
   return f == FMASK_CAUSAL || f == FMASK_CAUSAL_BOTTOM_RIGHT || f == FMASK_BAND || f == FMASK_TREE ||
-         is_segment_family(f);
+         f == FMASK_VARLEN || is_segment_family(f);
 }
 
 // Tree analysis on the host copy of the parent array: validity, and whether
@@ -100,6 +100,26 @@ fmask_status check_desc(const fmask_mask_desc* d, int* kind) {
         if (d->cu_seg[s + 1] <= d->cu_seg[s])
           return fail(FMASK_ERR_INVALID, "cu_seg not strictly increasing at %d", s);
       if (d->cu_seg[d->n_seg] != d->sq) return fail(FMASK_ERR_INVALID, "cu_seg[n_seg] != sq");
+      *kind = FMASK_ENC_INTERVALS;
+      return FMASK_OK;
+    }
+    case FMASK_VARLEN: {
+      if (!d->cu_seg || !d->cu_seg_k || !d->seg_mode || d->n_seg < 1)
+        return fail(FMASK_ERR_INVALID, "varlen needs cu_seg, cu_seg_k, seg_mode and n_seg >= 1");
+      if (d->n_seg > (1 << 24)) return fail(FMASK_ERR_INVALID, "too many segments");
+      if (d->cu_seg[0] != 0 || d->cu_seg_k[0] != 0)
+        return fail(FMASK_ERR_INVALID, "cu_seg[0] and cu_seg_k[0] must be 0");
+      for (int s = 0; s < d->n_seg; ++s) {
+        if (d->cu_seg[s + 1] < d->cu_seg[s] || d->cu_seg_k[s + 1] < d->cu_seg_k[s])
+          return fail(FMASK_ERR_INVALID, "cumulative lengths decrease at segment %d", s);
+        const int m = d->seg_mode[s];
+        if (m < FMASK_VL_FULL || m > FMASK_VL_PREFIX)
+          return fail(FMASK_ERR_INVALID, "seg_mode[%d] = %d is not a varlen mode", s, m);
+        if (m == FMASK_VL_PREFIX && (!d->seg_prefix || d->seg_prefix[s] < 0))
+          return fail(FMASK_ERR_INVALID, "seg_prefix[%d] missing or negative", s);
+      }
+      if (d->cu_seg[d->n_seg] != d->sq || d->cu_seg_k[d->n_seg] != d->skv)
+        return fail(FMASK_ERR_INVALID, "cumulative lengths must end at sq and skv");
       *kind = FMASK_ENC_INTERVALS;
       return FMASK_OK;
     }
@@ -157,6 +177,8 @@ EncLayout enc_layout(const fmask_mask_desc* d, int kind) {
   if (kind == FMASK_ENC_INTERVALS) {
     L.iv = c.take((size_t)nmask * 4 * d->skv * sizeof(int32_t));
     if (is_segment_family(d->family)) L.cu = c.take((size_t)(d->n_seg + 1) * sizeof(int32_t));
+    // varlen: cu_q [n+1], cu_k [n+1], mode [n], prefix [n]
+    if (d->family == FMASK_VARLEN) L.cu = c.take((size_t)(4 * (int64_t)d->n_seg + 2) * sizeof(int32_t));
     if (d->family == FMASK_TREE) {
       L.parent = c.take((size_t)std::max(1, d->tree_n) * sizeof(int32_t));
       L.tree_hi = c.take((size_t)std::max(1, d->tree_n) * sizeof(int32_t));
@@ -351,6 +373,26 @@ fmask_status fmask_encode(const fmask_mask_desc* desc, void* out, size_t out_byt
         if (e != hipSuccess) return hip_status(e, "copy cu_seg");
         p.cu = cu;
         p.n_seg = desc->n_seg;
+      }
+      if (f == FMASK_VARLEN) {
+        const int n = desc->n_seg;
+        int32_t* cu = at<int32_t>(out, L.cu);
+        int32_t* cuk = cu + (n + 1);
+        int32_t* md = cuk + (n + 1);
+        int32_t* pf = md + n;
+        e = hipMemcpyAsync(cu, desc->cu_seg, (size_t)(n + 1) * sizeof(int32_t), hipMemcpyHostToDevice, s);
+        if (e == hipSuccess)
+          e = hipMemcpyAsync(cuk, desc->cu_seg_k, (size_t)(n + 1) * sizeof(int32_t), hipMemcpyHostToDevice, s);
+        if (e == hipSuccess)
+          e = hipMemcpyAsync(md, desc->seg_mode, (size_t)n * sizeof(int32_t), hipMemcpyHostToDevice, s);
+        if (e == hipSuccess && desc->seg_prefix)
+          e = hipMemcpyAsync(pf, desc->seg_prefix, (size_t)n * sizeof(int32_t), hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_status(e, "copy varlen segments");
+        p.cu = cu;
+        p.cu_k = cuk;
+        p.mode = md;
+        p.prefix = pf;
+        p.n_seg = n;
       }
       if (f == FMASK_TREE) {
         int32_t* par = at<int32_t>(out, L.parent);

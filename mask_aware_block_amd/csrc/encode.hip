@@ -77,6 +77,27 @@ __global__ void k_family_intervals(SegParams p, int32_t* iv) {
         vhi = j + p.pre - off + 1;
         break;
       }
+      case FMASK_VARLEN: {  // the key's segment s: its query rows, under the segment's mode
+        const int s = segment_of(p.cu_k, p.n_seg, j);
+        const int64_t qs = p.cu[s], qe = p.cu[s + 1], ks = p.cu_k[s];
+        const int64_t jj = j - ks, off = (int64_t)(p.cu_k[s + 1] - ks) - (qe - qs);
+        int64_t lo = qs, hi = qe;
+        switch (p.mode[s]) {
+          case FMASK_VL_CAUSAL: lo = qs + jj; break;
+          case FMASK_VL_CAUSAL_BOTTOM_RIGHT: lo = qs + jj - off; break;
+          case FMASK_VL_BAND:
+            lo = qs + jj - p.next - off;
+            hi = qs + jj + p.pre - off + 1;
+            break;
+          case FMASK_VL_PREFIX:
+            if (jj >= p.prefix[s]) lo = qs + jj - off;
+            break;
+          default: break;  // FMASK_VL_FULL
+        }
+        vlo = lo > qs ? lo : qs;
+        vhi = hi < qe ? hi : qe;
+        break;
+      }
       case FMASK_TREE: {  // prefix columns: causal; draft column c: its subtree rows
         vlo = j;
         if (j >= p.tree_prefix) vhi = (int64_t)p.tree_prefix + p.tree_hi[j - p.tree_prefix] + 1;

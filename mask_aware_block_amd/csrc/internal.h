@@ -22,6 +22,10 @@ struct SegParams {
   int64_t pre, next;  // band, clamped by the host to +-(sq + skv + 1)
   int32_t tree_prefix;
   const int32_t* tree_hi;  // per draft node: last descendant (interval-form tree)
+  // varlen: device copies of cumulative key lengths, modes and prefix widths
+  const int32_t* cu_k;
+  const int32_t* mode;
+  const int32_t* prefix;
 };
 
 hipError_t launch_encode_family_intervals(const SegParams& p, int32_t* iv, hipStream_t s);

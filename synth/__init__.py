@@ -239,6 +239,23 @@ def workload(name, **over):
         w["mask"] = dict(family="selected_key", sq=w["Sq"], skv=w["Skv"], batch=1,
                          sel=selected_lists(rng, w["Sq"], nblk)[None], sel_cells=cells)
         return w
+    if name == "varlen_prefill_32k":
+        # packed batch of sequences with a KV cache (chunked prefill): sequence
+        # lengths by the document law at 32768 keys; each sequence's new
+        # queries are its last quarter (multiples of 64 stay multiples of 16),
+        # bottom-right causal inside each sequence
+        w = _base(name, 13, 1, 32, 8, 0, 32768, 128, "bf16")
+        w.update(over)
+        rng = streams(w["seed"])[3]
+        klens = doc_lengths(rng, w["Skv"])
+        qlens = [L // 4 for L in klens]
+        w["Sq"] = int(sum(qlens))
+        w["mask"] = dict(family="varlen", sq=w["Sq"], skv=w["Skv"],
+                         cu_q=np.cumsum([0] + qlens).astype(np.int32),
+                         cu_k=np.cumsum([0] + klens).astype(np.int32),
+                         seg_mode=["causal_bottom_right"] * len(klens))
+        w["seq_lengths"] = dict(q=qlens, kv=klens)
+        return w
     if name in ("selected_key_decode_128k", "selected_key_decode16_128k"):
         # few-query (decode) form: 1 or 16 queries at the end of a 128K context,
         # ordinary lists (no forced edge rows)
@@ -256,7 +273,8 @@ def workload(name, **over):
 
 WORKLOADS = ("tiny_causal_doc", "causal_doc_8k", "causal_doc_32k", "shared_question_32k",
              "band_32k", "band_neg_4k", "block_bitmap_16k", "tree_4k", "tree_4k_dfs",
-             "selected_key_128k", "selected_key_decode_128k", "selected_key_decode16_128k")
+             "selected_key_128k", "selected_key_decode_128k", "selected_key_decode16_128k",
+             "varlen_prefill_32k")
 
 
 def draw_qkv(w):

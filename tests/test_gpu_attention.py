@@ -71,6 +71,14 @@ def _specs(S, K):
                      tree_parent=synth.random_tree(rng, 64, order="dfs"))]
     else:
         out += [dict(family="causal_bottom_right", sq=S, skv=K)]
+    # a packed variable-length batch over the same totals
+    ql = np.diff(np.unique(np.concatenate(([0, S], rng.integers(0, S, 3))))).tolist()
+    kl = np.diff(np.unique(np.concatenate(([0, K], rng.integers(0, K, len(ql) - 1))))).tolist()
+    if len(kl) == len(ql):
+        modes = (["causal_bottom_right", "band", "prefix", "full", "causal"] * 2)[:len(ql)]
+        out += [dict(family="varlen", sq=S, skv=K, cu_q=np.cumsum([0] + ql).astype(np.int32),
+                     cu_k=np.cumsum([0] + kl).astype(np.int32), seg_mode=modes, pre=30, next=2,
+                     seg_prefix=[16] * len(ql))]
     return out
 
 
@@ -153,7 +161,7 @@ def test_selected_small():
     _dense_check(w, spec, "selected per batch")
 
 
-FULL = ["causal_doc_8k", "causal_doc_32k", "shared_question_32k", "band_32k", "band_neg_4k",
+FULL = ["causal_doc_8k", "causal_doc_32k", "shared_question_32k", "band_32k", "band_neg_4k", "varlen_prefill_32k",
         "block_bitmap_16k", "tree_4k", "tree_4k_dfs", "selected_key_128k"]
 
 
@@ -165,8 +173,8 @@ def test_full_size_sampled(name):
     o, lse = _run(w, arrays)
     rng = np.random.default_rng(1)
     extra = []
-    if "cu_seg" in spec:
-        cu = np.asarray(spec["cu_seg"])
+    if "cu_seg" in spec or "cu_q" in spec:
+        cu = np.asarray(spec.get("cu_seg", spec.get("cu_q")))
         extra = list(cu[1:-1]) + list(cu[1:-1] - 1)
     samples = sample_rows(w, 96, rng, extra=tuple(int(x) for x in extra[:40]))
     decode = OA.bf16_bits_to_f64 if w["dtype"] == "bf16" else None

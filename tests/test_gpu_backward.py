@@ -83,6 +83,11 @@ def test_small_families(D, S, K):
                   dict(family="document", sq=S, skv=K, cu_seg=cu)]
     else:
         specs += [dict(family="causal_bottom_right", sq=S, skv=K)]
+    ql = [S // 3, S // 3, S - 2 * (S // 3)]
+    kl = [K // 2, K // 4, K - K // 2 - K // 4]
+    specs += [dict(family="varlen", sq=S, skv=K, cu_q=np.cumsum([0] + ql).astype(np.int32),
+                   cu_k=np.cumsum([0] + kl).astype(np.int32),
+                   seg_mode=["causal_bottom_right", "prefix", "band"], seg_prefix=[0, 20, 0], pre=25, next=1)]
     for spec in specs:
         _grad_check(w, spec, f"{spec['family']} d{D} {S}x{K}")
 

@@ -47,6 +47,19 @@ def _small_specs():
         dict(family="tree", sq=300, skv=300, tree_prefix=236,
              tree_parent=synth.random_tree(rng, 64, order="dfs")),
     ]
+    # packed variable-length batches: every mode, empty segments, Sq != Skv
+    for trial in range(3):
+        n = 6
+        ql = rng.integers(0, 90, n)
+        kl = rng.integers(0, 120, n)
+        ql[1] = 0
+        kl[3] = 0
+        modes = ["full", "causal", "causal_bottom_right", "band", "prefix", "causal_bottom_right"]
+        out.append(dict(family="varlen", sq=int(ql.sum()), skv=int(kl.sum()),
+                        cu_q=np.concatenate(([0], np.cumsum(ql))).astype(np.int32),
+                        cu_k=np.concatenate(([0], np.cumsum(kl))).astype(np.int32),
+                        seg_mode=modes[trial:] + modes[:trial], pre=20 + trial, next=-2 + 3 * trial,
+                        seg_prefix=rng.integers(0, 40, n).astype(np.int32)))
     return out
 
 
@@ -187,7 +200,7 @@ def test_selected_lists_exact():
 
 
 @pytest.mark.parametrize("name", ["causal_doc_8k", "causal_doc_32k", "shared_question_32k", "band_32k",
-                                  "band_neg_4k", "block_bitmap_16k"])
+                                  "band_neg_4k", "block_bitmap_16k", "varlen_prefill_32k"])
 def test_full_size_tables(name):
     """Full-size encodings and tile tables: every tile state, sampled columns."""
     w = synth.workload(name)

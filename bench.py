@@ -188,6 +188,36 @@ def time_decode(torch, fm, synth, name, steps, warmup):
                 one_pass_gathered_gbs=gathered / (t1 * 1e-3) / 1e9)
 
 
+def time_dense_encode(torch, fm, synth, name, steps):
+    """Dense-mask input: the workload's mask materialised as uint8 [Sq][Skv] on the
+    device (from its compressed encoding), then encoded back from the dense form
+    (automatic form; one synchronising flag read).  Reports the encode time and
+    the dense vs compressed bytes."""
+    w = synth.workload(name)
+    S, K = w["Sq"], w["Skv"]
+    # the dense input: the family's own encoding expanded on the device
+    iv = fm.encode(w["mask"]).intervals()[0, 0].long()  # [4][K]
+    dense = torch.empty((1, 1, S, K), dtype=torch.uint8, device="cuda")
+    for r0 in range(0, S, 2048):
+        rows = torch.arange(r0, min(S, r0 + 2048), device="cuda")[:, None]
+        masked = ((iv[0] <= rows) & (rows < iv[1])) | ((iv[2] <= rows) & (rows < iv[3]))
+        dense[0, 0, r0:r0 + rows.shape[0]] = (~masked).to(torch.uint8)
+    spec = dict(family="dense", sq=S, skv=K, batch=1, heads=1, dense=dense)
+    mi = fm.MaskInput(spec)
+    enc = fm.encode(mi)  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        enc = fm.encode(mi)
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / steps
+    comp = 4 * 4 * K if enc.kind == fm.ENC_INTERVALS else int(enc.buf.numel())
+    del dense
+    return dict(workload=name + "_dense_input", Sq=S, Skv=K, kind="intervals" if enc.kind == fm.ENC_INTERVALS
+                else "bitmap", encode_ms=t * 1e3, dense_bytes=S * K, compressed_bytes=comp,
+                dense_read_gbs=S * K / t / 1e9)
+
+
 def time_backward(torch, fm, synth, name, steps, warmup):
     """Backward pass (fmask_attn_bwd) of a workload: attention-gradient launch time
     and effective TFLOP/s over 10 D flops per visible pair (QK^T, dO V^T, P^T dO,
@@ -199,7 +229,7 @@ def time_backward(torch, fm, synth, name, steps, warmup):
     tiles = fm.classify(enc, 128, 64)
     o, lse = fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"])
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(q.shape[0] * q.shape[1] * q.shape[2] * 8, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(fm.attn_bwd_workspace_bytes(q, k, v, o, tiles), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     run = lambda: fm.attn_bwd(q, k, v, o, lse, do, enc, tiles, scale=w["scale"], dq=dq, dk=dk, dv=dv,
                               workspace=ws)
@@ -323,11 +353,14 @@ def main():
                      "block_bitmap_16k", "tree_4k", "selected_key_128k"):
             others.append(time_workload(torch, fm, synth, name, max(3, args.steps // 2), 2,
                                         min(0.2, args.min_warmup_s)))
+            torch.cuda.empty_cache()
         for name in ("causal_doc_8k", "causal_doc_32k"):
             others.append(time_backward(torch, fm, synth, name, max(3, args.steps // 4), 2))
+            torch.cuda.empty_cache()
         for name in ("selected_key_decode_128k", "selected_key_decode16_128k"):
             others.append(time_decode(torch, fm, synth, name, max(20, args.steps), 5))
             torch.cuda.empty_cache()
+        others.append(time_dense_encode(torch, fm, synth, "causal_doc_8k", 5))
 
     achieved = head["effective_flop"] / (head["attn_ms"] * 1e-3) / 1e12
     out = {

@@ -92,7 +92,13 @@ enum fmask_family {
    * [cu_seg_k[s], cu_seg_k[s+1]) of the same segment s, under the segment's
    * mode seg_mode[s] (fmask_varlen_mode), with ii, jj the row / column inside
    * the segment and off = (segment keys) - (segment queries).               */
-  FMASK_VARLEN = 11
+  FMASK_VARLEN = 11,
+  /* Dense visibility given element by element: uint8 dense[batch][heads][sq][skv]
+   * (device, row-major, nonzero = visible) -- the "allMask" input of the
+   * Ascend sparseMode page, or Binary Block Masking's full mask.  Encoded into
+   * the interval form when every column has at most two masked runs, else
+   * into the 64 x 64 bitmap form (see dense_form).                            */
+  FMASK_DENSE = 12
 };
 
 /* Per-segment modes of FMASK_VARLEN. */
@@ -167,6 +173,15 @@ typedef struct fmask_mask_desc {
   const int32_t *cu_seg_k;
   const int32_t *seg_mode;
   const int32_t *seg_prefix;
+  /* dense (device): uint8 [batch][heads][sq][skv]; dense_form selects the
+   * encoding: FMASK_ENC_BITMAP (always possible, asynchronous),
+   * FMASK_ENC_INTERVALS (FMASK_ERR_INVALID if a column has more than two
+   * masked runs), or 0 = the interval form when possible, else the bitmap
+   * form.  The last two read one flag back from the device, i.e. they
+   * synchronise `stream` (the only entry point that does).                      */
+  const uint8_t *dense;
+  int32_t dense_form;
+  int32_t reserved3;
 } fmask_mask_desc;
 
 /* Canonical encoding (host struct filled by fmask_encode; device views into the
@@ -215,13 +230,6 @@ typedef struct fmask_tiles {
   const int32_t *list;             /* [batch][heads][nqt][nkt]                  */
   const int32_t *count;            /* [batch][heads][nqt]                       */
   const int32_t *order;            /* [batch*heads*nqt]                         */
-  /* The same table by key-tile column (used by the backward pass):
-   * col_list[b][h][kt][0..col_count) holds the non-SKIP qt in ascending
-   * order (FMASK_LIST_FULL_BIT set for FULL tiles); col_order lists the
-   * batch*heads*nkt columns by decreasing count, ties by index.                */
-  const int32_t *col_list;         /* [batch][heads][nkt][nqt]                  */
-  const int32_t *col_count;        /* [batch][heads][nkt]                       */
-  const int32_t *col_order;        /* [batch*heads*nkt]                         */
 } fmask_tiles;
 
 /* Attention problem.  Q [b][hq][sq][d], K and V [b][hkv][skv][d], O like Q, in
@@ -292,9 +300,11 @@ fmask_status fmask_attn_fwd_split(const fmask_attn_args *args, const void *q, co
                                   int32_t splits, void *workspace, size_t workspace_bytes,
                                   void *stream);
 
-/* Bytes of device workspace fmask_attn_bwd needs (one float per (batch, q
- * head, query row)); 0 if args is invalid.                                    */
-size_t fmask_attn_bwd_workspace_bytes(const fmask_attn_args *args);
+/* Bytes of device workspace fmask_attn_bwd needs: two floats per (batch, q
+ * head, query row) and the tile table by key-tile column (per column the
+ * non-SKIP query tiles, their count, and a longest-first order of the
+ * columns); 0 if the arguments are invalid.                                   */
+size_t fmask_attn_bwd_workspace_bytes(const fmask_attn_args *args, const fmask_tiles *tiles);
 
 /* Gradient of fmask_attn_fwd (same args, encoding and tile table): given the
  * forward's output O and log-sum-exp LSE and the output gradient dO, writes
@@ -307,7 +317,7 @@ size_t fmask_attn_bwd_workspace_bytes(const fmask_attn_args *args);
  * Layouts: dQ like Q (q_stride), dK like K (k_stride), dV like V (v_stride),
  * O and dO share o_stride; LSE float [b][hq][sq] contiguous, as the forward
  * writes it.  workspace: device buffer of fmask_attn_bwd_workspace_bytes
- * bytes.  Supported: BF16, d in {64, 128}, INTERVALS encoding, the tile table
+ * bytes (16-byte aligned); its contents are rewritten by every call.  Supported: BF16, d in {64, 128}, INTERVALS encoding, the tile table
  * at 128 x 64 (fmask_preferred_tile); otherwise FMASK_ERR_UNSUPPORTED.         */
 fmask_status fmask_attn_bwd(const fmask_attn_args *args, const void *q, const void *k,
                             const void *v, const void *o, const float *lse, const void *dout,

@@ -25,7 +25,7 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_HIP = 0, -1, -2, -3, -4
 FAMILIES = {
     "causal": 1, "document": 2, "causal_document": 3, "shared_question": 4, "band": 5,
     "tree": 6, "block_bitmap": 7, "selected_key": 8, "intervals": 9,
-    "causal_bottom_right": 10, "varlen": 11,
+    "causal_bottom_right": 10, "varlen": 11, "dense": 12,
 }
 VARLEN_MODES = {"full": 0, "causal": 1, "causal_bottom_right": 2, "band": 3, "prefix": 4}
 ENC_INTERVALS, ENC_BITMAP, ENC_SELECTED = 1, 2, 3
@@ -48,6 +48,7 @@ class MaskDesc(ctypes.Structure):
         ("force_diag", ctypes.c_int32), ("reserved2", ctypes.c_int32),
         ("sel", _vp), ("sel_n", ctypes.c_int32), ("sel_cells", ctypes.c_int32),
         ("raw_intervals", _vp), ("cu_seg_k", _vp), ("seg_mode", _vp), ("seg_prefix", _vp),
+        ("dense", _vp), ("dense_form", ctypes.c_int32), ("reserved3", ctypes.c_int32),
     ]
 
 
@@ -68,7 +69,6 @@ class Tiles(ctypes.Structure):
         ("nkt", ctypes.c_int32), ("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
         ("reserved0", ctypes.c_int32), ("reserved1", ctypes.c_int32),
         ("state", _vp), ("list", _vp), ("count", _vp), ("order", _vp),
-        ("col_list", _vp), ("col_count", _vp), ("col_order", _vp),
     ]
 
 
@@ -124,7 +124,7 @@ def lib():
         L.fmask_attn_fwd_split.argtypes = [ctypes.POINTER(AttnArgs), _vp, _vp, _vp, _vp, _vp,
                                            ctypes.POINTER(Encoded), ctypes.c_int32, _vp, ctypes.c_size_t, _vp]
         L.fmask_attn_fwd_split.restype = ctypes.c_int32
-        L.fmask_attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs)]
+        L.fmask_attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(Tiles)]
         L.fmask_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.fmask_attn_bwd.argtypes = [ctypes.POINTER(AttnArgs)] + [_vp] * 10 + [
             ctypes.c_size_t, ctypes.POINTER(Encoded), ctypes.POINTER(Tiles), _vp]
@@ -224,6 +224,12 @@ def make_desc(spec, device="cuda"):
             pf = np.ascontiguousarray(np.asarray(spec["seg_prefix"], dtype=np.int32))
             keep.append(pf)
             d.seg_prefix = pf.ctypes.data
+    if spec["family"] == "dense":
+        dn = _dev(spec["dense"], np.uint8, device)
+        keep.append(dn)
+        d.dense = dn.data_ptr()
+        d.dense_form = {None: 0, "auto": 0, "intervals": ENC_INTERVALS, "bitmap": ENC_BITMAP}[
+            spec.get("dense_form")]
     if spec.get("raw_intervals") is not None:
         raw = _dev(spec["raw_intervals"], np.int32, device)
         keep.append(raw)
@@ -327,15 +333,6 @@ class TileTable:
         od = self._view(t.order, 4 * rows, torch.int32, (rows,))
         return st, ls, cn, od
 
-    def columns(self):
-        """(col_list [b][h][nkt][nqt], col_count [b][h][nkt], col_order [b*h*nkt])."""
-        torch = _torch()
-        t = self.struct
-        cols = t.batch * t.heads * t.nkt
-        ls = self._view(t.col_list, 4 * cols * t.nqt, torch.int32, (t.batch, t.heads, t.nkt, t.nqt))
-        cn = self._view(t.col_count, 4 * cols, torch.int32, (t.batch, t.heads, t.nkt))
-        od = self._view(t.col_order, 4 * cols, torch.int32, (cols,))
-        return ls, cn, od
 
 
 def classify(enc, bm=None, bn=None, dtype="bf16", d=128, stream=None):
@@ -416,6 +413,12 @@ def attn_fwd_split(q, k, v, enc, splits=0, scale=None, out=None, lse=None, works
     return out, lse
 
 
+def attn_bwd_workspace_bytes(q, k, v, out, tiles):
+    """Bytes of device workspace attn_bwd needs (fmask_attn_bwd_workspace_bytes)."""
+    return lib().fmask_attn_bwd_workspace_bytes(ctypes.byref(attn_args(q, k, v, out, 1.0)),
+                                                ctypes.byref(tiles.struct))
+
+
 def attn_bwd(q, k, v, out, lse, dout, enc, tiles, scale=None, dq=None, dk=None, dv=None,
              workspace=None, stream=None):
     """Gradient of the masked attention forward (fmask_attn_bwd).
@@ -435,7 +438,7 @@ def attn_bwd(q, k, v, out, lse, dout, enc, tiles, scale=None, dq=None, dk=None, 
     if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
         raise ValueError("dq, dk, dv must be laid out like q, k, v")
     a = attn_args(q, k, v, out, scale)
-    nbytes = L.fmask_attn_bwd_workspace_bytes(ctypes.byref(a))
+    nbytes = L.fmask_attn_bwd_workspace_bytes(ctypes.byref(a), ctypes.byref(tiles.struct))
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     st = L.fmask_attn_bwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),

@@ -155,6 +155,16 @@ fmask_status check_desc(const fmask_mask_desc* d, int* kind) {
         return fail(FMASK_ERR_INVALID, "raw_intervals missing");
       *kind = FMASK_ENC_INTERVALS;
       return FMASK_OK;
+    case FMASK_DENSE:
+      if (d->sq > 0 && d->skv > 0 && !d->dense) return fail(FMASK_ERR_INVALID, "dense mask missing");
+      if (d->dense_form != 0 && d->dense_form != FMASK_ENC_INTERVALS && d->dense_form != FMASK_ENC_BITMAP)
+        return fail(FMASK_ERR_INVALID, "dense_form must be 0, FMASK_ENC_INTERVALS or FMASK_ENC_BITMAP");
+      if ((int64_t)d->batch * d->heads * d->sq * d->skv > ((int64_t)1 << 40) ||
+          (int64_t)d->batch * d->heads * ceil_div(d->skv, 64) > INT32_MAX)
+        return fail(FMASK_ERR_UNSUPPORTED, "dense mask too large");
+      // the interval form is tried first unless the bitmap form is asked for
+      *kind = d->dense_form == FMASK_ENC_BITMAP ? FMASK_ENC_BITMAP : FMASK_ENC_INTERVALS;
+      return FMASK_OK;
     default:
       return fail(FMASK_ERR_INVALID, "unknown mask family %d", f);
   }
@@ -163,7 +173,7 @@ fmask_status check_desc(const fmask_mask_desc* d, int* kind) {
 struct EncLayout {
   int kind = 0;
   size_t total = 0;
-  size_t iv = 0, cu = 0, parent = 0, tree_hi = 0;
+  size_t iv = 0, cu = 0, parent = 0, tree_hi = 0, flag = 0;
   size_t bstate = 0, bindex = 0, bbits = 0, row_count = 0, row_offset = 0, pool_count = 0;
   size_t list = 0, count = 0;
   int64_t nbq = 0, nbk = 0, cap = 0;
@@ -174,6 +184,9 @@ EncLayout enc_layout(const fmask_mask_desc* d, int kind) {
   L.kind = kind;
   Carve c;
   const int64_t nmask = (int64_t)d->batch * d->heads;
+  // A dense mask of the automatic form may end up in either form: room for both.
+  const bool dense_auto = d->family == FMASK_DENSE && d->dense_form == 0;
+  if (d->family == FMASK_DENSE && kind == FMASK_ENC_INTERVALS) L.flag = c.take(sizeof(int32_t));
   if (kind == FMASK_ENC_INTERVALS) {
     L.iv = c.take((size_t)nmask * 4 * d->skv * sizeof(int32_t));
     if (is_segment_family(d->family)) L.cu = c.take((size_t)(d->n_seg + 1) * sizeof(int32_t));
@@ -183,7 +196,8 @@ EncLayout enc_layout(const fmask_mask_desc* d, int kind) {
       L.parent = c.take((size_t)std::max(1, d->tree_n) * sizeof(int32_t));
       L.tree_hi = c.take((size_t)std::max(1, d->tree_n) * sizeof(int32_t));
     }
-  } else if (kind == FMASK_ENC_BITMAP) {
+  }
+  if (kind == FMASK_ENC_BITMAP || dense_auto) {
     L.nbq = ceil_div(d->sq, kBlk);
     L.nbk = ceil_div(d->skv, kBlk);
     const int64_t nblocks = nmask * L.nbq * L.nbk;
@@ -197,7 +211,7 @@ EncLayout enc_layout(const fmask_mask_desc* d, int kind) {
     L.row_offset = c.take((size_t)std::max<int64_t>(1, nmask * L.nbq) * sizeof(int32_t));
     L.pool_count = c.take(sizeof(int32_t));
     if (d->family == FMASK_TREE) L.parent = c.take((size_t)std::max(1, d->tree_n) * sizeof(int32_t));
-  } else {
+  } else if (kind == FMASK_ENC_SELECTED) {
     L.list = c.take((size_t)d->batch * d->sq * d->sel_n * sizeof(int32_t));
     L.count = c.take((size_t)d->batch * d->sq * sizeof(int32_t));
   }
@@ -211,9 +225,8 @@ T* at(void* base, size_t off) {
 }
 
 struct TileLayout {
-  size_t state = 0, list = 0, count = 0, order = 0, col_list = 0, col_count = 0, col_order = 0,
-         total = 0;
-  int64_t nqt = 0, nkt = 0, rows = 0, cols = 0;
+  size_t state = 0, list = 0, count = 0, order = 0, total = 0;
+  int64_t nqt = 0, nkt = 0, rows = 0;
 };
 
 fmask_status check_tiles_args(const fmask_encoded* e, int32_t bm, int32_t bn) {
@@ -239,10 +252,6 @@ TileLayout tile_layout(const fmask_encoded* e, int32_t bm, int32_t bn) {
   T.list = c.take((size_t)T.rows * T.nkt * sizeof(int32_t));
   T.count = c.take((size_t)T.rows * sizeof(int32_t));
   T.order = c.take((size_t)T.rows * sizeof(int32_t));
-  T.cols = (int64_t)e->batch * e->heads * T.nkt;
-  T.col_list = c.take((size_t)T.cols * T.nqt * sizeof(int32_t));
-  T.col_count = c.take((size_t)T.cols * sizeof(int32_t));
-  T.col_order = c.take((size_t)T.cols * sizeof(int32_t));
   T.total = std::max<size_t>(c.off, kAlign);
   return T;
 }
@@ -353,6 +362,23 @@ fmask_status fmask_encode(const fmask_mask_desc* desc, void* out, size_t out_byt
   enc->skv = desc->skv;
 
   hipError_t e = hipSuccess;
+  if (kind == FMASK_ENC_INTERVALS && f == FMASK_DENSE) {
+    int32_t* iv = at<int32_t>(out, L.iv);
+    int32_t* bad = at<int32_t>(out, L.flag);
+    enc->intervals = iv;
+    e = launch_encode_dense_intervals(desc->dense, nmask, sq, skv, iv, bad, s);
+    if (e != hipSuccess) return hip_status(e, "dense encode kernel");
+    int32_t hbad = 0;  // the one synchronising read: which form holds the mask
+    e = hipMemcpyAsync(&hbad, bad, sizeof(int32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e, "read dense flag");
+    if (!hbad) return FMASK_OK;
+    if (desc->dense_form == FMASK_ENC_INTERVALS)
+      return fail(FMASK_ERR_INVALID, "a column of the dense mask has more than two masked runs");
+    kind = FMASK_ENC_BITMAP;  // automatic form: fall back to the bitmap encoding
+    enc->kind = kind;
+    enc->intervals = nullptr;
+  }
   if (kind == FMASK_ENC_INTERVALS) {
     int32_t* iv = at<int32_t>(out, L.iv);
     enc->intervals = iv;
@@ -429,6 +455,9 @@ fmask_status fmask_encode(const fmask_mask_desc* desc, void* out, size_t out_byt
         if (e != hipSuccess) return hip_status(e, "copy tree_parent");
       }
       src.parent = par;
+    } else if (f == FMASK_DENSE) {
+      src.kind = 2;
+      src.dense = desc->dense;
     } else {
       src.kind = 0;
       src.state = desc->blk_state;
@@ -486,7 +515,7 @@ fmask_status fmask_classify(const fmask_encoded* enc, int32_t bm, int32_t bn, vo
   if (!out || ((uintptr_t)out % kAlign)) return fail(FMASK_ERR_INVALID, "out must be 256-byte aligned");
   const TileLayout T = tile_layout(enc, bm, bn);
   if (out_bytes < T.total) return fail(FMASK_ERR_CAPACITY, "out has %zu bytes, %zu needed", out_bytes, T.total);
-  if (T.rows > INT32_MAX || T.cols > INT32_MAX || T.rows * T.nkt > ((int64_t)1 << 40))
+  if (T.rows > INT32_MAX || T.rows * T.nkt > ((int64_t)1 << 40))
     return fail(FMASK_ERR_UNSUPPORTED, "tile table too large");
   hipStream_t s = (hipStream_t)stream;
   memset(tiles, 0, sizeof(*tiles));
@@ -516,17 +545,7 @@ fmask_status fmask_classify(const fmask_encoded* enc, int32_t bm, int32_t bn, vo
   e = launch_tile_lists(state, (int32_t)T.rows, (int32_t)T.nkt, list, count, s);
   if (e != hipSuccess) return hip_status(e, "tile list kernel");
   e = launch_tile_order(count, (int32_t)T.rows, order, s);
-  if (e != hipSuccess) return hip_status(e, "tile order kernel");
-  int32_t* col_list = at<int32_t>(out, T.col_list);
-  int32_t* col_count = at<int32_t>(out, T.col_count);
-  int32_t* col_order = at<int32_t>(out, T.col_order);
-  tiles->col_list = col_list;
-  tiles->col_count = col_count;
-  tiles->col_order = col_order;
-  e = launch_tile_cols(state, nmask, (int32_t)T.nqt, (int32_t)T.nkt, col_list, col_count, s);
-  if (e != hipSuccess) return hip_status(e, "tile column kernel");
-  e = launch_tile_order(col_count, (int32_t)T.cols, col_order, s);
-  return hip_status(e, "tile column order kernel");
+  return hip_status(e, "tile order kernel");
 }
 
 fmask_status fmask_attn_fwd(const fmask_attn_args* a, const void* q, const void* k, const void* v, void* o,
@@ -652,9 +671,33 @@ fmask_status fmask_attn_fwd_split(const fmask_attn_args* a, const void* q, const
                     "selected-key split kernels");
 }
 
-size_t fmask_attn_bwd_workspace_bytes(const fmask_attn_args* a) {
-  if (!a || a->b < 1 || a->hq < 1 || a->sq < 0 || a->sq > kMaxSeq) return 0;
-  return std::max<size_t>((size_t)a->b * a->hq * a->sq * 2 * sizeof(float), kAlign);
+}  // extern "C"
+
+namespace {
+struct BwdLayout {
+  size_t rows = 0, col_list = 0, col_count = 0, col_order = 0, total = 0;
+  int64_t cols = 0;
+};
+BwdLayout bwd_layout(const fmask_attn_args* a, const fmask_tiles* t) {
+  BwdLayout L;
+  Carve c;
+  L.cols = (int64_t)t->batch * t->heads * t->nkt;
+  L.rows = c.take((size_t)a->b * a->hq * a->sq * 2 * sizeof(float));
+  L.col_list = c.take((size_t)L.cols * t->nqt * sizeof(int32_t));
+  L.col_count = c.take((size_t)L.cols * sizeof(int32_t));
+  L.col_order = c.take((size_t)L.cols * sizeof(int32_t));
+  L.total = std::max<size_t>(c.off, kAlign);
+  return L;
+}
+}  // namespace
+
+extern "C" {
+
+size_t fmask_attn_bwd_workspace_bytes(const fmask_attn_args* a, const fmask_tiles* t) {
+  if (!a || !t || a->b < 1 || a->hq < 1 || a->sq < 0 || a->sq > kMaxSeq || t->batch < 1 || t->heads < 1 ||
+      t->nqt < 0 || t->nkt < 0)
+    return 0;
+  return bwd_layout(a, t).total;
 }
 
 fmask_status fmask_attn_bwd(const fmask_attn_args* a, const void* q, const void* k, const void* v,
@@ -676,7 +719,7 @@ fmask_status fmask_attn_bwd(const fmask_attn_args* a, const void* q, const void*
   if (tiles->bm != 128 || tiles->bn != 64)
     return fail(FMASK_ERR_UNSUPPORTED, "backward: tile table at 128 x 64 (have %d x %d)", tiles->bm, tiles->bn);
   if (tiles->nqt != ceil_div(a->sq, 128) || tiles->nkt != ceil_div(a->skv, 64) ||
-      tiles->batch != enc->batch || tiles->heads != enc->heads || !tiles->col_list)
+      tiles->batch != enc->batch || tiles->heads != enc->heads)
     return fail(FMASK_ERR_INVALID, "tile table does not match the encoding");
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
     return fail(FMASK_ERR_INVALID, "null tensor pointer");
@@ -689,7 +732,7 @@ fmask_status fmask_attn_bwd(const fmask_attn_args* a, const void* q, const void*
     if (a->q_stride[i] < 0 || a->k_stride[i] < 0 || a->v_stride[i] < 0 || a->o_stride[i] < 0)
       return fail(FMASK_ERR_INVALID, "negative stride");
   }
-  const size_t need = fmask_attn_bwd_workspace_bytes(a);
+  const size_t need = fmask_attn_bwd_workspace_bytes(a, tiles);
   if (!workspace || ((uintptr_t)workspace % 16)) return fail(FMASK_ERR_INVALID, "workspace must be 16-byte aligned");
   if (workspace_bytes < need)
     return fail(FMASK_ERR_CAPACITY, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
@@ -700,19 +743,30 @@ fmask_status fmask_attn_bwd(const fmask_attn_args* a, const void* q, const void*
   if ((int64_t)a->b * a->hq * a->sq > INT32_MAX / 4) return fail(FMASK_ERR_UNSUPPORTED, "problem too large");
   BwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
-  p.dq = dq; p.dk = dk; p.dv = dv; p.ws = (float*)workspace;
+  p.dq = dq; p.dk = dk; p.dv = dv;
   memcpy(p.qs, a->q_stride, sizeof(p.qs));
   memcpy(p.ks, a->k_stride, sizeof(p.ks));
   memcpy(p.vs, a->v_stride, sizeof(p.vs));
   memcpy(p.os, a->o_stride, sizeof(p.os));
   p.b = a->b; p.hq = a->hq; p.hkv = a->hkv; p.group = a->hq / a->hkv;
   p.sq = (int32_t)a->sq; p.skv = (int32_t)a->skv; p.scale = a->scale;
+  const BwdLayout L = bwd_layout(a, tiles);
+  if (L.cols > INT32_MAX / 4) return fail(FMASK_ERR_UNSUPPORTED, "tile table too large");
   p.list = tiles->list; p.count = tiles->count; p.order = tiles->order;
-  p.col_list = tiles->col_list; p.col_count = tiles->col_count; p.col_order = tiles->col_order;
+  p.ws = at<float>(workspace, L.rows);
+  int32_t* col_list = at<int32_t>(workspace, L.col_list);
+  int32_t* col_count = at<int32_t>(workspace, L.col_count);
+  int32_t* col_order = at<int32_t>(workspace, L.col_order);
+  p.col_list = col_list; p.col_count = col_count; p.col_order = col_order;
   p.nqt = tiles->nqt; p.nkt = tiles->nkt; p.bm = tiles->bm; p.bn = tiles->bn;
   p.mb = enc->batch; p.mh = enc->heads;
   p.iv = enc->intervals;
   hipStream_t s = (hipStream_t)stream;
+  // the tile table by key-tile column, and its longest-first order
+  hipError_t ec = launch_tile_cols(tiles->state, enc->batch * enc->heads, tiles->nqt, tiles->nkt, col_list,
+                                   col_count, s);
+  if (ec == hipSuccess) ec = launch_tile_order(col_count, (int32_t)L.cols, col_order, s);
+  if (ec != hipSuccess) return hip_status(ec, "tile column kernels");
   return hip_status(launch_attn_bwd_bf16(p, a->d, s), "attention backward kernels");
 }
 

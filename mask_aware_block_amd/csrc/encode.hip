@@ -9,6 +9,8 @@
 // * Bitmap form: 64 x 64 blocks (Binary Block Masking) with exact states and a
 //   compact pool of 64 row words per PARTIAL block, in row-major block order.
 // * Selected-key lists (llama.cpp selected-key PR): valid, distinct, ascending.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace fmask {
@@ -159,6 +161,103 @@ __global__ void k_tree_hi(const int32_t* parent, int32_t n, int32_t* hi) {
   }
 }
 
+// ------------------------------------------------------------------ dense
+// The masked rows of one column over a range of rows, as at most two maximal
+// runs [s0, e0), [s1, e1) and their number n (capped at 3: more than two).
+struct Runs {
+  int32_t n, s0, e0, s1, e1;
+};
+
+// a then b, where b's rows follow a's: a run of b that starts where a's last
+// run ends continues it.
+__device__ inline Runs join(Runs a, Runs b) {
+  if (b.n == 0) return a;
+  if (a.n == 0) return b;
+  if (a.n >= 3 || b.n >= 3) return Runs{3, 0, 0, 0, 0};
+  const int32_t last_e = a.n == 1 ? a.e0 : a.e1;
+  if (last_e == b.s0) {  // the two runs meet
+    if (a.n == 1) return Runs{b.n, a.s0, b.e0, b.s1, b.e1};
+    if (b.n == 1) return Runs{2, a.s0, a.e0, a.s1, b.e0};
+    return Runs{3, 0, 0, 0, 0};
+  }
+  if (a.n + b.n > 2) return Runs{3, 0, 0, 0, 0};
+  return Runs{2, a.s0, a.e0, b.s0, b.e0};
+}
+
+__device__ inline int32_t ctz64(uint64_t w) { return w ? __builtin_ctzll(w) : 64; }
+
+// Runs of the set bits of w (bit r = row base + r masked).
+__device__ inline Runs runs_of(uint64_t w, int32_t base) {
+  Runs r{0, 0, 0, 0, 0};
+  const int32_t starts = __popcll(w & ~(w << 1));
+  if (starts == 0) return r;
+  if (starts > 2) return Runs{3, 0, 0, 0, 0};
+  const int32_t s0 = ctz64(w);
+  const int32_t e0 = s0 + ctz64(~(w >> s0));
+  r.n = starts;
+  r.s0 = base + s0;
+  r.e0 = base + e0;
+  if (starts == 2) {
+    const uint64_t rest = w & ~((e0 >= 64 ? ~0ull : (1ull << e0) - 1ull));
+    const int32_t s1 = ctz64(rest);
+    r.s1 = base + s1;
+    r.e1 = base + s1 + ctz64(~(rest >> s1));
+  }
+  return r;
+}
+
+// One workgroup (16 waves) per (mask, 64-column strip); lane = column.  Wave w
+// walks its own contiguous share of the rows 64 at a time (one byte per lane
+// per row: a wave reads 64 consecutive bytes of a row), turning each 64-row
+// chunk into a bit word and that word into runs; the 16 shares are then joined
+// in row order through LDS.  A mask with a column of more than two runs raises
+// *bad.
+constexpr int kDenseWaves = 16;
+
+__global__ void __launch_bounds__(1024) k_dense_intervals(const uint8_t* dense, int32_t sq, int32_t skv,
+                                                          int32_t nstrip, int32_t* iv, int32_t* bad) {
+  __shared__ Runs part[kDenseWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t m = blockIdx.x / nstrip;
+  const int32_t j = (blockIdx.x % nstrip) * 64 + lane;
+  const int32_t share = (((sq + kDenseWaves - 1) / kDenseWaves) + 63) & ~63;
+  const int32_t r0 = wave * share, r1 = min(sq, r0 + share);
+  Runs acc{0, 0, 0, 0, 0};
+  if (j < skv) {
+    const uint8_t* col = dense + (size_t)m * sq * skv + j;
+    for (int32_t base = r0; base < r1; base += 64) {
+      const int32_t rows = min(64, r1 - base);
+      uint64_t w = 0;
+      if (rows == 64) {
+#pragma unroll 16
+        for (int r = 0; r < 64; ++r) w |= (uint64_t)(col[(size_t)(base + r) * skv] == 0) << r;
+      } else {
+        for (int r = 0; r < rows; ++r) w |= (uint64_t)(col[(size_t)(base + r) * skv] == 0) << r;
+      }
+      acc = join(acc, runs_of(w, base));
+    }
+  }
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0 || j >= skv) return;
+  for (int k = 1; k < kDenseWaves; ++k) acc = join(acc, part[k][lane]);
+  int32_t uts = 0, ute = 0, lts = sq, lte = sq;
+  if (acc.n == 1) {
+    if (acc.s0 == 0) ute = acc.e0; else { lts = acc.s0; lte = acc.e0; }
+  } else if (acc.n == 2) {
+    uts = acc.s0; ute = acc.e0; lts = acc.s1; lte = acc.e1;
+  } else if (acc.n > 2) {
+    atomicOr(bad, 1);
+  }
+  int32_t* o = iv + m * 4 * (int64_t)skv;
+  o[j] = uts;
+  o[skv + j] = ute;
+  o[2 * (int64_t)skv + j] = lts;
+  o[3 * (int64_t)skv + j] = lte;
+}
+
+__global__ void k_zero_int(int32_t* x) { *x = 0; }
+
 // ------------------------------------------------------------------ bitmap
 __device__ inline uint64_t col_mask(int32_t skv, int bj) {
   int valid = skv - bj * kBlk;
@@ -183,6 +282,11 @@ __device__ uint64_t source_word(const BitmapSrc& s, int m, int bi, int bj, int r
       int64_t c = i - (int64_t)bj * kBlk;
       if (c >= 0 && c < 64) w |= 1ull << c;
     }
+  } else if (s.kind == 2) {
+    // dense bytes of row i, columns 64 bj .. 64 bj + 63 (nonzero = visible)
+    const uint8_t* row = s.dense + ((size_t)m * s.sq + i) * s.skv + (size_t)bj * kBlk;
+    const int valid = min(64, s.skv - bj * kBlk);
+    for (int c = 0; c < valid; ++c) w |= (uint64_t)(row[c] != 0) << c;
   } else {
     int64_t P = s.tree_prefix;
     int64_t base = (int64_t)bj * kBlk;
@@ -357,6 +461,17 @@ hipError_t launch_encode_bitmap(const BitmapSrc& src, const BitmapOut& out, hipS
   hipLaunchKernelGGL(k_exclusive_scan, dim3(1), dim3(1024), 0, s, out.row_count, rows,
                      out.row_offset, out.pool_count);
   hipLaunchKernelGGL(k_bitmap_words, dim3(g4), dim3(256), 0, s, src, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_dense_intervals(const uint8_t* dense, int32_t nmask, int32_t sq, int32_t skv,
+                                         int32_t* iv, int32_t* bad, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero_int, dim3(1), dim3(1), 0, s, bad);
+  const int32_t nstrip = (skv + 63) / 64;
+  const int64_t blocks = (int64_t)nmask * nstrip;
+  if (blocks > 0)
+    hipLaunchKernelGGL(k_dense_intervals, dim3((unsigned)blocks), dim3(1024), 0, s, dense, sq, skv, nstrip,
+                       iv, bad);
   return hipGetLastError();
 }
 

@@ -47,6 +47,8 @@ struct BitmapSrc {
   // tree
   int32_t tree_prefix, tree_n;
   const int32_t* parent;
+  // dense (kind 2): uint8 [nmask][sq][skv], nonzero = visible
+  const uint8_t* dense;
 };
 
 struct BitmapOut {
@@ -60,6 +62,10 @@ struct BitmapOut {
 };
 
 hipError_t launch_encode_bitmap(const BitmapSrc& src, const BitmapOut& out, hipStream_t s);
+// Dense uint8 masks -> canonical intervals; *bad (zeroed here) becomes nonzero
+// if some column has more than two masked runs.
+hipError_t launch_encode_dense_intervals(const uint8_t* dense, int32_t nmask, int32_t sq, int32_t skv,
+                                         int32_t* iv, int32_t* bad, hipStream_t s);
 
 hipError_t launch_encode_selected(const int32_t* sel, int32_t nb, int32_t sq, int32_t n,
                                   int32_t nblk, int32_t* list, int32_t* count, hipStream_t s);

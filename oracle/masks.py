@@ -46,11 +46,14 @@ varlen                packed batch of segments (cumulative query lengths cu_q,
                       <= rr + next (rr = ii + off), "prefix" jj < prefix_s or
                       jj <= ii + off.  Ascend sparseMode page (actual_seq_qlen /
                       actual_seq_kvlen, modes 2, 3, 4, 5, 7, 8).
+dense                 the mask element by element, dense [B][H][Sq][Skv], nonzero =
+                      visible (Ascend sparseMode 1 "allMask"; Binary Block Masking's
+                      full mask).
 
 Spec keys: sq, skv and, per family, cu_seg (cumulative boundaries, first 0, last
 Sq), pre, next, tree_prefix, tree_parent, blk_state [B][H][nbq][nbk],
 blk_index (same shape), blk_bits [pool][64] (uint64), force_diag, sel [B][Sq][n],
-sel_cells, raw_intervals [B][H][4][Skv], cu_q, cu_k, seg_mode, seg_prefix.
+sel_cells, raw_intervals [B][H][4][Skv], cu_q, cu_k, seg_mode, seg_prefix, dense.
 """
 
 import numpy as np
@@ -147,6 +150,9 @@ def dense_vis(spec, b=0, h=0, rows=None):
         rr = np.broadcast_to(np.arange(lists.shape[0])[:, None], lists.shape)
         blockvis[rr[valid], lists[valid]] = True
         return blockvis[:, c[0] // cells]
+    if fam == "dense":
+        # the mask given element by element (nonzero = visible)
+        return np.asarray(spec["dense"])[bm, hm][r[:, 0]] != 0
     if fam == "varlen":
         # Packed variable-length batch (Ascend sparseMode page, actual_seq_qlen /
         # actual_seq_kvlen): row i of query segment s sees only the key columns

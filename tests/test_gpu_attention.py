@@ -209,3 +209,22 @@ def test_deterministic():
     o2, l2 = _run(w, arrays)
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(l1, l2)
+
+
+def test_dense_mask_input_both_forms():
+    """Attention over masks handed over element by element: an interval-shaped
+    mask (interval form) and a random one (bitmap form), per (batch, head)."""
+    rng = np.random.default_rng(41)
+    S, K = 300, 270
+    w = _small("bf16", 128, S, K, B=2, Hq=2, Hkv=2)
+    band = np.asarray(OM.dense_vis(dict(family="band", sq=S, skv=K, pre=50, next=3)))
+    vis = np.zeros((2, 2, S, K), dtype=np.uint8)
+    vis[0, 0] = band
+    vis[0, 1] = np.asarray(OM.dense_vis(dict(family="causal_bottom_right", sq=S, skv=K)))
+    vis[1, 0] = band
+    vis[1, 1] = vis[1, 0]
+    spec = dict(family="dense", sq=S, skv=K, batch=2, heads=2, dense=vis)
+    _dense_check(w, spec, "dense (interval form)")
+    vis2 = (rng.random((2, 2, S, K)) < 0.2).astype(np.uint8)
+    spec2 = dict(family="dense", sq=S, skv=K, batch=2, heads=2, dense=vis2)
+    _dense_check(w, spec2, "dense (bitmap form)")

@@ -117,3 +117,32 @@ def test_unsupported_combinations_are_refused():
     with pytest.raises(fm.FmaskError) as ei:
         fm.attn_bwd(q, k, v, o, lse, torch.zeros_like(o), enc, t64)
     assert ei.value.status == fm.ERR_UNSUPPORTED
+
+
+def test_workspace_reuse_and_size_check():
+    """A caller's workspace is checked against fmask_attn_bwd_workspace_bytes and
+    fully rewritten by each call: one buffer serves a larger then a smaller
+    problem (with different masks) and gives the same gradients as a fresh one."""
+    big = _small(128, 461, 461, seed=23)
+    small = _small(128, 200, 333, seed=24)
+    runs = []
+    for w, spec in ((big, dict(family="causal", sq=461, skv=461)),
+                    (small, dict(family="band", sq=200, skv=333, pre=30, next=2))):
+        q, k, v = to_device(w, synth.draw_qkv(w))
+        do = torch.from_numpy(synth.draw_dout(w).view(np.int16)).view(torch.bfloat16).cuda()
+        enc = fm.encode(spec)
+        tiles = fm.classify(enc, 128, 64)
+        o, lse = fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"])
+        runs.append((q, k, v, o, lse, do, enc, tiles, w["scale"]))
+    nbytes = [fm.attn_bwd_workspace_bytes(r[0], r[1], r[2], r[3], r[7]) for r in runs]
+    assert nbytes[0] > nbytes[1] > 0
+    ws = torch.full((nbytes[0],), 0x7f, dtype=torch.uint8, device="cuda")
+    for (q, k, v, o, lse, do, enc, tiles, scale) in runs:
+        ref = fm.attn_bwd(q, k, v, o, lse, do, enc, tiles, scale=scale)
+        got = fm.attn_bwd(q, k, v, o, lse, do, enc, tiles, scale=scale, workspace=ws)
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b)
+    q, k, v, o, lse, do, enc, tiles, scale = runs[0]
+    with pytest.raises(fm.FmaskError) as ei:
+        fm.attn_bwd(q, k, v, o, lse, do, enc, tiles, scale=scale, workspace=ws[: nbytes[0] - 16])
+    assert ei.value.status == fm.ERR_CAPACITY

@@ -209,8 +209,6 @@ def test_full_size_tables(name):
     bm, bn = fm.preferred_tile(w["dtype"], w["D"], enc.kind)
     t = fm.classify(enc, bm, bn)
     st, ls, cn, od = [x.cpu().numpy() for x in t.arrays()]
-    col_ls, col_cn, col_od = [x.cpu().numpy() for x in t.columns()]
-    allcc = []
     S = w["Sq"]
     rng = np.random.default_rng(0)
     nb = spec.get("batch", 1)
@@ -232,12 +230,95 @@ def test_full_size_tables(name):
         np.testing.assert_array_equal(ls[b, 0], el)
         np.testing.assert_array_equal(cn[b, 0], ec)
         allc.append(ec)
-        # the same table by key-tile column
-        cl, cc = OE.tile_lists(exp_st.T)
-        np.testing.assert_array_equal(col_ls[b, 0], cl)
-        np.testing.assert_array_equal(col_cn[b, 0], cc)
-        allcc.append(cc)
     np.testing.assert_array_equal(od, OE.tile_order(np.concatenate(allc)))
-    np.testing.assert_array_equal(col_od, OE.tile_order(np.concatenate(allcc)))
     if enc.kind == fm.ENC_INTERVALS:
         np.testing.assert_array_equal(got_iv, OE.intervals_from_dense(colvis))
+
+
+def _dense_spec(vis, form):
+    vis = np.asarray(vis, dtype=np.uint8)
+    B, H, S, K = vis.shape
+    return dict(family="dense", sq=S, skv=K, batch=B, heads=H, dense=vis, dense_form=form)
+
+
+def test_dense_masks_take_the_interval_form_when_they_can():
+    """Dense input of interval-representable masks: the automatic and the interval
+    forms both give the canonical intervals of the oracle; the bitmap form gives
+    the canonical bitmap."""
+    rng = np.random.default_rng(77)
+    S, K = 333, 290
+    fams = [dict(family="causal_bottom_right", sq=S, skv=K), dict(family="band", sq=S, skv=K, pre=40, next=-5)]
+    vis = np.stack([np.stack([np.asarray(OM.dense_vis(f)) for f in fams])])  # [1][2][S][K]
+    vis[0, 1, :, 7] = False  # a column with no visible row
+    for form in (None, "intervals"):
+        spec = _dense_spec(vis, form)
+        enc = fm.encode(spec)
+        assert enc.kind == fm.ENC_INTERVALS
+        got = enc.intervals().cpu().numpy()
+        for h in range(2):
+            np.testing.assert_array_equal(got[0, h], OE.intervals_from_dense(vis[0, h]))
+    spec = _dense_spec(vis, "bitmap")
+    enc = fm.encode(spec)
+    assert enc.kind == fm.ENC_BITMAP
+    _check_bitmap(enc, spec, 1, 2)
+
+
+def _runs_column(rng, S, cuts):
+    """A column of S rows with 0, 1 or 2 masked runs whose ends are drawn from
+    `cuts` (row indices that fall on the encoder's chunk edges) or at random."""
+    col = np.ones(S, dtype=bool)
+    n = rng.integers(0, 3)
+    pts = sorted(rng.choice(np.concatenate([cuts, rng.integers(0, S + 1, 8)]), 2 * n, replace=False))
+    for a, b in zip(pts[0::2], pts[1::2]):
+        col[a:b] = False
+    return col
+
+
+def test_dense_runs_across_row_chunks():
+    """Masked runs that start, end or meet on 64-row chunk edges and on the
+    edges of the encoder's per-wave row shares, at a ragged size: canonical
+    intervals bit-exact; a third run far from the other two sends the automatic
+    form to the bitmap and makes the interval form fail."""
+    rng = np.random.default_rng(79)
+    S, K = 2500, 300
+    cuts = np.array([0, 63, 64, 65, 128, 191, 192, 193, 384, 1152, 2496, 2499, 2500])
+    vis = np.stack([_runs_column(rng, S, cuts) for _ in range(K)], axis=1)[None, None]
+    vis[0, 0, :, 5] = True
+    vis[0, 0, :, 6] = False
+    vis[0, 0, 192:384, 7] = False  # one run that fills exactly one wave's share
+    spec = _dense_spec(vis, None)
+    enc = fm.encode(spec)
+    assert enc.kind == fm.ENC_INTERVALS
+    np.testing.assert_array_equal(enc.intervals().cpu().numpy()[0, 0], OE.intervals_from_dense(vis[0, 0]))
+    vis[0, 0, :, 9] = True
+    vis[0, 0, 10:20, 9] = False
+    vis[0, 0, 500:700, 9] = False
+    vis[0, 0, 2400:2500, 9] = False
+    enc = fm.encode(_dense_spec(vis, None))
+    assert enc.kind == fm.ENC_BITMAP
+    _check_bitmap(enc, _dense_spec(vis, None), 1, 1)
+    with pytest.raises(fm.FmaskError) as ei:
+        fm.encode(_dense_spec(vis, "intervals"))
+    assert ei.value.status == fm.ERR_INVALID
+
+
+def test_dense_masks_fall_back_to_the_bitmap_form():
+    rng = np.random.default_rng(78)
+    S, K = 300, 260
+    tree = dict(family="tree", sq=S, skv=S, tree_prefix=S - 64, tree_parent=synth.random_tree(rng, 64, order="bfs"))
+    rand = rng.random((S, K)) < 0.3
+    vis = np.zeros((2, 1, S, K), dtype=bool)
+    vis[0, 0] = np.asarray(OM.dense_vis(tree))[:, :K]
+    vis[1, 0] = rand
+    spec = _dense_spec(vis, None)
+    enc = fm.encode(spec)
+    assert enc.kind == fm.ENC_BITMAP
+    _check_bitmap(enc, spec, 2, 1)
+    with pytest.raises(fm.FmaskError) as ei:
+        fm.encode(_dense_spec(vis, "intervals"))
+    assert ei.value.status == fm.ERR_INVALID
+    # tables at the bitmap tile
+    t = fm.classify(enc, 64, 64)
+    st = t.arrays()[0].cpu().numpy()
+    for b in range(2):
+        np.testing.assert_array_equal(st[b, 0], OE.tile_states(vis[b, 0], 64, 64))

@@ -67,8 +67,16 @@ __device__ inline int vswz(int key) {
   return KCH == 16 ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
 }
 
-__device__ inline int overlap(int a0, int a1, int b0, int b1) {
-  return max(0, min(a1, b1) - max(a0, b0));
+// max / sum of x over lanes l and l ^ 32.  v_permlane32_swap of x with itself
+// leaves {x[l], x[l ^ 32]} in some order in the two results (no LDS round
+// trip, unlike a lane shuffle).
+__device__ inline float pair_max(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
 struct Item {
@@ -174,12 +182,12 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
 
   const int tg = lane >> 4, tr = (lane >> 2) & 3, tc4 = lane & 3;
   const int vrow_l = 4 * (tg >> 1) + tr;
-  int vofs[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    const int ch = 4 * db + 2 * (tg & 1) + (tc4 >> 1);
-    vofs[db] = vrow_l * (D * 2) + ((ch ^ vswz<G::KCH>(vrow_l)) * 16) + (tc4 & 1) * 8;
-  }
+  // V^T fragment (db, ks): chunk 4 db + x of row vrow_l + 16 ks, i.e. the
+  // db = 0 offset with 64 db XORed into the swizzled chunk bits.  K fragment
+  // (kh, t): chunk 2 t + half of key kh * 32 + l32, i.e. the t = 0 offset with
+  // 32 t XORed in (the swizzle only touches the chunk bits).
+  const int vofs0 = vrow_l * (D * 2) + (((2 * (tg & 1) + (tc4 >> 1)) ^ vswz<G::KCH>(vrow_l)) * 16) + (tc4 & 1) * 8;
+  const int kofs0 = l32 * (D * 2) + ((half ^ kswz<G::KCH>(l32)) * 16);
 
   // K tile kt and its raw intervals (wave w loads field w): LOADS + 1 loads.
   auto issue_k = [&](int kt, int buf) INLINE {
@@ -209,7 +217,11 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
       issue_v(kt);
       if (more) issue_k(e_next & 0x7fffffff, b ^ 1);
 
-      const char* kb = smem + G::K0 + b * G::TILE;
+      // (laundered so that the XORed offsets are formed where they are used
+      // rather than held in registers across the loop)
+      int kofs = kofs0 + b * G::TILE, vofs = vofs0;
+      asm volatile("" : "+v"(kofs), "+v"(vofs));
+      const char* kb = smem + G::K0;
       const char* vb = smem + G::V0;
       const int32_t* raw = (const int32_t*)(smem + G::IV0 + b * G::IVB);
       const bool ragged = (kt + 1) * BN > p.skv;
@@ -241,11 +253,9 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
           s[kh] = f32x16{};
-          const int key = kh * 32 + l32;
 #pragma unroll
           for (int t = 0; t < KT; ++t) {
-            const int ch = 2 * t + half;
-            bf16x8 a = *(const bf16x8*)(kb + key * (D * 2) + ((ch ^ kswz<G::KCH>(key)) * 16));
+            bf16x8 a = *(const bf16x8*)(kb + (kofs ^ (32 * t)) + kh * 32 * (D * 2));
             s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kh], 0, 0, 0);
           }
         }
@@ -268,11 +278,19 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
             }
           }
         }
-        // Online softmax (the other 32 keys of the row sit in lane ^ 32).
-        float mloc = fmaxf(s[0][0], s[1][0]);
+        // Online softmax (the other 32 keys of the row sit in lane ^ 32).  The
+        // row maximum uses the IEEE maximum (three operands per instruction, no
+        // canonicalisation of the MFMA results; masked scores are -inf, never
+        // NaN), over the first key half first, whose MFMAs finished earlier.
+        float m0 = __builtin_elementwise_maximum(s[0][0], s[0][1]);
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, fmaxf(s[0][r], s[1][r]));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        for (int r = 2; r < 16; r += 2)
+          m0 = __builtin_elementwise_maximum(m0, __builtin_elementwise_maximum(s[0][r], s[0][r + 1]));
+        float mloc = m0;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2)
+          mloc = __builtin_elementwise_maximum(mloc, __builtin_elementwise_maximum(s[1][r], s[1][r + 1]));
+        mloc = pair_max(mloc);
         const float m_cand = fmaxf(m_run, mloc);
         const bool grow = (m_cand - m_run) * c > 8.f;
         if (__any(grow)) {
@@ -312,7 +330,7 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
         for (int db = 0; db < DB; ++db) {
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
-            const char* a0 = vb + vofs[db] + (16 * ks) * (D * 2);
+            const char* a0 = vb + (vofs ^ (64 * db)) + (16 * ks) * (D * 2);
             bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)a0);
             bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(a0 + 8 * (D * 2)));
             bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -336,7 +354,7 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
   }
 
   // Epilogue: O = O / l, zero rows for l = 0, LSE in natural log.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < p.sq) {
     __bf16* O = (__bf16*)p.o + it.b * p.os[0] + it.h * p.os[1] + qrow * p.os[2];

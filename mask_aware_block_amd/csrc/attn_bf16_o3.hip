@@ -43,7 +43,7 @@ constexpr int NT = 64 * NW;
 constexpr int BM = 32 * NW;
 constexpr int kList = 256;  // tile-list entries staged in LDS
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kQkAhead = 4;  // K fragments read ahead of their MFMA
+constexpr int kQkAhead = 3;  // K fragments read ahead of their MFMA
 constexpr int kPvAhead = 3;  // V^T fragments read ahead of their MFMA
 
 template <int D>
@@ -249,25 +249,29 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
 
       bf16x8 pf[4];
       if (!skip) {
+        // S^T = K Q^T for the two 32-key halves: 2 D / 16 MFMAs, each K
+        // fragment read kQkAhead MFMAs ahead into a ring of registers
+        // (sched_barrier keeps the scheduler from sinking the reads back next
+        // to their MFMAs).
         f32x16 s[2];
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+        {
+          bf16x8 fr[kQkAhead];
+          auto kread = [&](int n) INLINE -> bf16x8 {
+            return *(const bf16x8*)(kb + (kofs ^ (32 * (n % KT))) + (n / KT) * 32 * (D * 2));
+          };
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          s[kh] = f32x16{};
+          for (int n = 0; n < kQkAhead; ++n) fr[n] = kread(n);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int t = 0; t < KT; ++t) {
-            bf16x8 a = *(const bf16x8*)(kb + (kofs ^ (32 * t)) + kh * 32 * (D * 2));
-            s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kh], 0, 0, 0);
+          for (int n = 0; n < 2 * KT; ++n) {
+            const bf16x8 a = fr[n % kQkAhead];
+            s[n / KT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[n % KT], s[n / KT], 0, 0, 0);
+            if (n + kQkAhead < 2 * KT) fr[n % kQkAhead] = kread(n + kQkAhead);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
-        // Keep kQkAhead K reads in flight ahead of the MFMAs that consume them
-        // (sched_group_barrier masks: 0x8 MFMA, 0x100 LDS read).
-        __builtin_amdgcn_sched_group_barrier(0x100, kQkAhead, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * KT - kQkAhead; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, kQkAhead, 0);
         if (need_mask) {
 #pragma unroll
           for (int kh = 0; kh < 2; ++kh) {

@@ -273,8 +273,8 @@ fmask_status fmask_classify(const fmask_encoded *enc, int32_t bm, int32_t bn, vo
  * without per-element masking, PARTIAL tiles are masked element by element.
  * tiles must come from fmask_classify on the same encoding (NULL for the
  * SELECTED kind, whose kernel walks the lists directly).  Tile shapes with a
- * kernel: BF16 INTERVALS 128x64 (preferred), 256x64, 64x64; BF16 BITMAP 64x64
- * (preferred), 128x64; F32 64x64.  Other shapes return FMASK_ERR_UNSUPPORTED.
+ * kernel: BF16 INTERVALS 128x64 (preferred), 256x64, 64x64; BF16 BITMAP 128x64
+ * (preferred), 64x64; F32 64x64.  Other shapes return FMASK_ERR_UNSUPPORTED.
  * Supported: BF16 with d in {64, 128} on INTERVALS / BITMAP; F32 with d in
  * {64, 128} on INTERVALS / BITMAP; BF16 with d in {128, 256}, sel_cells == 32
  * and hq / hkv in {1, 2, 4, 8, 12, 16} on SELECTED.                             */

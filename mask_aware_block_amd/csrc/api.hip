@@ -257,7 +257,7 @@ TileLayout tile_layout(const fmask_encoded* e, int32_t bm, int32_t bn) {
 }
 
 // Tile shapes with a kernel: bf16 intervals 256x64, 128x64 and 64x64; bf16
-// bitmap 64x64 and 128x64; fp32 64x64.
+// bitmap 128x64 and 64x64; fp32 64x64.
 bool tile_supported(int32_t dtype, int32_t kind, int32_t bm, int32_t bn) {
   if (bn != 64) return false;
   if (dtype == FMASK_F32) return bm == 64;
@@ -269,7 +269,7 @@ void preferred(int32_t dtype, int32_t d, int32_t kind, int32_t* bm, int32_t* bn)
   (void)d;
   *bn = 64;
   if (dtype == FMASK_F32) *bm = 64;
-  else *bm = (kind == FMASK_ENC_BITMAP) ? 64 : 128;
+  else *bm = 128;
 }
 
 }  // namespace
@@ -616,12 +616,13 @@ fmask_status fmask_attn_fwd(const fmask_attn_args* a, const void* q, const void*
   p.n_items = (int32_t)items;
   p.kind = enc->kind;
   p.iv = enc->intervals;
-  p.bstate = enc->blk_state; p.bindex = enc->blk_index; p.bbits = enc->blk_bits;
+  p.bstate = enc->blk_state; p.bindex = enc->blk_index; p.bbits = enc->blk_bits; p.pool_cap = enc->pool_cap;
   p.nbq = (int32_t)enc->nbq; p.nbk = (int32_t)enc->nbk;
   if (a->sq == 0) return FMASK_OK;
   hipError_t e;
   if (a->dtype == FMASK_F32) e = launch_attn_tile_f32(p, a->d, s);
-  else if (bm == 128 && enc->kind == FMASK_ENC_INTERVALS) e = launch_attn_o3_bf16(p, a->d, s);
+  else if (bm == 128 && (enc->kind == FMASK_ENC_INTERVALS || (enc->kind == FMASK_ENC_BITMAP && enc->pool_cap <= ((int64_t)1 << 22))))
+    e = launch_attn_o3_bf16(p, a->d, s);
   else e = launch_attn_tile_bf16(p, a->d, s);
   return hip_status(e, "attention kernel");
 }

@@ -1,6 +1,6 @@
 // Masked attention forward, bf16 inputs, fp32 accumulation, gfx950 MFMA:
-// 128-row query tiles of four 32-row waves, interval encoding, three
-// workgroups per CU (three waves per SIMD).
+// 128-row query tiles of four 32-row waves, interval or 64 x 64 bitmap
+// encoding, three workgroups per CU (three waves per SIMD).
 //
 // Same arithmetic and register layout as the 128-row kernel of
 // attn_bf16.hip (S^T = K Q^T per wave with one query row per lane, online
@@ -9,8 +9,11 @@
 // double-buffered V for occupancy.  LDS per workgroup is 52 KB:
 //   K tiles     2 x 16 KB   tile i + 1 streams in while tile i is computed
 //   V tile      1 x 16 KB   V(i) streams in behind QK(i) and the softmax
-//   intervals   2 x  1 KB   raw [4][64] int32, one field per wave
-//   row masks   4 x 256 B   per wave, for PARTIAL tiles
+//   mask data   2 x  1 KB   intervals: raw [4][64] int32, one field per wave;
+//                           bitmap: each wave's 32 row words of its block
+//   per-wave    1 KB        intervals: row masks of PARTIAL tiles;
+//                           bitmap: both 64-row blocks of the first 128 list
+//                           entries (pool index, or FULL / SKIP)
 //   tile list       1 KB
 // so three workgroups (12 waves) share a CU, and the MFMA work of one wave
 // overlaps the VALU work and load waits of the others.  Per tile:
@@ -42,6 +45,7 @@ constexpr int NW = 4;
 constexpr int NT = 64 * NW;
 constexpr int BM = 32 * NW;
 constexpr int kList = 256;  // tile-list entries staged in LDS
+constexpr int kBinfo = 128;  // bitmap: list entries whose block info is staged in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kQkAhead = 3;  // K fragments read ahead of their MFMA
 constexpr int kPvAhead = 3;  // V^T fragments read ahead of their MFMA
@@ -54,8 +58,9 @@ struct Geo {
   static constexpr int V0 = 2 * TILE;        // V buffer
   static constexpr int IV0 = 3 * TILE;       // raw interval buffers 0, 1: [4][BN] int32
   static constexpr int IVB = 4 * BN * 4;
-  static constexpr int RM0 = IV0 + 2 * IVB;  // per-wave row masks: [NW][BN] uint32
+  static constexpr int RM0 = IV0 + 2 * IVB;  // row masks [NW][BN] uint32, or block info [2][kBinfo] int32
   static constexpr int END = RM0 + NW * BN * 4;
+  static_assert(2 * kBinfo <= NW * BN, "block info fits the row-mask region");
   static constexpr int LOADS = BN * KCH / NT;
   static_assert(BN * KCH % NT == 0, "tile must split evenly over the workgroup");
 };
@@ -107,7 +112,11 @@ __device__ inline int logical_item(int gsz) {
   return ((k / gsz) * kXcds + xcd) * gsz + (k % gsz);
 }
 
-template <int D>
+// Block info of a 64 x 64 bitmap block: its pool index if PARTIAL, else
+// kBlkFull or kBlkSkip.
+constexpr int kBlkFull = -1, kBlkSkip = -2;
+
+template <int D, int KIND>
 __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using G = Geo<D>;
@@ -134,9 +143,33 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
   const int32_t* ivcol = p.iv + ((size_t)it.mb * p.mh + it.mh) * 4 * (size_t)p.skv;
 
   for (int i = tid; i < G::END / 16; i += NT) ((i32x4*)smem)[i] = i32x4{0, 0, 0, 0};
+  if (KIND == FMASK_ENC_BITMAP) __syncthreads();  // the block info below shares the cleared region
   for (int i = tid; i < min(cnt, kList); i += NT) lst[i] = list[i];
   auto entry = [&](int i) INLINE -> int {
     return i < kList ? __builtin_amdgcn_readfirstlane(lst[i]) : sload_wait(list + i);
+  };
+  // Bitmap: the two 64-row blocks (block rows 2 qt and 2 qt + 1) of list entry
+  // e; waves 0, 1 use the first, waves 2, 3 the second.
+  const size_t bbase = ((size_t)it.mb * p.mh + it.mh) * p.nbq;
+  auto block_info = [&](int e, int half_row) INLINE -> int {
+    const int bi = 2 * it.qt + half_row, kt = e & 0x7fffffff;
+    if (bi >= p.nbq) return kBlkSkip;
+    const size_t bx = (bbase + bi) * p.nbk + kt;
+    const int st = p.bstate[bx];
+    return st == FMASK_PARTIAL ? p.bindex[bx] : (st == FMASK_FULL ? kBlkFull : kBlkSkip);
+  };
+  int32_t* binfo = (int32_t*)(smem + G::RM0);  // [2][kBinfo]
+  if (KIND == FMASK_ENC_BITMAP) {
+    for (int i = tid; i < min(cnt, kBinfo); i += NT) {
+      const int e = list[i];
+      binfo[i] = block_info(e, 0);
+      binfo[kBinfo + i] = block_info(e, 1);
+    }
+  }
+  // This wave's block of list entry i (entry value e).
+  auto wave_block = [&](int i, int e) INLINE -> int {
+    if (i < kBinfo) return __builtin_amdgcn_readfirstlane(binfo[(w >> 1) * kBinfo + i]);
+    return __builtin_amdgcn_readfirstlane(block_info(e, w >> 1));
   };
 
   bf16x8 qf[KT];
@@ -155,7 +188,8 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
 
   const rsrc_t krs = make_rsrc(K, ((int64_t)(p.skv - 1) * ks2 + D) * 2);
   const rsrc_t vrs = make_rsrc(V, ((int64_t)(p.skv - 1) * vs2 + D) * 2);
-  const rsrc_t irs = make_rsrc(ivcol, (int64_t)4 * p.skv * 4);
+  const rsrc_t irs = KIND == FMASK_ENC_BITMAP ? make_rsrc(p.bbits, p.pool_cap * kBlk * 8)
+                                              : make_rsrc(ivcol, (int64_t)4 * p.skv * 4);
   // Direct-to-LDS loads: instruction n of wave w fills LDS chunks
   // P = (w * LOADS + n) * 64 + lane, i.e. row P / KCH, physical chunk P % KCH
   // holding logical chunk (P % KCH) ^ swizzle(row).
@@ -189,12 +223,22 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
   const int vofs0 = vrow_l * (D * 2) + (((2 * (tg & 1) + (tc4 >> 1)) ^ vswz<G::KCH>(vrow_l)) * 16) + (tc4 & 1) * 8;
   const int kofs0 = l32 * (D * 2) + ((half ^ kswz<G::KCH>(l32)) * 16);
 
-  // K tile kt and its raw intervals (wave w loads field w): LOADS + 1 loads.
-  auto issue_k = [&](int kt, int buf) INLINE {
+  // K tile kt (list entry i, value e) and its mask data: LOADS + 1 loads.
+  // Intervals: wave w loads field w.  Bitmap: wave w loads the 32 words of its
+  // rows when its block is PARTIAL, else a load past the pool's range (zeros)
+  // so that every wave always issues the same number of loads.
+  auto issue_k = [&](int i, int e, int buf) INLINE {
+    const int kt = e & 0x7fffffff;
     const int base = lds_w + G::K0 + buf * G::TILE, g0 = kt * kstep;
 #pragma unroll
     for (int n = 0; n < G::LOADS; ++n) dma16(krs, kgo[n] + g0, base + n * 1024);
-    dma4(irs, (w * p.skv + kt * BN + lane) * 4, lds_iv + buf * G::IVB);
+    if (KIND == FMASK_ENC_BITMAP) {
+      const int info = wave_block(i, e);
+      const int off = info >= 0 ? info * (kBlk * 8) + (w & 1) * 256 + lane * 4 : 0x7ffffff0;
+      dma4(irs, off, lds_iv + buf * G::IVB);
+    } else {
+      dma4(irs, (w * p.skv + kt * BN + lane) * 4, lds_iv + buf * G::IVB);
+    }
   };
   // V tile kt: LOADS loads.
   auto issue_v = [&](int kt) INLINE {
@@ -206,7 +250,7 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
   __syncthreads();  // LDS cleared and the list staged before any tile load lands
   if (cnt > 0) {
     int e_cur = entry(0);
-    issue_k(e_cur & 0x7fffffff, 0);
+    issue_k(0, e_cur, 0);
     wait_all();
     barrier();
     for (int i = 0; i < cnt; ++i) {
@@ -215,7 +259,7 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
       const int kt = e_cur & 0x7fffffff;
       const int e_next = more ? entry(i + 1) : 0;
       issue_v(kt);
-      if (more) issue_k(e_next & 0x7fffffff, b ^ 1);
+      if (more) issue_k(i + 1, e_next, b ^ 1);
 
       // (laundered so that the XORed offsets are formed where they are used
       // rather than held in registers across the loop)
@@ -228,7 +272,14 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
       bool need_mask = !(e_cur & (int)FMASK_LIST_FULL_BIT) || ragged;
       bool skip = false;
       uint32_t* rmask = (uint32_t*)(smem + G::RM0) + w * BN;
-      if (need_mask) {
+      uint64_t word = ~0ull;  // bitmap: this lane's row word (bit = visible key)
+      if (KIND == FMASK_ENC_BITMAP) {
+        const int info = wave_block(i, e_cur);
+        skip = info == kBlkSkip || r0 >= p.sq;
+        need_mask = info >= 0 || ragged;
+        if (info >= 0) word = *(const uint64_t*)(smem + G::IV0 + b * G::IVB + w * 256 + l32 * 8);
+        if (ragged) word &= (1ull << (p.skv - kt * BN)) - 1ull;
+      } else if (need_mask) {
         // This wave's 32-bit row mask of each key column (lane = key; bit r set
         // iff row r0 + r is masked; keys past skv are masked for every row),
         // and from it the wave's state for the tile.
@@ -273,12 +324,20 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
           }
         }
         if (need_mask) {
+          // bitmap: this lane's keys 8 (r / 4) + 4 half + r % 4 of each half,
+          // shifted so that the bit positions are constants
+          const uint64_t wl = word >> (4 * half);
 #pragma unroll
           for (int kh = 0; kh < 2; ++kh) {
+            const uint32_t wk = (uint32_t)(wl >> (32 * kh));
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int kl = kh * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-              if ((rmask[kl] >> l32) & 1u) s[kh][r] = -INFINITY;
+              if (KIND == FMASK_ENC_BITMAP) {
+                if (!((wk >> (8 * (r >> 2) + (r & 3))) & 1u)) s[kh][r] = -INFINITY;
+              } else {
+                if ((rmask[kl] >> l32) & 1u) s[kh][r] = -INFINITY;
+              }
             }
           }
         }
@@ -379,22 +438,28 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
 #endif
 }
 
-template <int D>
+template <int D, int KIND>
 hipError_t launch_d(const TileAttnParams& p, hipStream_t s) {
   const int gsz = (p.mh == 1) ? p.group : 1;
   if (p.n_items <= 0) return hipSuccess;
   const int64_t unit = (int64_t)kXcds * gsz;
   const int64_t npad = (p.n_items + unit - 1) / unit * unit;
-  hipLaunchKernelGGL((k_attn_o3<D>), dim3((unsigned)npad), dim3(NT), 0, s, p, gsz);
+  hipLaunchKernelGGL((k_attn_o3<D, KIND>), dim3((unsigned)npad), dim3(NT), 0, s, p, gsz);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_o3_bf16(const TileAttnParams& p, int32_t d, hipStream_t s) {
-  if (p.bn != BN || p.bm != BM || p.kind != FMASK_ENC_INTERVALS) return hipErrorInvalidValue;
-  if (d == 128) return launch_d<128>(p, s);
-  if (d == 64) return launch_d<64>(p, s);
+  if (p.bn != BN || p.bm != BM) return hipErrorInvalidValue;
+  if (p.kind == FMASK_ENC_INTERVALS) {
+    if (d == 128) return launch_d<128, FMASK_ENC_INTERVALS>(p, s);
+    if (d == 64) return launch_d<64, FMASK_ENC_INTERVALS>(p, s);
+  } else if (p.kind == FMASK_ENC_BITMAP) {
+    if (p.pool_cap > ((int64_t)1 << 22)) return hipErrorInvalidValue;  // 32-bit buffer offsets
+    if (d == 128) return launch_d<128, FMASK_ENC_BITMAP>(p, s);
+    if (d == 64) return launch_d<64, FMASK_ENC_BITMAP>(p, s);
+  }
   return hipErrorInvalidValue;
 }
 

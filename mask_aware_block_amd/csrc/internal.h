@@ -108,6 +108,7 @@ struct TileAttnParams {
   const uint8_t* bstate;
   const int32_t* bindex;
   const uint64_t* bbits;
+  int64_t pool_cap;    // entries of bbits
   int32_t nbq, nbk;
 };
 

@@ -67,7 +67,7 @@ def test_status_strings_and_preferred_tiles():
     for s in (fm.OK, fm.ERR_INVALID, fm.ERR_UNSUPPORTED, fm.ERR_CAPACITY, fm.ERR_HIP):
         assert L.fmask_status_str(s)
     assert fm.preferred_tile("bf16", 128, fm.ENC_INTERVALS) == (128, 64)
-    assert fm.preferred_tile("bf16", 128, fm.ENC_BITMAP) == (64, 64)
+    assert fm.preferred_tile("bf16", 128, fm.ENC_BITMAP) == (128, 64)
     assert fm.preferred_tile("f32", 64, fm.ENC_INTERVALS) == (64, 64)
     bm, bn = ctypes.c_int32(), ctypes.c_int32()
     assert L.fmask_preferred_tile(1, 96, fm.ENC_INTERVALS, ctypes.byref(bm), ctypes.byref(bn)) == fm.ERR_UNSUPPORTED

@@ -131,6 +131,65 @@ def test_interval_tile_shapes(bm):
         compare(w, o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"bm {bm} {spec['family']}")
 
 
+@pytest.mark.parametrize("bm", [128, 64])
+@pytest.mark.parametrize("D", [128, 64])
+def test_bitmap_tile_shapes(bm, D):
+    """Bitmap masks at the 64- and 128-row tiles (the 128-row kernel reads each
+    wave's own 64 x 64 block: FULL, SKIP or PARTIAL words): random block
+    patterns per batch on a ragged shape with GQA, and a BFS-numbered tree."""
+    S, K = 330, 390
+    w = _small("bf16", D, S, K, B=2, Hq=4, Hkv=2, seed=12)
+    rng = np.random.default_rng(5)
+    nbq, nbk = -(-S // 64), -(-K // 64)
+    sts, ixs, pools, off = [], [], [], 0
+    for _ in range(2):
+        st, ix, bits = synth.block_pattern(rng, nbq, nbk, 0.3, 0.3)
+        sts.append(st)
+        ixs.append(np.where(ix >= 0, ix + off, -1))
+        pools.append(bits)
+        off += bits.shape[0]
+    spec = dict(family="block_bitmap", sq=S, skv=K, batch=2, heads=1,
+                blk_state=np.stack(sts)[:, None], blk_index=np.stack(ixs)[:, None].astype(np.int32),
+                blk_bits=np.concatenate(pools).reshape(-1, 64), force_diag=False)
+    tree = dict(family="tree", sq=S, skv=S, tree_prefix=S - 64,
+                tree_parent=synth.random_tree(rng, 64, order="bfs"))
+    for sp, what in ((spec, "block bitmap"), (tree, "tree")):
+        ww = dict(w, Skv=sp["skv"])
+        arrays = synth.draw_qkv(ww)
+        q, k, v = to_device(ww, arrays)
+        enc = fm.encode(sp)
+        assert enc.kind == fm.ENC_BITMAP
+        tiles = fm.classify(enc, bm, 64)
+        o, lse = fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"])
+        torch.cuda.synchronize()
+        qq, kk, vv = (to_f64(ww, a) for a in arrays)
+        ro, rl = OA.attention_dense(qq, kk, vv, OA.spec_vis_fn(sp), w["scale"])
+        compare(ww, o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"{what} bm {bm} d{D}")
+
+
+def test_bitmap_long_tile_rows():
+    """More than 256 non-SKIP tiles in a row (past the kernel's LDS list stage):
+    a 16K+ key range of mostly FULL and some PARTIAL blocks."""
+    S, K = 150, 16384 + 1000
+    w = _small("bf16", 64, S, K, B=1, Hq=2, Hkv=1, seed=13)
+    rng = np.random.default_rng(6)
+    nbq, nbk = -(-S // 64), -(-K // 64)
+    st, ix, bits = synth.block_pattern(rng, nbq, nbk, 0.9, 0.08)
+    spec = dict(family="block_bitmap", sq=S, skv=K, batch=1, heads=1, blk_state=st[None, None],
+                blk_index=ix[None, None].astype(np.int32), blk_bits=bits.reshape(-1, 64), force_diag=False)
+    arrays = synth.draw_qkv(w)
+    q, k, v = to_device(w, arrays)
+    enc = fm.encode(spec)
+    for bm in (128, 64):
+        tiles = fm.classify(enc, bm, 64)
+        assert int(tiles.arrays()[2].max()) > 256
+        o, lse = fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"])
+        torch.cuda.synchronize()
+        qq, kk, vv = (to_f64(w, a) for a in arrays)
+        ro, rl = OA.attention_dense(qq, kk, vv, OA.spec_vis_fn(spec), w["scale"])
+        compare(w, o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"long rows bm {bm}")
+
+
 def test_gqa_groups_and_batch():
     for Hq, Hkv in [(8, 1), (8, 8), (6, 2)]:
         w = _small("bf16", 128, 257, 257, Hq=Hq, Hkv=Hkv, B=2)

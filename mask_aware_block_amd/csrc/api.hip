@@ -393,12 +393,16 @@ fmask_status fmask_encode(const fmask_mask_desc* desc, void* out, size_t out_byt
       p.pre = std::min(std::max(desc->pre_tokens, -lim), lim);
       p.next = std::min(std::max(desc->next_tokens, -lim), lim);
       if (is_segment_family(f)) {
-        int32_t* cu = at<int32_t>(out, L.cu);
-        e = hipMemcpyAsync(cu, desc->cu_seg, (size_t)(desc->n_seg + 1) * sizeof(int32_t),
-                           hipMemcpyHostToDevice, s);
-        if (e != hipSuccess) return hip_status(e, "copy cu_seg");
-        p.cu = cu;
         p.n_seg = desc->n_seg;
+        if (desc->n_seg <= kSegInline) {  // small: in the kernel's arguments
+          memcpy(p.cu_inline, desc->cu_seg, (size_t)(desc->n_seg + 1) * sizeof(int32_t));
+        } else {
+          int32_t* cu = at<int32_t>(out, L.cu);
+          e = hipMemcpyAsync(cu, desc->cu_seg, (size_t)(desc->n_seg + 1) * sizeof(int32_t),
+                             hipMemcpyHostToDevice, s);
+          if (e != hipSuccess) return hip_status(e, "copy cu_seg");
+          p.cu = cu;
+        }
       }
       if (f == FMASK_VARLEN) {
         const int n = desc->n_seg;

@@ -45,6 +45,9 @@ __device__ inline int segment_of(const int32_t* cu, int n_seg, int64_t pos) {
 }
 
 __global__ void k_family_intervals(SegParams p, int32_t* iv) {
+  // segment starts: in the arguments when few, else the device copy (varlen
+  // always uses its device copies)
+  const int32_t* cu = (p.family != FMASK_VARLEN && p.n_seg <= kSegInline) ? p.cu_inline : p.cu;
   for (int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; j < p.skv;
        j += (int64_t)gridDim.x * blockDim.x) {
     int64_t vlo = 0, vhi = p.sq;
@@ -56,21 +59,21 @@ __global__ void k_family_intervals(SegParams p, int32_t* iv) {
         vlo = j - ((int64_t)p.skv - p.sq);
         break;
       case FMASK_DOCUMENT: {
-        int s = segment_of(p.cu, p.n_seg, j);
-        vlo = p.cu[s];
-        vhi = p.cu[s + 1];
+        int s = segment_of(cu, p.n_seg, j);
+        vlo = cu[s];
+        vhi = cu[s + 1];
         break;
       }
       case FMASK_CAUSAL_DOCUMENT: {
-        int s = segment_of(p.cu, p.n_seg, j);
+        int s = segment_of(cu, p.n_seg, j);
         vlo = j;
-        vhi = p.cu[s + 1];
+        vhi = cu[s + 1];
         break;
       }
       case FMASK_SHARED_QUESTION: {  // question columns: every later row; answers: own answer
-        int s = segment_of(p.cu, p.n_seg, j);
+        int s = segment_of(cu, p.n_seg, j);
         vlo = j;
-        vhi = (s == 0) ? p.sq : p.cu[s + 1];
+        vhi = (s == 0) ? p.sq : cu[s + 1];
         break;
       }
       case FMASK_BAND: {  // r - pre <= j <= r + next with r = i + skv - sq

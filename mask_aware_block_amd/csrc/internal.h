@@ -14,11 +14,14 @@ constexpr int kBlk = FMASK_BLOCK;  // 64: bitmap granularity
 constexpr int kXcds = 8;           // MI355X: 8 XCDs, workgroups dealt round-robin
 
 // ---------------------------------------------------------------- encoder
+constexpr int kSegInline = 64;
+
 struct SegParams {
   int32_t family;
   int32_t sq, skv;
-  const int32_t* cu;  // device copy of cu_seg, n_seg + 1 entries
+  const int32_t* cu;  // device copy of cu_seg, n_seg + 1 entries (more than kSegInline segments)
   int32_t n_seg;
+  int32_t cu_inline[kSegInline + 1];  // cu_seg itself, up to kSegInline segments (no copy)
   int64_t pre, next;  // band, clamped by the host to +-(sq + skv + 1)
   int32_t tree_prefix;
   const int32_t* tree_hi;  // per draft node: last descendant (interval-form tree)

@@ -47,6 +47,15 @@ def _small_specs():
         dict(family="tree", sq=300, skv=300, tree_prefix=236,
              tree_parent=synth.random_tree(rng, 64, order="dfs")),
     ]
+    # more segments than the encoder passes in its kernel arguments (64): the
+    # segment starts go through a device copy instead
+    cu_many = np.unique(np.concatenate(([0, 1500], rng.choice(np.arange(1, 1500), 99, replace=False))))
+    cu_many = cu_many.astype(np.int32)
+    out += [dict(family=f, sq=1500, skv=1500, cu_seg=cu_many)
+            for f in ("document", "causal_document", "shared_question")]
+    for n in (64, 65):  # the last count passed in the arguments, the first copied
+        out.append(dict(family="causal_document", sq=1500, skv=1500,
+                        cu_seg=np.array(cu_many[:n].tolist() + [1500], dtype=np.int32)))
     # packed variable-length batches: every mode, empty segments, Sq != Skv
     for trial in range(3):
         n = 6

@@ -142,8 +142,8 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
   const int64_t ks2 = p.ks[2], vs2 = p.vs[2];
   const int32_t* ivcol = p.iv + ((size_t)it.mb * p.mh + it.mh) * 4 * (size_t)p.skv;
 
-  for (int i = tid; i < G::END / 16; i += NT) ((i32x4*)smem)[i] = i32x4{0, 0, 0, 0};
-  if (KIND == FMASK_ENC_BITMAP) __syncthreads();  // the block info below shares the cleared region
+  // (LDS is not cleared: every byte a wave reads is written first, K and V
+  // tiles entirely by their loads, zeros past the end included)
   for (int i = tid; i < min(cnt, kList); i += NT) lst[i] = list[i];
   auto entry = [&](int i) INLINE -> int {
     return i < kList ? __builtin_amdgcn_readfirstlane(lst[i]) : sload_wait(list + i);
@@ -172,13 +172,6 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
     return __builtin_amdgcn_readfirstlane(block_info(e, w >> 1));
   };
 
-  bf16x8 qf[KT];
-#pragma unroll
-  for (int t = 0; t < KT; ++t) {
-    if (qrow < p.sq) qf[t] = *(const bf16x8*)(Q + qrow * p.qs[2] + 16 * t + 8 * half);
-    else qf[t] = bf16x8{};
-  }
-  wait_all();  // nothing tracked may stay pending once untracked loads fly
 
   f32x16 acc[DB];
 #pragma unroll
@@ -247,10 +240,20 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
     for (int n = 0; n < G::LOADS; ++n) dma16s(vrs, vgo, g0 + n * vrow, base + n * 1024);
   };
 
-  __syncthreads();  // LDS cleared and the list staged before any tile load lands
+  __syncthreads();  // the list (and block info) staged
+  // The first K tile's loads fly while Q comes in.  (Every wait on the
+  // vector-memory counter drains the oldest loads first, so the compiler's
+  // waits for Q, which know nothing of the tile loads, still cover Q.)
+  const int e0 = cnt > 0 ? entry(0) : 0;
+  if (cnt > 0) issue_k(0, e0, 0);
+  bf16x8 qf[KT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    if (qrow < p.sq) qf[t] = *(const bf16x8*)(Q + qrow * p.qs[2] + 16 * t + 8 * half);
+    else qf[t] = bf16x8{};
+  }
   if (cnt > 0) {
-    int e_cur = entry(0);
-    issue_k(0, e_cur, 0);
+    int e_cur = e0;
     wait_all();
     barrier();
     for (int i = 0; i < cnt; ++i) {

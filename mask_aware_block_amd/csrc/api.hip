@@ -173,7 +173,7 @@ fmask_status check_desc(const fmask_mask_desc* d, int* kind) {
 struct EncLayout {
   int kind = 0;
   size_t total = 0;
-  size_t iv = 0, cu = 0, parent = 0, tree_hi = 0, flag = 0;
+  size_t iv = 0, cu = 0, parent = 0, tree_hi = 0, flag = 0, dws = 0;
   size_t bstate = 0, bindex = 0, bbits = 0, row_count = 0, row_offset = 0, pool_count = 0;
   size_t list = 0, count = 0;
   int64_t nbq = 0, nbk = 0, cap = 0;
@@ -186,7 +186,10 @@ EncLayout enc_layout(const fmask_mask_desc* d, int kind) {
   const int64_t nmask = (int64_t)d->batch * d->heads;
   // A dense mask of the automatic form may end up in either form: room for both.
   const bool dense_auto = d->family == FMASK_DENSE && d->dense_form == 0;
-  if (d->family == FMASK_DENSE && kind == FMASK_ENC_INTERVALS) L.flag = c.take(sizeof(int32_t));
+  if (d->family == FMASK_DENSE && kind == FMASK_ENC_INTERVALS) {
+    L.flag = c.take(sizeof(int32_t));
+    L.dws = c.take(std::max<size_t>(dense_ws_bytes(nmask, d->sq, d->skv), 16));
+  }
   if (kind == FMASK_ENC_INTERVALS) {
     L.iv = c.take((size_t)nmask * 4 * d->skv * sizeof(int32_t));
     if (is_segment_family(d->family)) L.cu = c.take((size_t)(d->n_seg + 1) * sizeof(int32_t));
@@ -366,7 +369,7 @@ fmask_status fmask_encode(const fmask_mask_desc* desc, void* out, size_t out_byt
     int32_t* iv = at<int32_t>(out, L.iv);
     int32_t* bad = at<int32_t>(out, L.flag);
     enc->intervals = iv;
-    e = launch_encode_dense_intervals(desc->dense, nmask, sq, skv, iv, bad, s);
+    e = launch_encode_dense_intervals(desc->dense, nmask, sq, skv, at<char>(out, L.dws), iv, bad, s);
     if (e != hipSuccess) return hip_status(e, "dense encode kernel");
     int32_t hbad = 0;  // the one synchronising read: which form holds the mask
     e = hipMemcpyAsync(&hbad, bad, sizeof(int32_t), hipMemcpyDeviceToHost, s);

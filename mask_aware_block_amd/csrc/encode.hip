@@ -11,6 +11,7 @@
 // * Selected-key lists (llama.cpp selected-key PR): valid, distinct, ascending.
 #include <algorithm>
 
+#include "device_util.h"
 #include "internal.h"
 
 namespace fmask {
@@ -170,6 +171,7 @@ __global__ void k_tree_hi(const int32_t* parent, int32_t n, int32_t* hi) {
 struct Runs {
   int32_t n, s0, e0, s1, e1;
 };
+static_assert(sizeof(Runs) == 20, "partial-run records are 20 bytes");
 
 // a then b, where b's rows follow a's: a run of b that starts where a's last
 // run ends continues it.
@@ -209,24 +211,85 @@ __device__ inline Runs runs_of(uint64_t w, int32_t base) {
   return r;
 }
 
-// One workgroup (16 waves) per (mask, 64-column strip); lane = column.  Wave w
-// walks its own contiguous share of the rows 64 at a time (one byte per lane
-// per row: a wave reads 64 consecutive bytes of a row), turning each 64-row
-// chunk into a bit word and that word into runs; the 16 shares are then joined
-// in row order through LDS.  A mask with a column of more than two runs raises
-// *bad.
+typedef int32_t dense_x4 __attribute__((ext_vector_type(4)));
+__device__ dense_x4 dense_load16(rsrc_t rsrc, int voffset, int soffset, int aux) __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+__device__ uint32_t write_lane(uint32_t value, uint32_t lane, uint32_t old) __asm("llvm.amdgcn.writelane.i32");
+
+// One workgroup (16 waves) per (mask, 64-column strip); lane = column in the
+// end.  Wave w walks its own contiguous share of the rows 64 at a time,
+// turning each 64-row chunk of its 64 columns into one bit word per column and
+// that word into runs; the 16 shares are then joined in row order through LDS.
+// A mask with a column of more than two runs raises *bad.
+//   ROWS (Skv a multiple of 16): lane r reads the 64 bytes of chunk row r with
+//     four 16-byte loads, and one ballot per column turns the 64 rows' bytes
+//     into that column's word, which v_writelane drops into the column's lane;
+//   otherwise: lane = column throughout, one byte per lane and row (a wave
+//     reads 64 consecutive bytes of a row).
 constexpr int kDenseWaves = 16;
 
+// Canonical intervals of a column from its runs (more than two: flag the mask).
+__device__ inline void dense_store(const Runs& acc, int32_t sq, int32_t skv, int64_t m, int32_t j, int32_t* iv,
+                                   int32_t* bad) {
+  int32_t uts = 0, ute = 0, lts = sq, lte = sq;
+  if (acc.n == 1) {
+    if (acc.s0 == 0) ute = acc.e0; else { lts = acc.s0; lte = acc.e0; }
+  } else if (acc.n == 2) {
+    uts = acc.s0; ute = acc.e0; lts = acc.s1; lte = acc.e1;
+  } else if (acc.n > 2) {
+    atomicOr(bad, 1);
+  }
+  int32_t* o = iv + m * 4 * (int64_t)skv;
+  o[j] = uts;
+  o[skv + j] = ute;
+  o[2 * (int64_t)skv + j] = lts;
+  o[3 * (int64_t)skv + j] = lte;
+}
+
+// Workgroup (m, strip, g) covers rows [g * grows, (g + 1) * grows) of the
+// strip; with one group it writes the intervals, else its joined runs go to
+// ws[m][g][column] for k_dense_join.
+template <bool ROWS>
 __global__ void __launch_bounds__(1024) k_dense_intervals(const uint8_t* dense, int32_t sq, int32_t skv,
-                                                          int32_t nstrip, int32_t* iv, int32_t* bad) {
+                                                          int32_t nstrip, int32_t ngroup, int32_t grows,
+                                                          Runs* ws, int32_t* iv, int32_t* bad) {
   __shared__ Runs part[kDenseWaves][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t m = blockIdx.x / nstrip;
-  const int32_t j = (blockIdx.x % nstrip) * 64 + lane;
-  const int32_t share = (((sq + kDenseWaves - 1) / kDenseWaves) + 63) & ~63;
-  const int32_t r0 = wave * share, r1 = min(sq, r0 + share);
+  const int32_t g = blockIdx.x % ngroup;
+  const int64_t m = blockIdx.x / ((int64_t)ngroup * nstrip);
+  const int32_t c0 = (int32_t)((blockIdx.x / ngroup) % nstrip) * 64, j = c0 + lane;
+  const int32_t g0 = g * grows, g1 = min(sq, g0 + grows);
+  const int32_t share = (((grows + kDenseWaves - 1) / kDenseWaves) + 63) & ~63;
+  const int32_t r0 = g0 + wave * share, r1 = min(g1, r0 + share);
   Runs acc{0, 0, 0, 0, 0};
-  if (j < skv) {
+  if (ROWS) {
+    // rows [base, base + rows) of mask m; lanes past the chunk and bytes past
+    // the mask read zeros, columns past skv are never written out
+    auto load = [&](int32_t base, dense_x4* d) {  // (an empty range past the share: zeros)
+      const rsrc_t r = make_rsrc(dense + ((size_t)m * sq + base) * skv, (int64_t)max(0, min(64, r1 - base)) * skv);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) d[k] = dense_load16(r, lane * skv + c0 + 16 * k, 0, 0);
+    };
+    dense_x4 d[4], dn[4];
+    load(r0, d);
+    for (int32_t base = r0; base < r1; base += 64) {
+      const int32_t rows = min(64, r1 - base);
+      load(base + 64, dn);  // the next chunk's bytes fly during this one
+      const int32_t past = lane >= rows ? 0x01010101 : 0;  // rows past the chunk: visible (not masked)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) d[k] |= past;
+      uint32_t wlo = 0, whi = 0;  // masked rows of column c0 + lane
+#pragma unroll
+      for (int col = 0; col < 64; ++col) {
+        const uint32_t byte = ((uint32_t)d[col >> 4][(col >> 2) & 3] >> (8 * (col & 3))) & 0xffu;
+        const uint64_t vis = __ballot(byte != 0u);
+        wlo = write_lane(~(uint32_t)vis, col, wlo);
+        whi = write_lane(~(uint32_t)(vis >> 32), col, whi);
+      }
+      acc = join(acc, runs_of(((uint64_t)whi << 32) | wlo, base));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) d[k] = dn[k];
+    }
+  } else if (j < skv) {
     const uint8_t* col = dense + (size_t)m * sq * skv + j;
     for (int32_t base = r0; base < r1; base += 64) {
       const int32_t rows = min(64, r1 - base);
@@ -244,19 +307,21 @@ __global__ void __launch_bounds__(1024) k_dense_intervals(const uint8_t* dense, 
   __syncthreads();
   if (wave != 0 || j >= skv) return;
   for (int k = 1; k < kDenseWaves; ++k) acc = join(acc, part[k][lane]);
-  int32_t uts = 0, ute = 0, lts = sq, lte = sq;
-  if (acc.n == 1) {
-    if (acc.s0 == 0) ute = acc.e0; else { lts = acc.s0; lte = acc.e0; }
-  } else if (acc.n == 2) {
-    uts = acc.s0; ute = acc.e0; lts = acc.s1; lte = acc.e1;
-  } else if (acc.n > 2) {
-    atomicOr(bad, 1);
+  if (ngroup == 1) dense_store(acc, sq, skv, m, j, iv, bad);
+  else ws[(m * ngroup + g) * skv + j] = acc;
+}
+
+// The row groups of each (mask, column) joined in row order.
+__global__ void k_dense_join(const Runs* ws, int64_t nmask, int32_t ngroup, int32_t sq, int32_t skv, int32_t* iv,
+                             int32_t* bad) {
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < nmask * skv;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = t / skv;
+    const int32_t j = (int32_t)(t % skv);
+    Runs acc{0, 0, 0, 0, 0};
+    for (int g = 0; g < ngroup; ++g) acc = join(acc, ws[(m * ngroup + g) * skv + j]);
+    dense_store(acc, sq, skv, m, j, iv, bad);
   }
-  int32_t* o = iv + m * 4 * (int64_t)skv;
-  o[j] = uts;
-  o[skv + j] = ute;
-  o[2 * (int64_t)skv + j] = lts;
-  o[3 * (int64_t)skv + j] = lte;
 }
 
 __global__ void k_zero_int(int32_t* x) { *x = 0; }
@@ -468,13 +533,24 @@ hipError_t launch_encode_bitmap(const BitmapSrc& src, const BitmapOut& out, hipS
 }
 
 hipError_t launch_encode_dense_intervals(const uint8_t* dense, int32_t nmask, int32_t sq, int32_t skv,
-                                         int32_t* iv, int32_t* bad, hipStream_t s) {
+                                         void* ws, int32_t* iv, int32_t* bad, hipStream_t s) {
   hipLaunchKernelGGL(k_zero_int, dim3(1), dim3(1), 0, s, bad);
   const int32_t nstrip = (skv + 63) / 64;
-  const int64_t blocks = (int64_t)nmask * nstrip;
-  if (blocks > 0)
-    hipLaunchKernelGGL(k_dense_intervals, dim3((unsigned)blocks), dim3(1024), 0, s, dense, sq, skv, nstrip,
-                       iv, bad);
+  const int32_t ngroup = dense_groups(nmask, sq, skv);
+  const int32_t grows = (int32_t)((((int64_t)sq + ngroup - 1) / ngroup + 63) / 64 * 64);
+  const int64_t blocks = (int64_t)nmask * nstrip * ngroup;
+  if (blocks <= 0) return hipGetLastError();
+  // 16-byte row loads need 16-byte aligned rows; 64 rows must stay within the
+  // 32-bit buffer offsets
+  if (skv % 16 == 0 && (uintptr_t)dense % 16 == 0 && (int64_t)64 * skv < ((int64_t)1 << 31))
+    hipLaunchKernelGGL(k_dense_intervals<true>, dim3((unsigned)blocks), dim3(1024), 0, s, dense, sq, skv,
+                       nstrip, ngroup, grows, (Runs*)ws, iv, bad);
+  else
+    hipLaunchKernelGGL(k_dense_intervals<false>, dim3((unsigned)blocks), dim3(1024), 0, s, dense, sq, skv,
+                       nstrip, ngroup, grows, (Runs*)ws, iv, bad);
+  if (ngroup > 1)
+    hipLaunchKernelGGL(k_dense_join, dim3(grid_for((int64_t)nmask * skv, 256)), dim3(256), 0, s, (const Runs*)ws,
+                       (int64_t)nmask, ngroup, sq, skv, iv, bad);
   return hipGetLastError();
 }
 

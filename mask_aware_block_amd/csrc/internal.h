@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "fmask.h"
 
 namespace fmask {
@@ -67,8 +69,22 @@ struct BitmapOut {
 hipError_t launch_encode_bitmap(const BitmapSrc& src, const BitmapOut& out, hipStream_t s);
 // Dense uint8 masks -> canonical intervals; *bad (zeroed here) becomes nonzero
 // if some column has more than two masked runs.
+// Dense mask -> canonical intervals.  Rows are split into dense_groups()
+// groups so that enough workgroups run; with more than one group `ws` holds
+// dense_ws_bytes() of partial runs.
+inline int32_t dense_groups(int64_t nmask, int32_t sq, int32_t skv) {
+  const int64_t strips = nmask * ((skv + 63) / 64);
+  if (strips <= 0) return 1;
+  const int64_t want = (512 + strips - 1) / strips;  // about 512 workgroups
+  const int64_t most = ((int64_t)sq + 1023) / 1024;  // at least 1024 rows per group
+  return (int32_t)std::max<int64_t>(1, std::min(want, most));
+}
+inline size_t dense_ws_bytes(int64_t nmask, int32_t sq, int32_t skv) {
+  const int32_t g = dense_groups(nmask, sq, skv);
+  return g > 1 ? (size_t)nmask * g * skv * 20 : 0;  // one 20-byte record of runs per (mask, group, column)
+}
 hipError_t launch_encode_dense_intervals(const uint8_t* dense, int32_t nmask, int32_t sq, int32_t skv,
-                                         int32_t* iv, int32_t* bad, hipStream_t s);
+                                         void* ws, int32_t* iv, int32_t* bad, hipStream_t s);
 
 hipError_t launch_encode_selected(const int32_t* sel, int32_t nb, int32_t sq, int32_t n,
                                   int32_t nblk, int32_t* list, int32_t* count, hipStream_t s);

@@ -284,13 +284,15 @@ def _runs_column(rng, S, cuts):
 
 
 def test_dense_runs_across_row_chunks():
-    """Masked runs that start, end or meet on 64-row chunk edges and on the
-    edges of the encoder's per-wave row shares, at a ragged size: canonical
+    """Masked runs that start, end or meet on 64-row chunk edges, on the edges
+    of the encoder's per-wave row shares and of its row groups (whose partial
+    runs a second kernel joins), at a ragged size: canonical
     intervals bit-exact; a third run far from the other two sends the automatic
     form to the bitmap and makes the interval form fail."""
     rng = np.random.default_rng(79)
     S, K = 2500, 300
-    cuts = np.array([0, 63, 64, 65, 128, 191, 192, 193, 384, 1152, 2496, 2499, 2500])
+    # 64-row chunks, per-wave shares and (896 rows each here) row groups
+    cuts = np.array([0, 63, 64, 65, 128, 191, 192, 193, 384, 895, 896, 897, 1152, 1792, 2496, 2499, 2500])
     vis = np.stack([_runs_column(rng, S, cuts) for _ in range(K)], axis=1)[None, None]
     vis[0, 0, :, 5] = True
     vis[0, 0, :, 6] = False

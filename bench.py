@@ -116,11 +116,13 @@ def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5):
     wall = (time.perf_counter() - t0) / steps
     t_enc = np.mean([a[0].elapsed_time(a[1]) for a in evs])
     t_cls = np.mean([a[1].elapsed_time(a[2]) for a in evs])
-    t_att = np.mean([a[2].elapsed_time(a[3]) for a in evs])
+    att = [a[2].elapsed_time(a[3]) for a in evs]
+    t_att = np.mean(att)
 
     rec = dict(workload=name, B=w["B"], Hq=w["Hq"], Hkv=w["Hkv"], Sq=w["Sq"], Skv=w["Skv"], D=w["D"],
                dtype=w["dtype"], ms_per_step=wall * 1e3, encode_ms=float(t_enc),
-               classify_ms=float(t_cls), attn_ms=float(t_att))
+               classify_ms=float(t_cls), attn_ms=float(t_att),
+               attn_ms_median=float(np.median(att)), attn_ms_min=float(np.min(att)))
     if selected:
         ls, cn = enc.lists()
         cells = int(cn.sum().item()) * w["mask"]["sel_cells"]  # listed cells per (b, query)
@@ -302,8 +304,14 @@ def cpu_baseline(synth, name, rows, heads):
     OA.attention_dense(q[:, :heads], k, v, vf, w["scale"])
     dt = time.perf_counter() - t0
     nvis = int(np.asarray(OM.dense_vis(spec, 0, 0, np.arange(rows))).sum()) * heads
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:  # pragma: no cover
+        pass
     return dict(value=4 * w["D"] * nvis / dt / 1e12, unit="effective TFLOP/s", cores=int(threads),
-                kind="oracle", seconds=dt,
+                kind="oracle", seconds=dt, affinity=len(os.sched_getaffinity(0)), cpu_model=cpu,
                 sample=f"{name}: query heads 0..{heads - 1} (K/V head 0), rows 0..{rows - 1} of {w['Sq']}, "
                        f"all {w['Skv']} keys, float64 dense masked softmax attention")
 

@@ -286,10 +286,12 @@ class MaskInput:
         self.desc, self.keep = make_desc(spec, device)
 
 
-def encode(spec, device="cuda", stream=None):
+def encode(spec, device="cuda", stream=None, out=None):
     """Run the mask encoder (fmask_encode) on the device.
 
-    spec: a mask spec dict (see make_desc) or a MaskInput.
+    spec: a mask spec dict (see make_desc) or a MaskInput.  out: optional uint8
+    device buffer to hold the encoding (reused when large enough, e.g. across
+    steps; the returned Encoding views it).
     """
     torch = _torch()
     L = lib()
@@ -300,17 +302,26 @@ def encode(spec, device="cuda", stream=None):
     nbytes = L.fmask_encode_bytes(ctypes.byref(desc))
     if nbytes == 0:
         _check(L.fmask_encode(ctypes.byref(desc), None, 0, ctypes.byref(Encoded()), None))
-    buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if out is not None and out.dtype == torch.uint8 and out.is_cuda and out.numel() >= nbytes:
+        buf = out
+    else:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
     enc = Encoded()
-    _check(L.fmask_encode(ctypes.byref(desc), _ptr(buf), nbytes, ctypes.byref(enc), _stream_handle(stream)))
+    _check(L.fmask_encode(ctypes.byref(desc), _ptr(buf), buf.numel(), ctypes.byref(enc), _stream_handle(stream)))
     keep.append(desc)
     return Encoding(enc, buf, keep)
 
 
+_preferred = {}
+
+
 def preferred_tile(dtype, d, kind):
-    bm, bn = ctypes.c_int32(), ctypes.c_int32()
-    _check(lib().fmask_preferred_tile(DTYPES[dtype], int(d), int(kind), ctypes.byref(bm), ctypes.byref(bn)))
-    return bm.value, bn.value
+    key = (id(lib()), dtype, int(d), int(kind))
+    if key not in _preferred:
+        bm, bn = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().fmask_preferred_tile(DTYPES[dtype], int(d), int(kind), ctypes.byref(bm), ctypes.byref(bn)))
+        _preferred[key] = (bm.value, bn.value)
+    return _preferred[key]
 
 
 class TileTable:
@@ -335,8 +346,10 @@ class TileTable:
 
 
 
-def classify(enc, bm=None, bn=None, dtype="bf16", d=128, stream=None):
-    """Run the tile classifier (fmask_classify) at bm x bn (default: the kernel's tile)."""
+def classify(enc, bm=None, bn=None, dtype="bf16", d=128, stream=None, out=None):
+    """Run the tile classifier (fmask_classify) at bm x bn (default: the kernel's
+    tile).  out: optional uint8 device buffer for the table (reused when large
+    enough)."""
     torch = _torch()
     L = lib()
     if bm is None or bn is None:
@@ -345,9 +358,12 @@ def classify(enc, bm=None, bn=None, dtype="bf16", d=128, stream=None):
     if nbytes == 0:
         _check(L.fmask_classify(ctypes.byref(enc.struct), int(bm), int(bn), None, 0,
                                 ctypes.byref(Tiles()), None))
-    buf = torch.empty(nbytes, dtype=torch.uint8, device=enc.buf.device)
+    if out is not None and out.dtype == torch.uint8 and out.is_cuda and out.numel() >= nbytes:
+        buf = out
+    else:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=enc.buf.device)
     t = Tiles()
-    _check(L.fmask_classify(ctypes.byref(enc.struct), int(bm), int(bn), _ptr(buf), nbytes,
+    _check(L.fmask_classify(ctypes.byref(enc.struct), int(bm), int(bn), _ptr(buf), buf.numel(),
                             ctypes.byref(t), _stream_handle(stream)))
     return TileTable(t, buf, enc)
 

@@ -15,6 +15,8 @@
 namespace fmask {
 namespace {
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
 __device__ inline int32_t overlap(int32_t r0, int32_t r1, int32_t a, int32_t b) {
   int32_t lo = max(r0, a), hi = min(r1, b);
   return hi > lo ? hi - lo : 0;
@@ -44,6 +46,39 @@ __global__ void __launch_bounds__(256) k_classify_intervals(const int32_t* iv, i
     uint8_t st = all_masked ? FMASK_SKIP : (none_masked ? FMASK_FULL : FMASK_PARTIAL);
     state[(m * nqt + qt) * (int64_t)nkt + kt] = st;
   }
+}
+
+// The same rule with one wave per (mask, key tile, 64 query tiles) when the
+// tile is 64 keys wide: lane = key column, whose intervals are read once; per
+// query tile two ballots give "every column fully masked" (SKIP) and "no
+// column masked" (FULL), and lane qt % 64 keeps that tile's state for one
+// store at the end.
+__global__ void __launch_bounds__(256) k_classify_intervals_cols(const int32_t* iv, int32_t nmask, int32_t sq,
+                                                                 int32_t skv, int32_t bm, int32_t nqt, int32_t nkt,
+                                                                 uint8_t* state) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int32_t nqg = (nqt + 63) / 64;
+  if (wv >= (int64_t)nmask * nkt * nqg) return;
+  const int32_t qg = (int32_t)(wv % nqg);
+  const int32_t kt = (int32_t)((wv / nqg) % nkt);
+  const int64_t m = wv / ((int64_t)nqg * nkt);
+  const int32_t j = kt * 64 + lane;
+  const bool col = j < skv;
+  const int32_t* c = iv + m * 4 * (int64_t)skv;
+  const int32_t us = col ? c[j] : 0, ue = col ? c[skv + j] : 0;
+  const int32_t ls = col ? c[2 * (int64_t)skv + j] : 0, le = col ? c[3 * (int64_t)skv + j] : 0;
+  uint8_t mine = FMASK_SKIP;
+  const int32_t q0 = qg * 64, q1 = min(nqt, q0 + 64);
+  for (int32_t qt = q0; qt < q1; ++qt) {
+    const int32_t r0 = qt * bm, r1 = min(sq, r0 + bm);
+    const int32_t mc = overlap(r0, r1, us, ue) + overlap(r0, r1, ls, le);
+    const bool all_masked = __ballot(col && mc != r1 - r0) == 0ull;
+    const bool none_masked = __ballot(col && mc != 0) == 0ull;
+    const uint8_t st = all_masked ? FMASK_SKIP : (none_masked ? FMASK_FULL : FMASK_PARTIAL);
+    if (lane == qt - q0) mine = st;
+  }
+  if (q0 + lane < q1) state[(m * nqt + q0 + lane) * (int64_t)nkt + kt] = mine;
 }
 
 // Bitmap form, tiles made of whole 64 x 64 blocks: combine the exact block states.
@@ -124,7 +159,7 @@ __global__ void __launch_bounds__(256) k_tile_cols(const uint8_t* state, int32_t
 // is unique, so order[rank] = row is a permutation.
 __global__ void __launch_bounds__(256) k_tile_order(const int32_t* count, int32_t rows,
                                                     int32_t* order) {
-  __shared__ int32_t chunk[1024];
+  __shared__ __attribute__((aligned(16))) int32_t chunk[1024];
   int x = blockIdx.x * blockDim.x + threadIdx.x;
   int32_t cx = x < rows ? count[x] : 0;
   int rank = 0;
@@ -133,11 +168,15 @@ __global__ void __launch_bounds__(256) k_tile_order(const int32_t* count, int32_
     for (int i = threadIdx.x; i < 1024; i += blockDim.x)
       chunk[i] = base + i < rows ? count[base + i] : -1;
     __syncthreads();
-    int lim = min(1024, rows - base);
-    for (int i = 0; i < lim; ++i) {
-      int32_t cy = chunk[i];
-      int y = base + i;
-      rank += (cy > cx) || (cy == cx && y < x);
+    // four counts per LDS read (the stage is padded with -1, below any count)
+    const int lim4 = (min(1024, rows - base) + 3) / 4;
+    const i32x4* c4 = (const i32x4*)chunk;
+#pragma unroll 4
+    for (int i = 0; i < lim4; ++i) {
+      const i32x4 cy = c4[i];
+      const int y = base + 4 * i;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) rank += (cy[k] > cx) || (cy[k] == cx && y + k < x);
     }
   }
   if (x < rows) order[rank] = x;
@@ -157,6 +196,14 @@ hipError_t launch_classify_intervals(const int32_t* iv, int32_t nmask, int32_t s
                                      uint8_t* state, hipStream_t s) {
   int64_t total = (int64_t)nmask * nqt * nkt;
   if (total <= 0) return hipSuccess;
+  if (bn == 64) {
+    const int64_t waves = (int64_t)nmask * nkt * ((nqt + 63) / 64);
+    if ((waves + 3) / 4 <= INT32_MAX) {
+      hipLaunchKernelGGL(k_classify_intervals_cols, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, iv, nmask,
+                         sq, skv, bm, nqt, nkt, state);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL(k_classify_intervals, dim3(grid_for(total, 256)), dim3(256), 0, s, iv, nmask,
                      sq, skv, bm, bn, nqt, nkt, state);
   return hipGetLastError();

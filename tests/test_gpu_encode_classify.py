@@ -333,3 +333,22 @@ def test_dense_masks_fall_back_to_the_bitmap_form():
     st = t.arrays()[0].cpu().numpy()
     for b in range(2):
         np.testing.assert_array_equal(st[b, 0], OE.tile_states(vis[b, 0], 64, 64))
+
+
+def test_caller_buffers_reused_across_calls():
+    """encode / classify into caller-owned buffers (bigger than needed, reused
+    for a second, different mask): the same encodings and tables as fresh ones."""
+    a = dict(family="causal_document", sq=700, skv=700, cu_seg=np.array([0, 100, 450, 700], dtype=np.int32))
+    b = dict(family="band", sq=650, skv=650, pre=40, next=3)
+    ebuf = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    tbuf = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    for spec in (a, b):
+        ref = fm.encode(spec)
+        got = fm.encode(spec, out=ebuf)
+        assert got.buf.data_ptr() == ebuf.data_ptr()
+        assert torch.equal(got.intervals(), ref.intervals())
+        tr = fm.classify(ref, 128, 64)
+        tg = fm.classify(got, 128, 64, out=tbuf)
+        assert tg.buf.data_ptr() == tbuf.data_ptr()
+        for x, y in zip(tr.arrays(), tg.arrays()):
+            assert torch.equal(x, y)

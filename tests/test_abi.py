@@ -138,3 +138,58 @@ def test_classify_and_attn_host_validation():
     a.dtype = 1
     assert L.fmask_attn_fwd(ctypes.byref(a), None, p, p, p, None, ctypes.byref(enc), ctypes.byref(tiles),
                             None) == fm.ERR_INVALID  # null tensor
+
+
+def test_split_backward_varlen_dense_host_validation():
+    """The entry points added for decode, backward, varlen and dense input
+    reject bad arguments with status codes before any launch."""
+    L = fm.lib()
+    p = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails a host check first
+    a = fm.AttnArgs()
+    a.dtype, a.b, a.hq, a.hkv, a.sq, a.skv, a.d, a.scale = 1, 1, 8, 2, 512, 512, 128, 0.08
+    # split decode: SELECTED encodings only, splits in [0, 64]
+    iv_enc = fm.Encoded()
+    iv_enc.kind, iv_enc.batch, iv_enc.heads, iv_enc.sq, iv_enc.skv = fm.ENC_INTERVALS, 1, 1, 512, 512
+    assert L.fmask_attn_fwd_split(ctypes.byref(a), p, p, p, p, None, ctypes.byref(iv_enc), 0, None, 0,
+                                  None) == fm.ERR_UNSUPPORTED
+    sel = fm.Encoded()
+    sel.kind, sel.batch, sel.heads, sel.sq, sel.skv, sel.sel_n = fm.ENC_SELECTED, 1, 1, 512, 512, 64
+    assert L.fmask_attn_fwd_split(ctypes.byref(a), p, p, p, p, None, ctypes.byref(sel), 65, None, 0,
+                                  None) == fm.ERR_INVALID
+    assert L.fmask_attn_split_workspace_bytes(ctypes.byref(a), ctypes.byref(iv_enc), 4) == 0
+    assert L.fmask_attn_split_workspace_bytes(ctypes.byref(a), ctypes.byref(sel), 4) > 0
+    # backward: bf16 only, 128 x 64 tables, workspace at least the queried size
+    t = fm.Tiles()
+    t.bm, t.bn, t.nqt, t.nkt, t.batch, t.heads = 128, 64, 4, 8, 1, 1
+    need = L.fmask_attn_bwd_workspace_bytes(ctypes.byref(a), ctypes.byref(t))
+    assert need >= 8 * 512 * 8
+    args = [ctypes.byref(a)] + [p] * 4 + [ctypes.cast(p, ctypes.c_void_p)] + [p] * 4
+    assert L.fmask_attn_bwd(*args, p, need - 16, ctypes.byref(iv_enc), ctypes.byref(t), None) == fm.ERR_CAPACITY
+    t64 = fm.Tiles()
+    t64.bm, t64.bn, t64.nqt, t64.nkt, t64.batch, t64.heads = 64, 64, 8, 8, 1, 1
+    assert L.fmask_attn_bwd(*args, p, need, ctypes.byref(iv_enc), ctypes.byref(t64), None) == fm.ERR_UNSUPPORTED
+    a.dtype = 0
+    assert L.fmask_attn_bwd(*args, p, need, ctypes.byref(iv_enc), ctypes.byref(t), None) == fm.ERR_UNSUPPORTED
+    a.dtype = 1
+    assert L.fmask_attn_bwd(*args, p, need, ctypes.byref(sel), ctypes.byref(t), None) == fm.ERR_UNSUPPORTED
+    # varlen: segment lengths must add up, modes must be known
+    enc = fm.Encoded()
+    cu = np.array([0, 100, 300], dtype=np.int32)
+    cuk = np.array([0, 50, 260], dtype=np.int32)  # ends at 260, skv is 300
+    md = np.array([1, 2], dtype=np.int32)
+    vl = _desc(family=fm.FAMILIES["varlen"], sq=300, skv=300, cu_seg=cu.ctypes.data, cu_seg_k=cuk.ctypes.data,
+               seg_mode=md.ctypes.data, n_seg=2)
+    assert L.fmask_encode(ctypes.byref(vl), None, 0, ctypes.byref(enc), None) == fm.ERR_INVALID
+    assert b"end at sq and skv" in L.fmask_last_error()
+    cuk_ok = np.array([0, 50, 300], dtype=np.int32)
+    md_bad = np.array([1, 9], dtype=np.int32)
+    vl2 = _desc(family=fm.FAMILIES["varlen"], sq=300, skv=300, cu_seg=cu.ctypes.data, cu_seg_k=cuk_ok.ctypes.data,
+                seg_mode=md_bad.ctypes.data, n_seg=2)
+    assert L.fmask_encode(ctypes.byref(vl2), None, 0, ctypes.byref(enc), None) == fm.ERR_INVALID
+    assert b"not a varlen mode" in L.fmask_last_error()
+    # dense: the mask pointer and a known form are required
+    dn = _desc(family=fm.FAMILIES["dense"], sq=64, skv=64)
+    assert L.fmask_encode(ctypes.byref(dn), None, 0, ctypes.byref(enc), None) == fm.ERR_INVALID
+    dn2 = _desc(family=fm.FAMILIES["dense"], sq=64, skv=64, dense=1 << 20, dense_form=fm.ENC_SELECTED)
+    assert L.fmask_encode(ctypes.byref(dn2), None, 0, ctypes.byref(enc), None) == fm.ERR_INVALID
+    assert b"dense_form" in L.fmask_last_error()

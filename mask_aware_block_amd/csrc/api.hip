@@ -465,6 +465,7 @@ fmask_status fmask_encode(const fmask_mask_desc* desc, void* out, size_t out_byt
     } else if (f == FMASK_DENSE) {
       src.kind = 2;
       src.dense = desc->dense;
+      src.dense_vec = skv % 16 == 0 && (uintptr_t)desc->dense % 16 == 0;
     } else {
       src.kind = 0;
       src.state = desc->blk_state;

@@ -354,7 +354,24 @@ __device__ uint64_t source_word(const BitmapSrc& s, int m, int bi, int bj, int r
     // dense bytes of row i, columns 64 bj .. 64 bj + 63 (nonzero = visible)
     const uint8_t* row = s.dense + ((size_t)m * s.sq + i) * s.skv + (size_t)bj * kBlk;
     const int valid = min(64, s.skv - bj * kBlk);
-    for (int c = 0; c < valid; ++c) w |= (uint64_t)(row[c] != 0) << c;
+    if (s.dense_vec && valid == 64) {
+      // four 16-byte loads; bit 7 of ((b & 0x7f) + 0x7f) | b is set iff byte b
+      // is nonzero (no carry leaves the byte), then those bits are gathered
+      const uint4* row16 = (const uint4*)row;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = row16[q];
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t t = ((((d[k] & 0x7f7f7f7fu) + 0x7f7f7f7fu) | d[k]) & 0x80808080u) >> 7;
+          const uint32_t nib = (t & 1u) | ((t >> 7) & 2u) | ((t >> 14) & 4u) | ((t >> 21) & 8u);
+          w |= (uint64_t)nib << (16 * q + 4 * k);
+        }
+      }
+    } else {
+      for (int c = 0; c < valid; ++c) w |= (uint64_t)(row[c] != 0) << c;
+    }
   } else {
     int64_t P = s.tree_prefix;
     int64_t base = (int64_t)bj * kBlk;

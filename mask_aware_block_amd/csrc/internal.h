@@ -40,7 +40,7 @@ hipError_t launch_tree_hi(const int32_t* parent, int32_t n, int32_t* hi, hipStre
 
 // Source of the 64-bit row words of a 64 x 64 block, for the bitmap encoder.
 struct BitmapSrc {
-  int32_t kind;  // 0 = caller bitmap, 1 = tree
+  int32_t kind;  // 0 = caller bitmap, 1 = tree, 2 = dense bytes
   int32_t nmask, nbq, nbk;
   int32_t sq, skv;
   // caller bitmap
@@ -52,8 +52,10 @@ struct BitmapSrc {
   // tree
   int32_t tree_prefix, tree_n;
   const int32_t* parent;
-  // dense (kind 2): uint8 [nmask][sq][skv], nonzero = visible
+  // dense (kind 2): uint8 [nmask][sq][skv], nonzero = visible; dense_vec: rows
+  // 16-byte aligned (skv % 16 == 0 and an aligned base), read 16 bytes at a time
   const uint8_t* dense;
+  int32_t dense_vec;
 };
 
 struct BitmapOut {

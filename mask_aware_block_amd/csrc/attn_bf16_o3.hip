@@ -47,6 +47,7 @@ constexpr int BM = 32 * NW;
 constexpr int kList = 256;  // tile-list entries staged in LDS
 constexpr int kBinfo = 128;  // bitmap: list entries whose block info is staged in LDS
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyMax = 4294967296.f;  // 2^kLazyLog2 with kLazyLog2 = 32: bound on a lane's share of a row sum
 constexpr int kQkAhead = 3;  // K fragments read ahead of their MFMA
 constexpr int kPvAhead = 3;  // V^T fragments read ahead of their MFMA
 
@@ -306,11 +307,11 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
         // S^T = K Q^T for the two 32-key halves: 2 D / 16 MFMAs, each K
         // fragment read kQkAhead MFMAs ahead into a ring of registers
         // (sched_barrier keeps the scheduler from sinking the reads back next
-        // to their MFMAs).
+        // to their MFMAs); then the tile's mask.
         f32x16 s[2];
-        s[0] = f32x16{};
-        s[1] = f32x16{};
-        {
+        auto scores = [&]() INLINE {
+          s[0] = f32x16{};
+          s[1] = f32x16{};
           bf16x8 fr[kQkAhead];
           auto kread = [&](int n) INLINE -> bf16x8 {
             return *(const bf16x8*)(kb + (kofs ^ (32 * (n % KT))) + (n / KT) * 32 * (D * 2));
@@ -325,67 +326,79 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
             if (n + kQkAhead < 2 * KT) fr[n % kQkAhead] = kread(n + kQkAhead);
             __builtin_amdgcn_sched_barrier(0);
           }
-        }
-        if (need_mask) {
-          // bitmap: this lane's keys 8 (r / 4) + 4 half + r % 4 of each half,
-          // shifted so that the bit positions are constants
-          const uint64_t wl = word >> (4 * half);
+          if (need_mask) {
+            // bitmap: this lane's keys 8 (r / 4) + 4 half + r % 4 of each half,
+            // shifted so that the bit positions are constants
+            const uint64_t wl = word >> (4 * half);
 #pragma unroll
-          for (int kh = 0; kh < 2; ++kh) {
-            const uint32_t wk = (uint32_t)(wl >> (32 * kh));
+            for (int kh = 0; kh < 2; ++kh) {
+              const uint32_t wk = (uint32_t)(wl >> (32 * kh));
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int kl = kh * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-              if (KIND == FMASK_ENC_BITMAP) {
-                if (!((wk >> (8 * (r >> 2) + (r & 3))) & 1u)) s[kh][r] = -INFINITY;
-              } else {
-                if ((rmask[kl] >> l32) & 1u) s[kh][r] = -INFINITY;
+              for (int r = 0; r < 16; ++r) {
+                const int kl = kh * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (KIND == FMASK_ENC_BITMAP) {
+                  if (!((wk >> (8 * (r >> 2) + (r & 3))) & 1u)) s[kh][r] = -INFINITY;
+                } else {
+                  if ((rmask[kl] >> l32) & 1u) s[kh][r] = -INFINITY;
+                }
               }
             }
           }
-        }
-        // Online softmax (the other 32 keys of the row sit in lane ^ 32).  The
-        // row maximum uses the IEEE maximum (three operands per instruction, no
-        // canonicalisation of the MFMA results; masked scores are -inf, never
-        // NaN), over the first key half first, whose MFMAs finished earlier.
-        float m0 = __builtin_elementwise_maximum(s[0][0], s[0][1]);
+        };
+        // P = exp2(S c - m c) in bf16 against the running maximum m, and this
+        // lane's share of the row sum.
+        float lsum;
+        auto probs = [&]() INLINE {
+          const float mneg = -m_run * c;
 #pragma unroll
-        for (int r = 2; r < 16; r += 2)
-          m0 = __builtin_elementwise_maximum(m0, __builtin_elementwise_maximum(s[0][r], s[0][r + 1]));
-        float mloc = m0;
+          for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
-        for (int r = 0; r < 16; r += 2)
-          mloc = __builtin_elementwise_maximum(mloc, __builtin_elementwise_maximum(s[1][r], s[1][r + 1]));
-        mloc = pair_max(mloc);
-        const float m_cand = fmaxf(m_run, mloc);
-        const bool grow = (m_cand - m_run) * c > 8.f;
-        if (__any(grow)) {
-          const float m_new = grow ? m_cand : m_run;
+            for (int tp = 0; tp < 2; ++tp) {
+              f32x8 pv;
+#pragma unroll
+              for (int j = 0; j < 8; ++j)
+                pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][8 * tp + j], c, mneg));
+              pf[kh * 2 + tp] = __builtin_convertvector(pv, bf16x8);
+            }
+          }
+          const bf16x2 one2 = bf16x2{(__bf16)1.0f, (__bf16)1.0f};
+          lsum = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][2 * j], pf[ks][2 * j + 1]}, one2, lsum, false);
+        };
+        // Online softmax with a lazy maximum: the tile's probabilities are
+        // formed against the running maximum without taking the tile's own
+        // maximum first.  Only when some lane's share of a row sum leaves
+        // [0, 2^kLazyLog2] (the first visible tile of a row, where the running
+        // maximum is still -FLT_MAX and P overflows, or scores that grew by more
+        // than kLazyLog2 in the exp2 domain) is the tile redone with its exact
+        // maximum: S again (K is still staged), the maximum over both key halves
+        // (IEEE maximum, the other 32 keys of a row sit in lane ^ 32), O and l
+        // rescaled, P again.  In between P may exceed 1 by up to 2^kLazyLog2,
+        // which bf16 and the fp32 sums carry without loss of relative precision.
+        scores();
+        probs();
+        if (__any(!(lsum <= kLazyMax))) {
+          scores();
+          float mloc = __builtin_elementwise_maximum(s[0][0], s[0][1]);
+#pragma unroll
+          for (int r = 2; r < 16; r += 2)
+            mloc = __builtin_elementwise_maximum(mloc, __builtin_elementwise_maximum(s[0][r], s[0][r + 1]));
+#pragma unroll
+          for (int r = 0; r < 16; r += 2)
+            mloc = __builtin_elementwise_maximum(mloc, __builtin_elementwise_maximum(s[1][r], s[1][r + 1]));
+          const float m_new = fmaxf(m_run, pair_max(mloc));
           const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
           m_run = m_new;
           l_run *= alpha;
 #pragma unroll
           for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+          probs();
         }
-        const float mneg = -m_run * c;
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-          for (int tp = 0; tp < 2; ++tp) {
-            f32x8 pv;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][8 * tp + j], c, mneg));
-            pf[kh * 2 + tp] = __builtin_convertvector(pv, bf16x8);
-          }
-        }
-        const bf16x2 one2 = bf16x2{(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][2 * j], pf[ks][2 * j + 1]}, one2,
-                                                    l_run, false);
+        l_run += lsum;
       }
       // V(i) landed (K(i+1) and its intervals may still be in flight).
       if (more) wait_vmcnt<G::LOADS + 1>();

@@ -48,17 +48,18 @@ __global__ void __launch_bounds__(256) k_classify_intervals(const int32_t* iv, i
   }
 }
 
-// The same rule with one wave per (mask, key tile, 64 query tiles) when the
-// tile is 64 keys wide: lane = key column, whose intervals are read once; per
-// query tile two ballots give "every column fully masked" (SKIP) and "no
-// column masked" (FULL), and lane qt % 64 keeps that tile's state for one
-// store at the end.
+// The same rule with one wave per (mask, key tile, kQtPerWave query tiles)
+// when the tile is 64 keys wide: lane = key column, whose intervals are read
+// once; per query tile two ballots give "every column fully masked" (SKIP) and
+// "no column masked" (FULL), and lane qt % kQtPerWave keeps that tile's state
+// for one store at the end.
+constexpr int kQtPerWave = 16;
 __global__ void __launch_bounds__(256) k_classify_intervals_cols(const int32_t* iv, int32_t nmask, int32_t sq,
                                                                  int32_t skv, int32_t bm, int32_t nqt, int32_t nkt,
                                                                  uint8_t* state) {
   const int lane = threadIdx.x & 63;
   const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int32_t nqg = (nqt + 63) / 64;
+  const int32_t nqg = (nqt + kQtPerWave - 1) / kQtPerWave;
   if (wv >= (int64_t)nmask * nkt * nqg) return;
   const int32_t qg = (int32_t)(wv % nqg);
   const int32_t kt = (int32_t)((wv / nqg) % nkt);
@@ -68,13 +69,20 @@ __global__ void __launch_bounds__(256) k_classify_intervals_cols(const int32_t* 
   const int32_t* c = iv + m * 4 * (int64_t)skv;
   const int32_t us = col ? c[j] : 0, ue = col ? c[skv + j] : 0;
   const int32_t ls = col ? c[2 * (int64_t)skv + j] : 0, le = col ? c[3 * (int64_t)skv + j] : 0;
+  // Rows [r0, r1) of a column are all masked iff they lie inside one of its
+  // runs (canonical runs neither overlap nor abut), and none is masked iff
+  // neither (non-empty) run meets them: comparisons only, combined as lane masks.
+  const uint64_t cols = __ballot(col);
+  const uint64_t ne_u = __ballot(us < ue), ne_l = __ballot(ls < le);  // non-empty runs
   uint8_t mine = FMASK_SKIP;
-  const int32_t q0 = qg * 64, q1 = min(nqt, q0 + 64);
+  const int32_t q0 = qg * kQtPerWave, q1 = min(nqt, q0 + kQtPerWave);
   for (int32_t qt = q0; qt < q1; ++qt) {
     const int32_t r0 = qt * bm, r1 = min(sq, r0 + bm);
-    const int32_t mc = overlap(r0, r1, us, ue) + overlap(r0, r1, ls, le);
-    const bool all_masked = __ballot(col && mc != r1 - r0) == 0ull;
-    const bool none_masked = __ballot(col && mc != 0) == 0ull;
+    // (one compare per ballot: the masks combine on the scalar unit)
+    const uint64_t inside = (__ballot(us <= r0) & __ballot(r1 <= ue)) | (__ballot(ls <= r0) & __ballot(r1 <= le));
+    const uint64_t meets = (ne_u & __ballot(us < r1) & __ballot(r0 < ue)) | (ne_l & __ballot(ls < r1) & __ballot(r0 < le));
+    const bool all_masked = (inside & cols) == cols;
+    const bool none_masked = (meets & cols) == 0ull;
     const uint8_t st = all_masked ? FMASK_SKIP : (none_masked ? FMASK_FULL : FMASK_PARTIAL);
     if (lane == qt - q0) mine = st;
   }
@@ -118,14 +126,24 @@ __global__ void __launch_bounds__(256) k_tile_lists(const uint8_t* state, int32_
   const uint8_t* st = state + (int64_t)row * nkt;
   int32_t* out = list + (int64_t)row * nkt;
   int running = 0;
-  for (int base = 0; base < nkt; base += 64) {
-    int kt = base + lane;
-    uint8_t s = kt < nkt ? st[kt] : (uint8_t)FMASK_SKIP;
-    bool keep = s != FMASK_SKIP;
-    uint64_t bal = __ballot(keep);
-    int rank = running + __popcll(bal & ((1ull << lane) - 1ull));
-    if (keep) out[rank] = (int32_t)((uint32_t)kt | (s == FMASK_FULL ? FMASK_LIST_FULL_BIT : 0u));
-    running += __popcll(bal);
+  // the states of up to 512 tiles loaded at once (8 per lane), then compacted
+  // 64 at a time
+  for (int base0 = 0; base0 < nkt; base0 += 512) {
+    uint8_t sv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int kt = base0 + 64 * k + lane;
+      sv[k] = kt < nkt ? st[kt] : (uint8_t)FMASK_SKIP;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int kt = base0 + 64 * k + lane;
+      const bool keep = sv[k] != FMASK_SKIP;
+      const uint64_t bal = __ballot(keep);
+      const int rank = running + __popcll(bal & ((1ull << lane) - 1ull));
+      if (keep) out[rank] = (int32_t)((uint32_t)kt | (sv[k] == FMASK_FULL ? FMASK_LIST_FULL_BIT : 0u));
+      running += __popcll(bal);
+    }
   }
   for (int i = running + lane; i < nkt; i += 64) out[i] = 0;
   if (lane == 0) count[row] = running;
@@ -159,25 +177,28 @@ __global__ void __launch_bounds__(256) k_tile_cols(const uint8_t* state, int32_t
 // is unique, so order[rank] = row is a permutation.
 __global__ void __launch_bounds__(256) k_tile_order(const int32_t* count, int32_t rows,
                                                     int32_t* order) {
-  __shared__ __attribute__((aligned(16))) int32_t chunk[1024];
-  int x = blockIdx.x * blockDim.x + threadIdx.x;
-  int32_t cx = x < rows ? count[x] : 0;
+  // Row y's key count[y] * 2^32 + (2^32 - 1 - y): the rank of row x is the
+  // number of larger keys (longer rows first, ties by index), one 64-bit
+  // compare per row.
+  __shared__ __attribute__((aligned(16))) uint64_t key[512];
+  const int x = blockIdx.x * blockDim.x + threadIdx.x;
+  auto key_of = [](int32_t c, int y) -> uint64_t { return ((uint64_t)(uint32_t)c << 32) | (uint32_t)(~y); };
+  const uint64_t kx = x < rows ? key_of(count[x], x) : 0ull;
   int rank = 0;
-  for (int base = 0; base < rows; base += 1024) {
+  for (int base = 0; base < rows; base += 512) {
     __syncthreads();
-    for (int i = threadIdx.x; i < 1024; i += blockDim.x)
-      chunk[i] = base + i < rows ? count[base + i] : -1;
-    __syncthreads();
-    // four counts per LDS read (the stage is padded with -1, below any count)
-    const int lim4 = (min(1024, rows - base) + 3) / 4;
-    const i32x4* c4 = (const i32x4*)chunk;
-#pragma unroll 4
-    for (int i = 0; i < lim4; ++i) {
-      const i32x4 cy = c4[i];
-      const int y = base + 4 * i;
+    uint64_t v[2];  // both loads in flight before the stores; padding keys are 0
 #pragma unroll
-      for (int k = 0; k < 4; ++k) rank += (cy[k] > cx) || (cy[k] == cx && y + k < x);
+    for (int k = 0; k < 2; ++k) {
+      const int y = base + threadIdx.x + 256 * k;
+      v[k] = y < rows ? key_of(count[y], y) : 0ull;
     }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) key[threadIdx.x + 256 * k] = v[k];
+    __syncthreads();
+    const int lim = min(512, rows - base);
+#pragma unroll 8
+    for (int i = 0; i < lim; ++i) rank += key[i] > kx;
   }
   if (x < rows) order[rank] = x;
 }
@@ -197,7 +218,7 @@ hipError_t launch_classify_intervals(const int32_t* iv, int32_t nmask, int32_t s
   int64_t total = (int64_t)nmask * nqt * nkt;
   if (total <= 0) return hipSuccess;
   if (bn == 64) {
-    const int64_t waves = (int64_t)nmask * nkt * ((nqt + 63) / 64);
+    const int64_t waves = (int64_t)nmask * nkt * ((nqt + kQtPerWave - 1) / kQtPerWave);
     if ((waves + 3) / 4 <= INT32_MAX) {
       hipLaunchKernelGGL(k_classify_intervals_cols, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, iv, nmask,
                          sq, skv, bm, nqt, nkt, state);

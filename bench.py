@@ -74,7 +74,7 @@ def visible_pairs_bitmap(torch, enc):
     return n_full + part.reshape(e.batch, e.heads)
 
 
-def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5):
+def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5, graph=False):
     w = synth.workload(name)
     q, k, v = (_bf16(torch, a) if w["dtype"] == "bf16" else torch.from_numpy(a).cuda()
                for a in synth.draw_qkv(w))
@@ -119,6 +119,28 @@ def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5):
         enc, tiles = step(evs[i])
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
+    eager_wall = wall
+    if graph:
+        # The same step captured once as a HIP graph and replayed: every replay
+        # runs the encoder, classifier and attention kernels again; only the
+        # host's launch work between them is gone.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(max(warmup, 3)):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
     t_enc = np.mean([a[0].elapsed_time(a[1]) for a in evs])
     t_cls = np.mean([a[1].elapsed_time(a[2]) for a in evs])
     att = [a[2].elapsed_time(a[3]) for a in evs]
@@ -126,7 +148,8 @@ def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5):
 
     rec = dict(workload=name, B=w["B"], Hq=w["Hq"], Hkv=w["Hkv"], Sq=w["Sq"], Skv=w["Skv"], D=w["D"],
                dtype=w["dtype"], ms_per_step=wall * 1e3, encode_ms=float(t_enc),
-               classify_ms=float(t_cls), attn_ms=float(t_att),
+               classify_ms=float(t_cls), attn_ms=float(t_att), eager_ms_per_step=eager_wall * 1e3,
+               step_launch="hip graph replay" if graph else "eager",
                attn_ms_median=float(np.median(att)), attn_ms_min=float(np.min(att)))
     if selected:
         ls, cn = enc.lists()
@@ -329,6 +352,8 @@ def main():
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the 32K causal-document step (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step as one captured HIP graph instead of launching its calls eagerly")
     ap.add_argument("--cpu-rows", type=int, default=32768)
     ap.add_argument("--min-warmup-s", type=float, default=0.5,
                     help="warm up for at least this long (clocks settle); 0 for counter runs")
@@ -359,13 +384,18 @@ def main():
     if args.backward_only:
         print(json.dumps(time_backward(torch, fm, synth, "causal_doc_32k", args.steps, args.warmup)))
         return
-    head = time_workload(torch, fm, synth, "causal_doc_32k", args.steps, args.warmup, args.min_warmup_s)
+    # (--graph: steps of mask families whose encoder records kernel launches
+    # only are replayed as one HIP graph; on this stack that measured slower
+    # than launching them eagerly, so eager is the default.)
+    graphable = {"causal_doc_32k", "causal_doc_8k", "shared_question_32k", "band_32k", "band_neg_4k"}
+    head = time_workload(torch, fm, synth, "causal_doc_32k", args.steps, args.warmup, args.min_warmup_s,
+                         graph=args.graph)
     others = []
     if not args.headline_only:
         for name in ("causal_doc_8k", "shared_question_32k", "band_32k", "band_neg_4k", "varlen_prefill_32k",
                      "block_bitmap_16k", "tree_4k", "selected_key_128k"):
             others.append(time_workload(torch, fm, synth, name, max(3, args.steps // 2), 2,
-                                        min(0.2, args.min_warmup_s)))
+                                        min(0.2, args.min_warmup_s), graph=name in graphable and args.graph))
             torch.cuda.empty_cache()
         for name in ("causal_doc_8k", "causal_doc_32k"):
             others.append(time_backward(torch, fm, synth, name, max(3, args.steps // 4), 2))
@@ -389,7 +419,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) Q/K/V, seeded document lengths)",
-        "config": {"workload": "causal_document_32k", "batch": 1, "q_heads": 32, "kv_heads": 8,
+        "config": {"workload": "causal_document_32k", "step_launch": head["step_launch"],
+                   "eager_ms_per_step": head["eager_ms_per_step"], "batch": 1, "q_heads": 32, "kv_heads": 8,
                    "seq_len": 32768, "head_dim": 128, "doc_lengths": head["doc_lengths"],
                    "visible_pairs": head["visible_pairs"]},
         "fraction_of_peak": head["effective_tflops"] / PEAK_BF16_TFLOPS,

@@ -491,7 +491,7 @@ fmask_status fmask_encode(const fmask_mask_desc* desc, void* out, size_t out_byt
     enc->nbk = L.nbk;
     enc->pool_cap = L.cap;
     if (L.nbq * L.nbk == 0) {
-      e = hipMemsetAsync(o.pool_count, 0, sizeof(int32_t), s);
+      e = launch_zero_int(o.pool_count, s);
       return hip_status(e, "clear pool count");
     }
     e = launch_encode_bitmap(src, o, s);

@@ -549,6 +549,11 @@ hipError_t launch_encode_bitmap(const BitmapSrc& src, const BitmapOut& out, hipS
   return hipGetLastError();
 }
 
+hipError_t launch_zero_int(int32_t* x, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero_int, dim3(1), dim3(1), 0, s, x);
+  return hipGetLastError();
+}
+
 hipError_t launch_encode_dense_intervals(const uint8_t* dense, int32_t nmask, int32_t sq, int32_t skv,
                                          void* ws, int32_t* iv, int32_t* bad, hipStream_t s) {
   hipLaunchKernelGGL(k_zero_int, dim3(1), dim3(1), 0, s, bad);

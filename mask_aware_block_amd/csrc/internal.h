@@ -36,6 +36,8 @@ struct SegParams {
 hipError_t launch_encode_family_intervals(const SegParams& p, int32_t* iv, hipStream_t s);
 hipError_t launch_encode_raw_intervals(const int32_t* raw, int32_t nmask, int32_t sq, int32_t skv,
                                        int32_t* iv, hipStream_t s);
+// *x = 0 by a one-thread kernel (a fill a captured HIP graph replays correctly).
+hipError_t launch_zero_int(int32_t* x, hipStream_t s);
 hipError_t launch_tree_hi(const int32_t* parent, int32_t n, int32_t* hi, hipStream_t s);
 
 // Source of the 64-bit row words of a 64 x 64 block, for the bitmap encoder.

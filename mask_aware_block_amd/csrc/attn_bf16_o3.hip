@@ -21,6 +21,7 @@
 //   wave state of tile i (SKIP / FULL / PARTIAL for its 32 rows); QK; mask; softmax
 //   wait V(i); barrier; PV(i)
 //   wait for everything; barrier
+// and at the end O goes out through LDS (whole 128-byte row pieces per store).
 #include <float.h>
 
 #include "device_util.h"
@@ -380,6 +381,18 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
         // rescaled, P again.  In between P may exceed 1 by up to 2^kLazyLog2,
         // which bf16 and the fp32 sums carry without loss of relative precision.
         scores();
+        if (i == 0) {
+          // first tile of the row: start from its exact maximum (O and l are
+          // still zero), so that the lazy attempt below holds
+          float mloc = __builtin_elementwise_maximum(s[0][0], s[0][1]);
+#pragma unroll
+          for (int r = 2; r < 16; r += 2)
+            mloc = __builtin_elementwise_maximum(mloc, __builtin_elementwise_maximum(s[0][r], s[0][r + 1]));
+#pragma unroll
+          for (int r = 0; r < 16; r += 2)
+            mloc = __builtin_elementwise_maximum(mloc, __builtin_elementwise_maximum(s[1][r], s[1][r + 1]));
+          m_run = fmaxf(m_run, pair_max(mloc));
+        }
         probs();
         if (__any(!(lsum <= kLazyMax))) {
           scores();
@@ -432,24 +445,38 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
     }
   }
 
-  // Epilogue: O = O / l, zero rows for l = 0, LSE in natural log.
+  // Epilogue: O = O / l (zero rows for l = 0), staged through LDS so that
+  // every store writes 16-byte pieces of whole 128-byte row segments; LSE in
+  // natural log.  Each wave stages 32 rows x 64 columns at a time in its own
+  // 4 KB of the K buffers, which no wave reads any more.
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qrow < p.sq) {
-    __bf16* O = (__bf16*)p.o + it.b * p.os[0] + it.h * p.os[1] + qrow * p.os[2];
+  {
+    char* stg = smem + G::K0 + w * 4096;
+    __bf16* Ob = (__bf16*)p.o + it.b * p.os[0] + it.h * p.os[1];
+    const int rr = lane >> 3, ch = lane & 7;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int rd = 0; rd < D / 64; ++rd) {
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d0 = db * 32 + 8 * rg + 4 * half;
-        f32x4 x = f32x4{acc[db][4 * rg], acc[db][4 * rg + 1], acc[db][4 * rg + 2], acc[db][4 * rg + 3]} * inv;
-        *(bf16x4*)(O + d0) = __builtin_convertvector(x, bf16x4);
+      for (int dh = 0; dh < 2; ++dh) {
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int db = 2 * rd + dh, cc = dh * 4 + rg;
+          f32x4 x = f32x4{acc[db][4 * rg], acc[db][4 * rg + 1], acc[db][4 * rg + 2], acc[db][4 * rg + 3]} * inv;
+          *(bf16x4*)(stg + l32 * 128 + ((cc ^ (l32 & 7)) * 16) + half * 8) = __builtin_convertvector(x, bf16x4);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int row = 8 * k + rr;
+        const bf16x8 v = *(const bf16x8*)(stg + row * 128 + ((ch ^ (row & 7)) * 16));
+        if (r0 + row < p.sq) *(bf16x8*)(Ob + (int64_t)(r0 + row) * p.os[2] + rd * 64 + ch * 8) = v;
       }
     }
-    if (p.lse && half == 0) {
-      const float lse = l_tot > 0.f ? m_run * p.scale + logf(l_tot) : -INFINITY;
-      p.lse[((int64_t)it.b * p.hq + it.h) * p.sq + qrow] = lse;
-    }
+  }
+  if (qrow < p.sq && p.lse && half == 0) {
+    const float lse = l_tot > 0.f ? m_run * p.scale + logf(l_tot) : -INFINITY;
+    p.lse[((int64_t)it.b * p.hq + it.h) * p.sq + qrow] = lse;
   }
 #endif
 }

@@ -26,6 +26,16 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
+# Per-source additions.  attn_bwd.hip: its dK/dV kernel runs one wave per SIMD
+# with more than 256 registers live; left to its heuristics the compiler gives
+# every MFMA of that kernel accumulator-register (AGPR) operands and then
+# copies the scores to VGPRs for the VALU and the gradients back and forth
+# (about 700 v_accvgpr moves per launch of the loop body).  VGPR-form MFMAs
+# leave 44 such moves and run the backward about 5% faster, bit-identically.
+PER_FILE = {
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
@@ -33,7 +43,7 @@ def sources():
 
 def _compile(src, extra):
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *PER_FILE.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

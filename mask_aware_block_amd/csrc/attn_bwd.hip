@@ -286,12 +286,18 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdParams p, int expand, int 
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
               const int r = 8 * tp + j;
-              float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][r], c, -lse2));
-              if (need_mask) {
-                const int kl = kh * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                if ((rmask[kl] >> l32) & 1u) pr = 0.f;
-              }
+              const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][r], c, -lse2));
               x[j] = pr * (dp[kh][r] - dlt);
+            }
+            // element masks of a PARTIAL tile in one pass (one uniform branch,
+            // not one per element; a masked value is replaced, whatever it was)
+            if (need_mask) {
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const int r = 8 * tp + j;
+                const int kl = kh * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                x[j] = ((rmask[kl] >> l32) & 1u) ? 0.f : x[j];
+              }
             }
             dsf[kh * 2 + tp] = __builtin_convertvector(x, bf16x8);
           }
@@ -511,15 +517,21 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
 #pragma unroll
               for (int q4 = 0; q4 < 4; ++q4) {
                 const int r = 8 * tp + 4 * j4 + q4;
-                float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -ll[q4]));
-                if (!full) {
-                  const int grow = qt * BM + rl + q4;
-                  const bool masked = ((uint32_t)(grow - us) < (uint32_t)(ue - us)) ||
-                                      ((uint32_t)(grow - ls) < (uint32_t)(le - ls)) || grow >= p.sq;
-                  if (masked) pr = 0.f;
-                }
+                const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -ll[q4]));
                 xp[4 * j4 + q4] = pr;
                 xs[4 * j4 + q4] = pr * (dp[r] - dl[q4]);
+              }
+            }
+            // element masks of a PARTIAL tile, in one pass over the 8 values
+            // (one uniform branch rather than one per element)
+            if (!full) {
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const int grow = qt * BM + lr0 + 8 * (2 * tp + j / 4) + 4 * half + j % 4;
+                const bool masked = ((uint32_t)(grow - us) < (uint32_t)(ue - us)) ||
+                                    ((uint32_t)(grow - ls) < (uint32_t)(le - ls)) || grow >= p.sq;
+                xp[j] = masked ? 0.f : xp[j];
+                xs[j] = masked ? 0.f : xs[j];
               }
             }
             pb[tp] = __builtin_convertvector(xp, bf16x8);

@@ -42,6 +42,7 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 constexpr int BN = 64;    // keys per tile
 constexpr int BM = 128;   // query rows per tile
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kAhead = 3;  // dK/dV kernel: operand fragments read ahead of their MFMA
 
 // 16-byte chunk swizzle serving both access patterns: 16 consecutive rows
 // read at one logical chunk hit 16 distinct (bank) positions, and the four
@@ -491,16 +492,27 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           const int lr0 = rw * 64 + rb * 32;  // first tile row of this block
+          // S = Q K^T, then dP = dO V^T: 2 KT MFMAs, each A fragment read
+          // kAhead MFMAs ahead into a ring of registers (one wave per SIMD:
+          // nothing else hides the LDS latency)
           f32x16 s = f32x16{}, dp = f32x16{};
+          {
+            auto frag = [&](int n) INLINE -> bf16x8 {
+              const char* tb = n < KT ? qb : ob;
+              return *(const bf16x8*)(tb + chunk_off<D>(lr0 + l32, 2 * (n % KT) + half));
+            };
+            bf16x8 fr[kAhead];
 #pragma unroll
-          for (int t = 0; t < KT; ++t) {
-            const bf16x8 aq = *(const bf16x8*)(qb + chunk_off<D>(lr0 + l32, 2 * t + half));
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[t], s, 0, 0, 0);
-          }
+            for (int n = 0; n < kAhead; ++n) fr[n] = frag(n);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int t = 0; t < KT; ++t) {
-            const bf16x8 ao = *(const bf16x8*)(ob + chunk_off<D>(lr0 + l32, 2 * t + half));
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[t], dp, 0, 0, 0);
+            for (int n = 0; n < 2 * KT; ++n) {
+              const bf16x8 a = fr[n % kAhead];
+              if (n < KT) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[n], s, 0, 0, 0);
+              else dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[n - KT], dp, 0, 0, 0);
+              if (n + kAhead < 2 * KT) fr[n % kAhead] = frag(n + kAhead);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
           // P, dS: lane = key, rows lr0 + 8 (r / 4) + 4 half + r % 4
           bf16x8 pb[2], sb[2];
@@ -538,14 +550,25 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
             sb[tp] = __builtin_convertvector(xs, bf16x8);
           }
           // dV^T += dO^T P,  dK^T += Q^T dS  (contraction over the 32 rows)
+          // (MFMA m: db = m / 4, ks = m / 2 % 2, dV for even m and dK for odd
+          // m; its transposed fragment read kAhead MFMAs ahead)
+          {
+            auto frag = [&](int m) INLINE -> bf16x8 {
+              const int db = m / 4, ks = (m / 2) % 2;
+              return tr_frag<D>((m & 1) ? qb : ob, lr0 + 16 * ks, tlo[db], thi[db]);
+            };
+            bf16x8 fr[kAhead];
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
+            for (int m = 0; m < kAhead; ++m) fr[m] = frag(m);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-              const bf16x8 ao = tr_frag<D>(ob, lr0 + 16 * ks, tlo[db], thi[db]);
-              dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb[ks], dv[db], 0, 0, 0);
-              const bf16x8 aq = tr_frag<D>(qb, lr0 + 16 * ks, tlo[db], thi[db]);
-              dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb[ks], dk[db], 0, 0, 0);
+            for (int m = 0; m < 4 * DB; ++m) {
+              const int db = m / 4, ks = (m / 2) % 2;
+              const bf16x8 a = fr[m % kAhead];
+              if (m & 1) dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[ks], dk[db], 0, 0, 0);
+              else dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], dv[db], 0, 0, 0);
+              if (m + kAhead < 4 * DB) fr[m % kAhead] = frag(m + kAhead);
+              __builtin_amdgcn_sched_barrier(0);
             }
           }
         }

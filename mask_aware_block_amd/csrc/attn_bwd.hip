@@ -42,7 +42,7 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 constexpr int BN = 64;    // keys per tile
 constexpr int BM = 128;   // query rows per tile
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kAhead = 3;  // dK/dV kernel: operand fragments read ahead of their MFMA
+constexpr int kAhead = 3;  // operand fragments read ahead of their MFMA
 
 // 16-byte chunk swizzle serving both access patterns: 16 consecutive rows
 // read at one logical chunk hit 16 distinct (bank) positions, and the four
@@ -260,21 +260,29 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdParams p, int expand, int 
         need_mask = __ballot((mk & valid) != 0u) != 0ull;
       }
       if (!skip) {
+        // S^T = K Q^T and dP^T = V dO^T for the two 32-key halves: MFMA n is
+        // key half n / 2 KT, S for n / KT even, dP for odd; its K or V
+        // fragment is read kAhead MFMAs ahead into a ring of registers
         f32x16 s[2], dp[2];
+        {
+          auto frag = [&](int n) INLINE -> bf16x8 {
+            const int kh = n / (2 * KT), t = n % KT;
+            return *(const bf16x8*)(((n / KT) & 1 ? vb : kb) + chunk_off<D>(kh * 32 + l32, 2 * t + half));
+          };
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          s[kh] = f32x16{};
-          dp[kh] = f32x16{};
-          const int key = kh * 32 + l32;
+          for (int kh = 0; kh < 2; ++kh) s[kh] = dp[kh] = f32x16{};
+          bf16x8 fr[kAhead];
 #pragma unroll
-          for (int t = 0; t < KT; ++t) {
-            const bf16x8 a = *(const bf16x8*)(kb + chunk_off<D>(key, 2 * t + half));
-            s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kh], 0, 0, 0);
-          }
+          for (int n = 0; n < kAhead; ++n) fr[n] = frag(n);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int t = 0; t < KT; ++t) {
-            const bf16x8 a = *(const bf16x8*)(vb + chunk_off<D>(key, 2 * t + half));
-            dp[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, df[t], dp[kh], 0, 0, 0);
+          for (int n = 0; n < 4 * KT; ++n) {
+            const int kh = n / (2 * KT), t = n % KT;
+            const bf16x8 a = fr[n % kAhead];
+            if ((n / KT) & 1) dp[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, df[t], dp[kh], 0, 0, 0);
+            else s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kh], 0, 0, 0);
+            if (n + kAhead < 4 * KT) fr[n % kAhead] = frag(n + kAhead);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
         // P^T and dS^T (key slots in the order the PV-style operand expects)
@@ -303,13 +311,18 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdParams p, int expand, int 
             dsf[kh * 2 + tp] = __builtin_convertvector(x, bf16x8);
           }
         }
-        // dQ^T += K^T dS^T
+        // dQ^T += K^T dS^T (MFMA m: db = m / 4, ks = m % 4; fragments read ahead)
+        {
+          auto frag = [&](int m) INLINE -> bf16x8 { return tr_frag<D>(kb, 16 * (m % 4), tlo[m / 4], thi[m / 4]); };
+          bf16x8 fr[kAhead];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+          for (int m = 0; m < kAhead; ++m) fr[m] = frag(m);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 a = tr_frag<D>(kb, 16 * ks, tlo[db], thi[db]);
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[ks], acc[db], 0, 0, 0);
+          for (int m = 0; m < 4 * DB; ++m) {
+            acc[m / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m % kAhead], dsf[m % 4], acc[m / 4], 0, 0, 0);
+            if (m + kAhead < 4 * DB) fr[m % kAhead] = frag(m + kAhead);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }

@@ -373,9 +373,10 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
         // Online softmax with a lazy maximum: the tile's probabilities are
         // formed against the running maximum without taking the tile's own
         // maximum first.  Only when some lane's share of a row sum leaves
-        // [0, 2^kLazyLog2] (the first visible tile of a row, where the running
-        // maximum is still -FLT_MAX and P overflows, or scores that grew by more
-        // than kLazyLog2 in the exp2 domain) is the tile redone with its exact
+        // [0, 2^kLazyLog2] (a row's first visible tile when that is not the
+        // wave's first tile, so that the running maximum is still -FLT_MAX and
+        // P overflows, or scores that grew by more than kLazyLog2 in the exp2
+        // domain) is the tile redone with its exact
         // maximum: S again (K is still staged), the maximum over both key halves
         // (IEEE maximum, the other 32 keys of a row sit in lane ^ 32), O and l
         // rescaled, P again.  In between P may exceed 1 by up to 2^kLazyLog2,

@@ -20,7 +20,10 @@
 // Tiles whose rows and keys a wave does not see at all are skipped per wave;
 // FULL tiles run without element masks.  Operand fragments that are read
 // both row-wise (16-byte reads) and transposed (ds_read_b64_tr_b16) live in
-// LDS under a swizzle that keeps both access patterns free of bank conflicts.
+// LDS under a swizzle that keeps both access patterns free of bank conflicts,
+// and every MFMA operand read from LDS is read kAhead MFMAs ahead into a ring
+// of registers (the dK/dV kernel runs one wave per SIMD, so nothing else hides
+// the LDS latency).  The file is compiled with VGPR-form MFMAs (build.py).
 #include <float.h>
 
 #include "device_util.h"

@@ -230,9 +230,13 @@ __global__ void __launch_bounds__(D) k_selected_combine(SelAttnParams p, int nsp
   const float c = p.scale * kLog2e;
   const size_t stride = (size_t)G * (D + 2);
   const float* base = ws + item * nsplit * stride;
+  // (the loops are unrolled so that eight splits' loads are in flight at once
+  // rather than one latency per split)
   float M = -FLT_MAX;
+#pragma unroll 8
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[s * stride + g]);
   float L = 0.f, acc_o = 0.f;
+#pragma unroll 8
   for (int s = 0; s < nsplit; ++s) {
     const float f = __builtin_amdgcn_exp2f((base[s * stride + g] - M) * c);
     L += base[s * stride + G + g] * f;

@@ -90,6 +90,29 @@ def test_small_families(dtype, D, S, K):
         _dense_check(w, spec, f"{spec['family']} {dtype} d{D} {S}x{K}")
 
 
+@pytest.mark.parametrize("family", ["causal", "causal_document"])
+def test_running_maximum_jumps(family):
+    """Scores that grow from key tile to key tile by far more than the lazy
+    bound (q.k rises by about 300, i.e. 38 in the exp2 domain, per 64 keys), so
+    that the kernel's lazy maximum overflows and redoes the tile with its exact
+    maximum on every tile after a row's first, and rescales O and l each time."""
+    S, D = 512, 128
+    w = _small("bf16", D, S, S, Hq=4, Hkv=2)
+    rng = np.random.default_rng(5)
+    u = np.ones(D, np.float32)
+    q = (u + 0.1 * rng.standard_normal((1, 4, S, D))).astype(np.float32)
+    tile = (np.arange(S) // 64).astype(np.float32)
+    k = (rng.standard_normal((1, 2, S, D)) + (300.0 / D) * tile[None, None, :, None] * u).astype(np.float32)
+    v = rng.standard_normal((1, 2, S, D)).astype(np.float32)
+    arrays = tuple(synth._f32_to_bf16_bits(a) for a in (q, k, v))
+    spec = (dict(family="causal", sq=S, skv=S) if family == "causal" else
+            dict(family="causal_document", sq=S, skv=S, cu_seg=np.array([0, 200, 330, S], np.int32)))
+    o, lse = _run(w, arrays, spec)
+    qd, kd, vd = (to_f64(w, a) for a in arrays)
+    ro, rl = OA.attention_dense(qd, kd, vd, OA.spec_vis_fn(spec), w["scale"])
+    compare(w, o, lse, ro, rl, f"running maximum jumps, {family}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_small_bitmap_and_raw_intervals(dtype):
     S, K = 320, 260

@@ -90,7 +90,7 @@ def test_small_families(dtype, D, S, K):
         _dense_check(w, spec, f"{spec['family']} {dtype} d{D} {S}x{K}")
 
 
-@pytest.mark.parametrize("family", ["causal", "causal_document"])
+@pytest.mark.parametrize("family", ["causal", "causal_document", "tree"])
 def test_running_maximum_jumps(family):
     """Scores that grow from key tile to key tile by far more than the lazy
     bound (q.k rises by about 300, i.e. 38 in the exp2 domain, per 64 keys), so
@@ -105,8 +105,13 @@ def test_running_maximum_jumps(family):
     k = (rng.standard_normal((1, 2, S, D)) + (300.0 / D) * tile[None, None, :, None] * u).astype(np.float32)
     v = rng.standard_normal((1, 2, S, D)).astype(np.float32)
     arrays = tuple(synth._f32_to_bf16_bits(a) for a in (q, k, v))
-    spec = (dict(family="causal", sq=S, skv=S) if family == "causal" else
-            dict(family="causal_document", sq=S, skv=S, cu_seg=np.array([0, 200, 330, S], np.int32)))
+    if family == "causal":
+        spec = dict(family="causal", sq=S, skv=S)
+    elif family == "causal_document":
+        spec = dict(family="causal_document", sq=S, skv=S, cu_seg=np.array([0, 200, 330, S], np.int32))
+    else:  # bitmap encoding
+        spec = dict(family="tree", sq=S, skv=S, tree_prefix=S - 64,
+                    tree_parent=synth.random_tree(np.random.default_rng(3), 64, order="bfs"))
     o, lse = _run(w, arrays, spec)
     qd, kd, vd = (to_f64(w, a) for a in arrays)
     ro, rl = OA.attention_dense(qd, kd, vd, OA.spec_vis_fn(spec), w["scale"])

@@ -556,8 +556,9 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
 #pragma unroll
               for (int j = 0; j < 8; ++j) {
                 const int grow = qt * BM + lr0 + 8 * (2 * tp + j / 4) + 4 * half + j % 4;
-                const bool masked = ((uint32_t)(grow - us) < (uint32_t)(ue - us)) ||
-                                    ((uint32_t)(grow - ls) < (uint32_t)(le - ls)) || grow >= p.sq;
+                // (| rather than ||: three compares, no branches)
+                const bool masked = ((uint32_t)(grow - us) < (uint32_t)(ue - us)) |
+                                    ((uint32_t)(grow - ls) < (uint32_t)(le - ls)) | (grow >= p.sq);
                 xp[j] = masked ? 0.f : xp[j];
                 xs[j] = masked ? 0.f : xs[j];
               }

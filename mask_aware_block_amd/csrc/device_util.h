@@ -31,22 +31,25 @@ __device__ inline int lds_addr(const void* p) {
 // compiler's wait counting does not see them: it neither orders later LDS
 // reads behind them nor drains them when waiting for an ordinary load.  The
 // kernels make the data visible themselves (vmcnt wait, then a barrier).
-// `lds` is the LDS byte address (see lds_addr), wave-uniform.
+// `lds` is the LDS byte address (see lds_addr), wave-uniform.  A scalar write
+// of M0 needs one wait state before a load with the LDS bit reads it (the
+// compiler pads only the code it generates, not inline assembly), hence the
+// s_nop between the two.
 __device__ inline void dma16(rsrc_t r, int voff, int lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(lds), "v"(voff), "s"(r)
                : "memory", "m0");
 }
 // Same, with a wave-uniform byte offset added through the scalar offset field.
 __device__ inline void dma16s(rsrc_t r, int voff, int soff, int lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(lds), "v"(voff), "s"(r), "s"(soff)
                : "memory", "m0");
 }
 __device__ inline void dma4(rsrc_t r, int voff, int lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :
                : "s"(lds), "v"(voff), "s"(r)
                : "memory", "m0");

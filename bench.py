@@ -363,6 +363,8 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="replay each step as one captured HIP graph instead of launching its calls eagerly")
     ap.add_argument("--cpu-rows", type=int, default=32768)
+    ap.add_argument("--cpu-heads", type=int, default=3,
+                    help="query heads of the CPU-baseline sample (about 5 s of oracle work each)")
     ap.add_argument("--min-warmup-s", type=float, default=0.5,
                     help="warm up for at least this long (clocks settle); 0 for counter runs")
     ap.add_argument("--copy-probe", action="store_true",
@@ -440,7 +442,7 @@ def main():
         "workloads": others,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(synth, "causal_doc_32k", args.cpu_rows, 1)
+        out["cpu_baseline"] = cpu_baseline(synth, "causal_doc_32k", args.cpu_rows, args.cpu_heads)
     print(json.dumps(out))
 
 

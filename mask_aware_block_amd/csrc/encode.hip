@@ -215,16 +215,20 @@ typedef int32_t dense_x4 __attribute__((ext_vector_type(4)));
 __device__ dense_x4 dense_load16(rsrc_t rsrc, int voffset, int soffset, int aux) __asm("llvm.amdgcn.raw.buffer.load.v4i32");
 __device__ uint32_t write_lane(uint32_t value, uint32_t lane, uint32_t old) __asm("llvm.amdgcn.writelane.i32");
 
-// One workgroup (16 waves) per (mask, 64-column strip); lane = column in the
+// One workgroup (16 waves) per (mask, column strip); lane = column in the
 // end.  Wave w walks its own contiguous share of the rows 64 at a time,
-// turning each 64-row chunk of its 64 columns into one bit word per column and
+// turning each 64-row chunk of its columns into one bit word per column and
 // that word into runs; the 16 shares are then joined in row order through LDS.
 // A mask with a column of more than two runs raises *bad.
-//   ROWS (Skv a multiple of 16): lane r reads the 64 bytes of chunk row r with
-//     four 16-byte loads, and one ballot per column turns the 64 rows' bytes
-//     into that column's word, which v_writelane drops into the column's lane;
-//   otherwise: lane = column throughout, one byte per lane and row (a wave
-//     reads 64 consecutive bytes of a row).
+//   ROWS (Skv a multiple of 16): strips of 128 columns, so that a wave reads
+//     whole 128-byte lines (with 64-column strips the two halves of a line
+//     went to workgroups on different XCDs and every line was fetched twice).
+//     Lane r reads the 128 bytes of chunk row r with eight 16-byte loads, and
+//     one ballot per column turns the 64 rows' bytes into that column's word,
+//     which v_writelane drops into lane (column % 64) of the word pair of
+//     its half of the strip; a lane ends up with two columns.
+//   otherwise: strips of 64 columns, lane = column throughout, one byte per
+//     lane and row (a wave reads 64 consecutive bytes of a row).
 constexpr int kDenseWaves = 16;
 
 // Canonical intervals of a column from its runs (more than two: flag the mask).
@@ -252,42 +256,50 @@ template <bool ROWS>
 __global__ void __launch_bounds__(1024) k_dense_intervals(const uint8_t* dense, int32_t sq, int32_t skv,
                                                           int32_t nstrip, int32_t ngroup, int32_t grows,
                                                           Runs* ws, int32_t* iv, int32_t* bad) {
-  __shared__ Runs part[kDenseWaves][64];
+  constexpr int SW = dense_strip(ROWS);  // columns per strip
+  constexpr int NC = SW / 64;            // columns per lane
+  __shared__ Runs part[kDenseWaves][SW];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int32_t g = blockIdx.x % ngroup;
   const int64_t m = blockIdx.x / ((int64_t)ngroup * nstrip);
-  const int32_t c0 = (int32_t)((blockIdx.x / ngroup) % nstrip) * 64, j = c0 + lane;
+  const int32_t c0 = (int32_t)((blockIdx.x / ngroup) % nstrip) * SW, j = c0 + lane;
   const int32_t g0 = g * grows, g1 = min(sq, g0 + grows);
   const int32_t share = (((grows + kDenseWaves - 1) / kDenseWaves) + 63) & ~63;
   const int32_t r0 = g0 + wave * share, r1 = min(g1, r0 + share);
-  Runs acc{0, 0, 0, 0, 0};
+  Runs acc[NC];
+#pragma unroll
+  for (int h = 0; h < NC; ++h) acc[h] = Runs{0, 0, 0, 0, 0};
   if (ROWS) {
     // rows [base, base + rows) of mask m; lanes past the chunk and bytes past
-    // the mask read zeros, columns past skv are never written out
+    // the mask read zeros, columns past skv (whose bytes are the next row's,
+    // or zeros past the mask) are never written out
     auto load = [&](int32_t base, dense_x4* d) {  // (an empty range past the share: zeros)
       const rsrc_t r = make_rsrc(dense + ((size_t)m * sq + base) * skv, (int64_t)max(0, min(64, r1 - base)) * skv);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) d[k] = dense_load16(r, lane * skv + c0 + 16 * k, 0, 0);
+      for (int k = 0; k < SW / 16; ++k) d[k] = dense_load16(r, lane * skv + c0 + 16 * k, 0, 0);
     };
-    dense_x4 d[4], dn[4];
+    dense_x4 d[SW / 16], dn[SW / 16];
     load(r0, d);
     for (int32_t base = r0; base < r1; base += 64) {
       const int32_t rows = min(64, r1 - base);
       load(base + 64, dn);  // the next chunk's bytes fly during this one
       const int32_t past = lane >= rows ? 0x01010101 : 0;  // rows past the chunk: visible (not masked)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) d[k] |= past;
-      uint32_t wlo = 0, whi = 0;  // masked rows of column c0 + lane
+      for (int k = 0; k < SW / 16; ++k) d[k] |= past;
+      uint32_t wlo[NC], whi[NC];  // masked rows of columns c0 + 64 h + lane
 #pragma unroll
-      for (int col = 0; col < 64; ++col) {
+      for (int h = 0; h < NC; ++h) wlo[h] = whi[h] = 0;
+#pragma unroll
+      for (int col = 0; col < SW; ++col) {
         const uint32_t byte = ((uint32_t)d[col >> 4][(col >> 2) & 3] >> (8 * (col & 3))) & 0xffu;
         const uint64_t vis = __ballot(byte != 0u);
-        wlo = write_lane(~(uint32_t)vis, col, wlo);
-        whi = write_lane(~(uint32_t)(vis >> 32), col, whi);
+        wlo[col >> 6] = write_lane(~(uint32_t)vis, col & 63, wlo[col >> 6]);
+        whi[col >> 6] = write_lane(~(uint32_t)(vis >> 32), col & 63, whi[col >> 6]);
       }
-      acc = join(acc, runs_of(((uint64_t)whi << 32) | wlo, base));
 #pragma unroll
-      for (int k = 0; k < 4; ++k) d[k] = dn[k];
+      for (int h = 0; h < NC; ++h) acc[h] = join(acc[h], runs_of(((uint64_t)whi[h] << 32) | wlo[h], base));
+#pragma unroll
+      for (int k = 0; k < SW / 16; ++k) d[k] = dn[k];
     }
   } else if (j < skv) {
     const uint8_t* col = dense + (size_t)m * sq * skv + j;
@@ -300,15 +312,22 @@ __global__ void __launch_bounds__(1024) k_dense_intervals(const uint8_t* dense, 
       } else {
         for (int r = 0; r < rows; ++r) w |= (uint64_t)(col[(size_t)(base + r) * skv] == 0) << r;
       }
-      acc = join(acc, runs_of(w, base));
+      acc[0] = join(acc[0], runs_of(w, base));
     }
   }
-  part[wave][lane] = acc;
+#pragma unroll
+  for (int h = 0; h < NC; ++h) part[wave][64 * h + lane] = acc[h];
   __syncthreads();
-  if (wave != 0 || j >= skv) return;
-  for (int k = 1; k < kDenseWaves; ++k) acc = join(acc, part[k][lane]);
-  if (ngroup == 1) dense_store(acc, sq, skv, m, j, iv, bad);
-  else ws[(m * ngroup + g) * skv + j] = acc;
+  if (wave != 0) return;
+#pragma unroll
+  for (int h = 0; h < NC; ++h) {
+    const int32_t jh = j + 64 * h;
+    if (jh >= skv) break;
+    Runs a = acc[h];
+    for (int k = 1; k < kDenseWaves; ++k) a = join(a, part[k][64 * h + lane]);
+    if (ngroup == 1) dense_store(a, sq, skv, m, jh, iv, bad);
+    else ws[(m * ngroup + g) * skv + jh] = a;
+  }
 }
 
 // The row groups of each (mask, column) joined in row order.
@@ -557,14 +576,15 @@ hipError_t launch_zero_int(int32_t* x, hipStream_t s) {
 hipError_t launch_encode_dense_intervals(const uint8_t* dense, int32_t nmask, int32_t sq, int32_t skv,
                                          void* ws, int32_t* iv, int32_t* bad, hipStream_t s) {
   hipLaunchKernelGGL(k_zero_int, dim3(1), dim3(1), 0, s, bad);
-  const int32_t nstrip = (skv + 63) / 64;
+  const bool rows = skv % 16 == 0 && (uintptr_t)dense % 16 == 0 && (int64_t)64 * skv < ((int64_t)1 << 31);
+  const int32_t nstrip = (skv + dense_strip(rows) - 1) / dense_strip(rows);
   const int32_t ngroup = dense_groups(nmask, sq, skv);
   const int32_t grows = (int32_t)((((int64_t)sq + ngroup - 1) / ngroup + 63) / 64 * 64);
   const int64_t blocks = (int64_t)nmask * nstrip * ngroup;
   if (blocks <= 0) return hipGetLastError();
   // 16-byte row loads need 16-byte aligned rows; 64 rows must stay within the
   // 32-bit buffer offsets
-  if (skv % 16 == 0 && (uintptr_t)dense % 16 == 0 && (int64_t)64 * skv < ((int64_t)1 << 31))
+  if (rows)
     hipLaunchKernelGGL(k_dense_intervals<true>, dim3((unsigned)blocks), dim3(1024), 0, s, dense, sq, skv,
                        nstrip, ngroup, grows, (Runs*)ws, iv, bad);
   else

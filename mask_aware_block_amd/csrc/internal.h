@@ -76,10 +76,13 @@ hipError_t launch_encode_bitmap(const BitmapSrc& src, const BitmapOut& out, hipS
 // Dense mask -> canonical intervals.  Rows are split into dense_groups()
 // groups so that enough workgroups run; with more than one group `ws` holds
 // dense_ws_bytes() of partial runs.
+// Columns per workgroup strip: 128 where 16-byte row loads are possible
+// (whole 128-byte lines per wave), else 64.
+constexpr int dense_strip(bool row_loads) { return row_loads ? 128 : 64; }
 inline int32_t dense_groups(int64_t nmask, int32_t sq, int32_t skv) {
-  const int64_t strips = nmask * ((skv + 63) / 64);
+  const int64_t strips = nmask * ((skv + 127) / 128);
   if (strips <= 0) return 1;
-  const int64_t want = (512 + strips - 1) / strips;  // about 512 workgroups
+  const int64_t want = (256 + strips - 1) / strips;  // about 256 workgroups of 16 waves (128-column strips)
   const int64_t most = ((int64_t)sq + 1023) / 1024;  // at least 1024 rows per group
   return (int32_t)std::max<int64_t>(1, std::min(want, most));
 }

@@ -283,20 +283,26 @@ def _runs_column(rng, S, cuts):
     return col
 
 
-def test_dense_runs_across_row_chunks():
+@pytest.mark.parametrize("K", [300, 208, 256])
+def test_dense_runs_across_row_chunks(K):
     """Masked runs that start, end or meet on 64-row chunk edges, on the edges
     of the encoder's per-wave row shares and of its row groups (whose partial
     runs a second kernel joins), at a ragged size: canonical
     intervals bit-exact; a third run far from the other two sends the automatic
-    form to the bitmap and makes the interval form fail."""
+    form to the bitmap and makes the interval form fail.  K = 300 takes the
+    byte-per-lane path (64-column strips); 208 and 256 (multiples of 16) the
+    16-byte row loads over 128-column strips, 208 with a strip that ends
+    inside its second half."""
     rng = np.random.default_rng(79)
-    S, K = 2500, 300
+    S = 2500
     # 64-row chunks, per-wave shares and (896 rows each here) row groups
     cuts = np.array([0, 63, 64, 65, 128, 191, 192, 193, 384, 895, 896, 897, 1152, 1792, 2496, 2499, 2500])
     vis = np.stack([_runs_column(rng, S, cuts) for _ in range(K)], axis=1)[None, None]
     vis[0, 0, :, 5] = True
     vis[0, 0, :, 6] = False
     vis[0, 0, 192:384, 7] = False  # one run that fills exactly one wave's share
+    vis[0, 0, :, 70] = False  # columns in the second half of a 128-column strip
+    vis[0, 0, 896:1792, 199] = False
     spec = _dense_spec(vis, None)
     enc = fm.encode(spec)
     assert enc.kind == fm.ENC_INTERVALS

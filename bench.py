@@ -377,6 +377,9 @@ def main():
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the backward pass of the 32K causal-document workload "
                          "(for profiling runs); prints its own JSON line")
+    ap.add_argument("--dense-only", action="store_true",
+                    help="time only the dense-mask encode of the 8K causal-document mask (for profiling runs); "
+                         "prints its own JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
@@ -398,6 +401,9 @@ def main():
         del src, dst
     if args.backward_only:
         print(json.dumps(time_backward(torch, fm, synth, "causal_doc_32k", args.steps, args.warmup)))
+        return
+    if args.dense_only:
+        print(json.dumps(time_dense_encode(torch, fm, synth, "causal_doc_8k", args.steps)))
         return
     # (--graph: steps of mask families whose encoder records kernel launches
     # only are replayed as one HIP graph; on this stack that measured slower

@@ -8,7 +8,11 @@
 - the band's non-empty condition the Ascend page states for negative
   nextTokens / preTokens (which pins inclusive ends);
 - dense -> canonical intervals -> dense round trips, closed-form intervals per
-  family, closed-form causal / band tile states, brute-force tile states.
+  family, closed-form causal / band tile states, brute-force tile states;
+- the (batch, head) slice a mask given per batch entry and head is read at, and
+  the broadcast of a mask given once, against element-by-element loops;
+- the dense family (any nonzero byte visible) against the families it is built
+  from.
 """
 
 import json
@@ -340,3 +344,129 @@ def test_varlen_intervals_round_trip():
             continue
         iv = E.intervals_from_dense(vis)  # every column stays within two masked runs
         np.testing.assert_array_equal(E.dense_from_intervals(iv, vis.shape[0]), vis)
+
+
+# ------------------------------------------- per-(batch, head) slices, dense
+
+def _masked_by_intervals_loop(raw_bh, sq, skv):
+    """Visibility of one raw-interval slice, element by element (pure Python)."""
+    out = np.ones((sq, skv), dtype=bool)
+    for j in range(skv):
+        uts, ute, lts, lte = (int(raw_bh[f][j]) for f in range(4))
+        for i in range(sq):
+            if uts <= i < ute or lts <= i < lte:
+                out[i, j] = False
+    return out
+
+
+def _bitmap_loop(state_bh, index_bh, bits, sq, skv):
+    """Visibility of one 64 x 64 bitmap slice, element by element (pure Python)."""
+    out = np.zeros((sq, skv), dtype=bool)
+    for i in range(sq):
+        for j in range(skv):
+            st = int(state_bh[i // 64, j // 64])
+            if st == 2:
+                out[i, j] = True
+            elif st == 1:
+                word = int(bits[int(index_bh[i // 64, j // 64]), i % 64])
+                out[i, j] = bool((word >> (j % 64)) & 1)
+    return out
+
+
+def test_mask_index_selects_the_batch_head_slice():
+    """A mask given per (batch, head) -- the Ascend sparseMode page's attenMask
+    shapes [B, N, S, S] and the Binary Block Masking block matrix per sequence --
+    is read at slice (b, h); a mask given once for the batch (or for all heads)
+    serves every batch entry (or head) from slice 0."""
+    rng = np.random.default_rng(5)
+    sq, skv, B, H = 70, 90, 2, 3
+    raw = np.zeros((B, H, 4, skv), dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            a = rng.integers(0, sq, skv)
+            raw[b, h, 0] = 0
+            raw[b, h, 1] = a                                   # UT = [0, a)
+            raw[b, h, 2] = np.minimum(sq, a + 1 + rng.integers(0, 20, skv))
+            raw[b, h, 3] = sq                                  # LT = [a + 1 + g, sq)
+    expect = {(b, h): _masked_by_intervals_loop(raw[b, h], sq, skv) for b in range(B) for h in range(H)}
+    # the six slices really differ, so a wrong slice cannot pass by accident
+    assert len({e.tobytes() for e in expect.values()}) == B * H
+    spec = dict(family="intervals", sq=sq, skv=skv, raw_intervals=raw, batch=B, heads=H)
+    for (b, h), e in expect.items():
+        np.testing.assert_array_equal(dense(spec, b, h), e)
+    # batch = 1: every batch entry uses slice 0 of the batch axis
+    spec1 = dict(family="intervals", sq=sq, skv=skv, raw_intervals=raw[:1], batch=1, heads=H)
+    for b in range(B):
+        for h in range(H):
+            np.testing.assert_array_equal(dense(spec1, b, h), expect[(0, h)])
+    # heads = 1: every head uses slice 0 of the head axis
+    spech = dict(family="intervals", sq=sq, skv=skv, raw_intervals=raw[:, :1], batch=B, heads=1)
+    for b in range(B):
+        for h in range(H):
+            np.testing.assert_array_equal(dense(spech, b, h), expect[(b, 0)])
+
+    # block bitmap, per (batch, head)
+    sq, skv = 130, 150
+    nbq, nbk = 3, 3
+    st = rng.integers(0, 3, (B, H, nbq, nbk)).astype(np.uint8)
+    ix = np.full(st.shape, -1, dtype=np.int32)
+    npart = int((st == 1).sum())
+    ix[st == 1] = np.arange(npart, dtype=np.int32)
+    bits = rng.integers(0, 2 ** 63, (npart, 64), dtype=np.int64).astype(np.uint64)
+    bits ^= rng.integers(0, 2, (npart, 64)).astype(np.uint64) << np.uint64(63)
+    expect = {(b, h): _bitmap_loop(st[b, h], ix[b, h], bits, sq, skv) for b in range(B) for h in range(H)}
+    assert len({e.tobytes() for e in expect.values()}) == B * H
+    spec = dict(family="block_bitmap", sq=sq, skv=skv, blk_state=st, blk_index=ix, blk_bits=bits,
+                batch=B, heads=H)
+    for (b, h), e in expect.items():
+        np.testing.assert_array_equal(dense(spec, b, h), e)
+    spec1 = dict(spec, blk_state=st[:1], blk_index=ix[:1], batch=1)
+    for b in range(B):
+        for h in range(H):
+            np.testing.assert_array_equal(dense(spec1, b, h), expect[(0, h)])
+    spech = dict(spec, blk_state=st[:, :1], blk_index=ix[:, :1], heads=1)
+    for b in range(B):
+        for h in range(H):
+            np.testing.assert_array_equal(dense(spech, b, h), expect[(b, 0)])
+
+
+def test_dense_family_equals_the_families_it_is_built_from():
+    """A dense uint8 mask (Ascend sparseMode 1 "allMask"; Binary Block Masking's
+    full mask) holds any byte value; every nonzero byte means visible.  Built from
+    six families with visible bytes drawn from 1..255, slice (b, h) must equal the
+    family it was built from, and a zero written into a visible position hides
+    exactly that position."""
+    rng = np.random.default_rng(8)
+    S = 96
+    fams = [
+        dict(family="causal", sq=S, skv=S),
+        dict(family="causal_document", sq=S, skv=S, cu_seg=np.array([0, 20, 64, S], np.int32)),
+        dict(family="shared_question", sq=S, skv=S, cu_seg=np.array([0, 32, 50, 80, S], np.int32)),
+        dict(family="band", sq=S, skv=S, pre=9, next=-3),
+        dict(family="tree", sq=S, skv=S, tree_prefix=S - 8,
+             tree_parent=np.array([-1, 0, 0, 1, 1, 2, 3, 3], np.int32)),
+        dict(family="document", sq=S, skv=S, cu_seg=np.array([0, 40, S], np.int32)),
+    ]
+    B, H = 2, 3
+    vis = np.stack([np.asarray(M.dense_vis(f)) for f in fams]).reshape(B, H, S, S)
+    val = rng.integers(1, 256, (B, H, S, S)).astype(np.uint8)   # 1..255, includes 1 and >= 2
+    assert (val == 1).any() and (val >= 128).any()
+    d = np.where(vis, val, 0).astype(np.uint8)
+    spec = dict(family="dense", sq=S, skv=S, dense=d, batch=B, heads=H)
+    for k, f in enumerate(fams):
+        b, h = divmod(k, H)
+        np.testing.assert_array_equal(dense(spec, b, h), np.asarray(M.dense_vis(f)))
+    # polarity: clearing one visible byte hides exactly that element
+    b, h = 1, 2
+    i, j = map(int, np.argwhere(vis[b, h])[len(np.argwhere(vis[b, h])) // 2])
+    d2 = d.copy()
+    d2[b, h, i, j] = 0
+    got = dense(dict(spec, dense=d2), b, h)
+    want = vis[b, h].copy()
+    want[i, j] = False
+    np.testing.assert_array_equal(got, want)
+    # a mask given once for all heads serves each head from head slice 0
+    spech = dict(family="dense", sq=S, skv=S, dense=d[:, :1], batch=B, heads=1)
+    for b in range(B):
+        for h in range(H):
+            np.testing.assert_array_equal(dense(spech, b, h), vis[b, 0])

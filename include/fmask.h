@@ -300,6 +300,23 @@ fmask_status fmask_attn_fwd_split(const fmask_attn_args *args, const void *q, co
                                   int32_t splits, void *workspace, size_t workspace_bytes,
                                   void *stream);
 
+/* The split form of fmask_attn_fwd_split for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops and harnesses
+ * that forbid hipMalloc): the partial states go to a scratch area the library
+ * holds on every GPU it runs on, FMASK_SPLIT_SCRATCH_BYTES long, instead of a
+ * caller workspace.  Same arguments, checks and result as fmask_attn_fwd_split
+ * (the same kernels run).  A problem whose partial states exceed the scratch
+ * (fmask_attn_split_workspace_bytes(args, enc, splits) > FMASK_SPLIT_SCRATCH_
+ * BYTES for splits > 1) returns FMASK_ERR_CAPACITY before any launch.  The
+ * first call on a device looks the scratch address up (no allocation, no
+ * stream operation).  Every call on a GPU shares that GPU's scratch and leaves
+ * its partial states there: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and must be ordered by the caller.        */
+#define FMASK_SPLIT_SCRATCH_BYTES ((size_t)16 << 20)
+fmask_status fmask_attn_fwd_split_noalloc(const fmask_attn_args *args, const void *q, const void *k,
+                                          const void *v, void *o, float *lse,
+                                          const fmask_encoded *enc, int32_t splits, void *stream);
+
 /* Bytes of device workspace fmask_attn_bwd needs: two floats per (batch, q
  * head, query row) and the tile table by key-tile column (per column the
  * non-SKIP query tiles, their count, and a longest-first order of the

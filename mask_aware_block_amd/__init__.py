@@ -85,6 +85,7 @@ class AttnArgs(ctypes.Structure):
 
 EXPORTS = ("fmask_encode_bytes", "fmask_encode", "fmask_classify_bytes", "fmask_classify",
            "fmask_attn_fwd", "fmask_attn_split_workspace_bytes", "fmask_attn_fwd_split",
+           "fmask_attn_fwd_split_noalloc",
            "fmask_attn_bwd_workspace_bytes", "fmask_attn_bwd",
            "fmask_preferred_tile", "fmask_status_str", "fmask_last_error")
 
@@ -124,6 +125,9 @@ def lib():
         L.fmask_attn_fwd_split.argtypes = [ctypes.POINTER(AttnArgs), _vp, _vp, _vp, _vp, _vp,
                                            ctypes.POINTER(Encoded), ctypes.c_int32, _vp, ctypes.c_size_t, _vp]
         L.fmask_attn_fwd_split.restype = ctypes.c_int32
+        L.fmask_attn_fwd_split_noalloc.argtypes = [ctypes.POINTER(AttnArgs), _vp, _vp, _vp, _vp, _vp,
+                                                   ctypes.POINTER(Encoded), ctypes.c_int32, _vp]
+        L.fmask_attn_fwd_split_noalloc.restype = ctypes.c_int32
         L.fmask_attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(Tiles)]
         L.fmask_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.fmask_attn_bwd.argtypes = [ctypes.POINTER(AttnArgs)] + [_vp] * 10 + [
@@ -425,6 +429,28 @@ def attn_fwd_split(q, k, v, enc, splits=0, scale=None, out=None, lse=None, works
     st = L.fmask_attn_fwd_split(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                 ctypes.byref(enc.struct), int(splits), _ptr(workspace), workspace.numel(),
                                 _stream_handle(stream))
+    _check(st)
+    return out, lse
+
+
+SPLIT_SCRATCH_BYTES = 16 << 20  # FMASK_SPLIT_SCRATCH_BYTES
+
+
+def attn_fwd_split_noalloc(q, k, v, enc, splits=0, scale=None, out=None, lse=None, stream=None):
+    """attn_fwd_split with the partial states in the library's own per-GPU
+    scratch (fmask_attn_fwd_split_noalloc): nothing is allocated, so out and
+    lse must be given when the caller cannot allocate either."""
+    torch = _torch()
+    L = lib()
+    if scale is None:
+        scale = 1.0 / float(q.shape[-1]) ** 0.5
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    a = attn_args(q, k, v, out, scale)
+    st = L.fmask_attn_fwd_split_noalloc(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                        ctypes.byref(enc.struct), int(splits), _stream_handle(stream))
     _check(st)
     return out, lse
 

@@ -1,11 +1,13 @@
 // libfmask C ABI: argument checking, buffer layout and kernel launches.
 // Every host-detectable error is reported before anything is launched; the
-// library never allocates, frees or synchronises.
+// library never allocates, frees or synchronises (the no-allocation split form
+// uses a fixed scratch array that is part of the library's code object).
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "internal.h"
@@ -644,10 +646,15 @@ size_t fmask_attn_split_workspace_bytes(const fmask_attn_args* a, const fmask_en
   return std::max<size_t>(floats * sizeof(float), kAlign);
 }
 
-fmask_status fmask_attn_fwd_split(const fmask_attn_args* a, const void* q, const void* k, const void* v,
-                                  void* o, float* lse, const fmask_encoded* enc, int32_t splits,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
-  g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+
+// Checks and launches of the split form; the partial states go to `workspace`
+// (workspace_bytes long).  what_ws names the buffer in error messages.
+fmask_status split_fwd(const fmask_attn_args* a, const void* q, const void* k, const void* v, void* o,
+                       float* lse, const fmask_encoded* enc, int32_t splits, void* workspace,
+                       size_t workspace_bytes, const char* what_ws, void* stream) {
   if (!a || !enc) return fail(FMASK_ERR_INVALID, "null args or encoding");
   if (enc->kind != FMASK_ENC_SELECTED) return fail(FMASK_ERR_UNSUPPORTED, "split form: SELECTED encoding only");
   if (splits < 0 || splits > 64) return fail(FMASK_ERR_INVALID, "splits must be in [0, 64] (0 = automatic)");
@@ -672,12 +679,62 @@ fmask_status fmask_attn_fwd_split(const fmask_attn_args* a, const void* q, const
   const int32_t ns = splits == 0 ? auto_splits(a, enc->sel_n) : splits;
   const size_t need = fmask_attn_split_workspace_bytes(a, enc, ns);
   if (ns > 1) {
-    if (!workspace || ((uintptr_t)workspace % 16)) return fail(FMASK_ERR_INVALID, "workspace must be 16-byte aligned");
+    if (!workspace || ((uintptr_t)workspace % 16)) return fail(FMASK_ERR_INVALID, "%s must be 16-byte aligned", what_ws);
     if (workspace_bytes < need)
-      return fail(FMASK_ERR_CAPACITY, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+      return fail(FMASK_ERR_CAPACITY, "%s has %zu bytes, %zu needed", what_ws, workspace_bytes, need);
   }
   return hip_status(launch_attn_selected_bf16(p, a->d, ns, (float*)workspace, (hipStream_t)stream),
                     "selected-key split kernels");
+}
+
+// Scratch area of the no-allocation split form: part of the library's code
+// object, so every GPU the library runs on holds one copy for the life of the
+// process.  Host code never uses the array's name as an address: its device
+// address is looked up once per device (scratch_on_current_device) and that
+// pointer is what the kernels receive.
+static __device__ __align__(256) float scratch[FMASK_SPLIT_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+fmask_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FMASK_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(split scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FMASK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fmask_status fmask_attn_fwd_split(const fmask_attn_args* a, const void* q, const void* k, const void* v,
+                                  void* o, float* lse, const fmask_encoded* enc, int32_t splits,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  return split_fwd(a, q, k, v, o, lse, enc, splits, workspace, workspace_bytes, "workspace", stream);
+}
+
+fmask_status fmask_attn_fwd_split_noalloc(const fmask_attn_args* a, const void* q, const void* k, const void* v,
+                                          void* o, float* lse, const fmask_encoded* enc, int32_t splits,
+                                          void* stream) {
+  g_err[0] = 0;
+  if (!a || !enc) return fail(FMASK_ERR_INVALID, "null args or encoding");
+  void* ws = nullptr;
+  const fmask_status st = scratch_on_current_device(&ws);
+  if (st != FMASK_OK) return st;
+  return split_fwd(a, q, k, v, o, lse, enc, splits, ws, FMASK_SPLIT_SCRATCH_BYTES, "the library's split scratch",
+                   stream);
 }
 
 }  // extern "C"

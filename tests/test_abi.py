@@ -156,6 +156,9 @@ def test_split_backward_varlen_dense_host_validation():
     sel.kind, sel.batch, sel.heads, sel.sq, sel.skv, sel.sel_n = fm.ENC_SELECTED, 1, 1, 512, 512, 64
     assert L.fmask_attn_fwd_split(ctypes.byref(a), p, p, p, p, None, ctypes.byref(sel), 65, None, 0,
                                   None) == fm.ERR_INVALID
+    # no-allocation split form: null arguments are refused before the scratch lookup
+    assert L.fmask_attn_fwd_split_noalloc(None, p, p, p, p, None, ctypes.byref(sel), 0, None) == fm.ERR_INVALID
+    assert L.fmask_attn_fwd_split_noalloc(ctypes.byref(a), p, p, p, p, None, None, 0, None) == fm.ERR_INVALID
     assert L.fmask_attn_split_workspace_bytes(ctypes.byref(a), ctypes.byref(iv_enc), 4) == 0
     assert L.fmask_attn_split_workspace_bytes(ctypes.byref(a), ctypes.byref(sel), 4) > 0
     # backward: bf16 only, 128 x 64 tables, workspace at least the queried size

@@ -221,7 +221,10 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
   // K tile kt (list entry i, value e) and its mask data: LOADS + 1 loads.
   // Intervals: wave w loads field w.  Bitmap: wave w loads the 32 words of its
   // rows when its block is PARTIAL, else a load past the pool's range (zeros)
-  // so that every wave always issues the same number of loads.
+  // so that every wave always issues the same number of loads.  The pool's
+  // buffer resource spans pool_cap * 512 bytes <= 2^31 (the launcher refuses
+  // larger pools: buffer offsets and num_records are 32-bit), so the dummy
+  // offset 0xfffffff0 is out of range for every accepted pool.
   auto issue_k = [&](int i, int e, int buf) INLINE {
     const int kt = e & 0x7fffffff;
     const int base = lds_w + G::K0 + buf * G::TILE, g0 = kt * kstep;
@@ -229,7 +232,7 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
     for (int n = 0; n < G::LOADS; ++n) dma16(krs, kgo[n] + g0, base + n * 1024);
     if (KIND == FMASK_ENC_BITMAP) {
       const int info = wave_block(i, e);
-      const int off = info >= 0 ? info * (kBlk * 8) + (w & 1) * 256 + lane * 4 : 0x7ffffff0;
+      const int off = info >= 0 ? info * (kBlk * 8) + (w & 1) * 256 + lane * 4 : (int)0xfffffff0u;
       dma4(irs, off, lds_iv + buf * G::IVB);
     } else {
       dma4(irs, (w * p.skv + kt * BN + lane) * 4, lds_iv + buf * G::IVB);

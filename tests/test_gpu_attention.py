@@ -289,6 +289,88 @@ def test_poison_masked_kv_does_not_leak():
     np.testing.assert_array_equal(l1, l2)
 
 
+def test_poison_unselected_blocks_do_not_leak():
+    """Selected-key lists (one-pass and split forms): NaN in every K/V block that
+    no query lists must not reach the output (those blocks are never gathered;
+    the selected-key PR's poison cases).  The lists hold -1 entries, duplicates
+    and an out-of-range index; the last block is ragged."""
+    S, K = 40, 32 * 40 + 5
+    w = _small("bf16", 256, S, K, Hq=8, Hkv=2, seed=21)
+    rng = np.random.default_rng(22)
+    sel = synth.selected_lists(rng, S, 20, n=64)  # blocks 0..19 only
+    sel[5, 3] = 999  # outside [0, nblk): skipped like -1
+    spec = dict(family="selected_key", sq=S, skv=K, batch=1, sel=sel[None], sel_cells=32)
+    arrays = synth.draw_qkv(w)
+    k, v = arrays[1].copy(), arrays[2].copy()
+    k[:, :, 20 * 32:] = 0x7FC0  # bf16 NaN in blocks 20..40
+    v[:, :, 20 * 32:] = 0x7FC0
+    enc = fm.encode(spec)
+    outs = []
+    for arr in (arrays, (arrays[0], k, v)):
+        q_, k_, v_ = to_device(w, arr)
+        o1, l1 = fm.attn_fwd(q_, k_, v_, enc, None, scale=w["scale"])
+        o2, l2 = fm.attn_fwd_split(q_, k_, v_, enc, splits=3, scale=w["scale"])
+        torch.cuda.synchronize()
+        outs.append([t.float().cpu().numpy() for t in (o1, l1, o2, l2)])
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
+    assert np.isfinite(outs[1][0]).all()
+
+
+@pytest.mark.parametrize("bm", [128, 64])
+def test_poison_bitmap_skip_column_does_not_leak(bm):
+    """Block bitmap: NaN in a 64-key column whose blocks are SKIP for every row
+    (never loaded) leaves the output bit-identical."""
+    S, K = 300, 640
+    w = _small("bf16", 128, S, K, Hq=2, Hkv=2, seed=23)
+    rng = np.random.default_rng(24)
+    nbq, nbk = -(-S // 64), K // 64
+    st, ix, bits = synth.block_pattern(rng, nbq, nbk, 0.3, 0.3)
+    st[:, 5] = 0  # block column 5: keys 320..383, SKIP for every row
+    npart = int((st == 1).sum())
+    ix = np.full(st.shape, -1, dtype=np.int32)
+    ix[st == 1] = np.arange(npart, dtype=np.int32)
+    bits = bits[:npart] if len(bits) >= npart else np.resize(bits, (npart, 64))
+    spec = dict(family="block_bitmap", sq=S, skv=K, batch=1, heads=1, blk_state=st[None, None],
+                blk_index=ix[None, None], blk_bits=np.asarray(bits, dtype=np.uint64).reshape(-1, 64),
+                force_diag=False)
+    arrays = synth.draw_qkv(w)
+    k, v = arrays[1].copy(), arrays[2].copy()
+    k[:, :, 320:384] = 0x7FC0
+    v[:, :, 320:384] = 0x7FC0
+    enc = fm.encode(spec)
+    tiles = fm.classify(enc, bm, 64)
+    res = []
+    for arr in (arrays, (arrays[0], k, v)):
+        q_, k_, v_ = to_device(w, arr)
+        o, lse = fm.attn_fwd(q_, k_, v_, enc, tiles, scale=w["scale"])
+        torch.cuda.synchronize()
+        res.append((o.float().cpu().numpy(), lse.cpu().numpy()))
+    np.testing.assert_array_equal(res[0][0], res[1][0])
+    np.testing.assert_array_equal(res[0][1], res[1][1])
+    qq, kk, vv = (to_f64(w, a) for a in arrays)
+    ro, rl = OA.attention_dense(qq, kk, vv, OA.spec_vis_fn(spec), w["scale"])
+    compare(w, res[1][0], res[1][1], ro, rl, f"bitmap poison bm {bm}")
+
+
+def test_interval_long_tile_rows():
+    """Interval encoding with more than 256 non-SKIP tiles in a row, past the
+    kernel's LDS list stage: bottom-right causal, 150 queries over 20000 keys."""
+    S, K = 150, 20000
+    w = _small("bf16", 128, S, K, B=1, Hq=2, Hkv=1, seed=25)
+    spec = dict(family="causal_bottom_right", sq=S, skv=K)
+    arrays = synth.draw_qkv(w)
+    q, k, v = to_device(w, arrays)
+    enc = fm.encode(spec)
+    tiles = fm.classify(enc, 128, 64)
+    assert int(tiles.arrays()[2].max()) > 256
+    o, lse = fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"])
+    torch.cuda.synchronize()
+    qq, kk, vv = (to_f64(w, a) for a in arrays)
+    ro, rl = OA.attention_dense(qq, kk, vv, OA.spec_vis_fn(spec), w["scale"])
+    compare(w, o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, "interval long rows")
+
+
 def test_deterministic():
     w = synth.workload("causal_doc_8k", Hq=8, Hkv=2)
     arrays = synth.draw_qkv(w)

@@ -319,6 +319,25 @@ def test_dense_runs_across_row_chunks(K):
     assert ei.value.status == fm.ERR_INVALID
 
 
+@pytest.mark.parametrize("K", [208, 256])
+def test_dense_row_loads_with_several_masks(K):
+    """The 16-byte row-load path of the dense encoder with one mask per (batch,
+    head) (2 x 2 distinct masks) and several row groups: the mask index taken
+    from the workgroup, the per-mask row base and the per-(mask, group) partial
+    runs; every slice bit-exact with the oracle's canonical intervals."""
+    rng = np.random.default_rng(81)
+    S = 2500
+    cuts = np.array([0, 63, 64, 65, 191, 192, 384, 895, 896, 897, 1792, 2496, 2500])
+    vis = np.stack([np.stack([np.stack([_runs_column(rng, S, cuts) for _ in range(K)], axis=1)
+                              for _ in range(2)]) for _ in range(2)])
+    assert len({vis[b, h].tobytes() for b in range(2) for h in range(2)}) == 4
+    enc = fm.encode(_dense_spec(vis, "intervals"))
+    got = enc.intervals().cpu().numpy()
+    for b in range(2):
+        for h in range(2):
+            np.testing.assert_array_equal(got[b, h], OE.intervals_from_dense(vis[b, h]), err_msg=f"mask ({b}, {h})")
+
+
 def test_dense_masks_fall_back_to_the_bitmap_form():
     rng = np.random.default_rng(78)
     S, K = 300, 260

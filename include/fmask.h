@@ -252,7 +252,22 @@ size_t fmask_encode_bytes(const fmask_mask_desc *desc);
 
 /* Turn the mask description into its canonical compressed encoding (mask
  * encoder).  out: device buffer of at least fmask_encode_bytes(desc) bytes, 256-
- * byte aligned.  *enc (host) receives the kind and device views into out.       */
+ * byte aligned.  *enc (host) receives the kind and device views into out.
+ * Defining passages: the FlashMask rebuttal (the mask types, and a mask kept
+ * as a compact description instead of an Sq x Skv matrix whose size grows with
+ * the sequence, "Response to Weaknesses and Questions"); the Ascend
+ * "sparseMode" page (preTokens / nextTokens band and the cumulative-length
+ * arrays of the varlen examples); the Binary Block Masking abstract (block
+ * masks, packing, tree masks); the selected-key PR overview (per-query lists
+ * of 32-cell blocks, -1 and duplicate entries skipped).
+ * Host arrays: segment starts of up to 64 segments travel in kernel arguments;
+ * larger cu_seg arrays, tree_parent and the varlen arrays are copied from the
+ * caller's host memory with hipMemcpyAsync, which the HIP runtime stages before
+ * the call returns (the caller may free them afterwards).  Those copies are not
+ * safe under HIP graph capture (a captured copy would read the host array at
+ * replay): capture only encodes of the other families.  The DENSE family in
+ * the automatic or the interval form reads one flag back and synchronises the
+ * stream (see dense_form).                                                      */
 fmask_status fmask_encode(const fmask_mask_desc *desc, void *out, size_t out_bytes,
                           fmask_encoded *enc, void *stream);
 
@@ -262,11 +277,24 @@ size_t fmask_classify_bytes(const fmask_encoded *enc, int32_t bm, int32_t bn);
 /* Reduce an INTERVALS or BITMAP encoding to the exact per-tile SKIP / PARTIAL /
  * FULL table at tile size bm x bn, plus per-row compact lists of the non-SKIP
  * tiles and a longest-first order of tile rows (tile classifier).  bm and bn are
- * multiples of 16 in [16, 256]; the BITMAP kind needs multiples of 64.          */
+ * multiples of 16 in [16, 256]; the BITMAP kind needs multiples of 64.
+ * Defining passages: the FlashMask rebuttal ("Response to Weaknesses and
+ * Questions": the kernel's tiling block size is separate from the mask's
+ * block size, and fully masked blocks are not computed); the Binary Block
+ * Masking abstract (blocks classified as empty, full or partially filled).
+ * out: device buffer of fmask_classify_bytes(enc, bm, bn) bytes, 256-byte
+ * aligned; *tiles (host) receives device views into out.  Kernels only: safe
+ * under HIP graph capture.                                                      */
 fmask_status fmask_classify(const fmask_encoded *enc, int32_t bm, int32_t bn, void *out,
                             size_t out_bytes, fmask_tiles *tiles, void *stream);
 
-/* Masked attention forward: for every (batch, q head, row) with visible set V_i,
+/* Defining passages: the FlashMask rebuttal ("Response to Weaknesses and
+ * Questions": exact attention under the packed-sequence masks, fully masked
+ * blocks skipped), the Ascend "sparseMode" page (attenMask: the scores QK^T
+ * are masked where the mask is set, before the softmax), the Binary Block
+ * Masking abstract, and the selected-key PR (visibility only from the list,
+ * an empty list giving a zero row).
+ * Masked attention forward: for every (batch, q head, row) with visible set V_i,
  * s_ij = scale * <Q_i, K_j>, O_i = sum_{j in V_i} softmax(s_i)_j V_j and
  * LSE_i = log sum_{j in V_i} exp(s_ij); a row with no visible key gets O_i = 0
  * and LSE_i = -inf.  SKIP tiles are never loaded, FULL tiles are computed

@@ -32,9 +32,12 @@ __device__ inline int lds_addr(const void* p) {
 // reads behind them nor drains them when waiting for an ordinary load.  The
 // kernels make the data visible themselves (vmcnt wait, then a barrier).
 // `lds` is the LDS byte address (see lds_addr), wave-uniform.  A scalar write
-// of M0 needs one wait state before a load with the LDS bit reads it (the
-// compiler pads only the code it generates, not inline assembly), hence the
-// s_nop between the two.
+// of M0 needs one wait state before a memory instruction with the LDS bit
+// reads it (AMD CDNA4 ISA reference guide, "Manually Inserted Wait States
+// (NOPs)": S_MOV to M0 followed by an LDS-DMA load, 1 wait state); the
+// compiler pads only the code it generates, not inline assembly, hence the
+// s_nop between the two.  Without it the load may use the previous M0 and put
+// its data into the previous load's destination.
 __device__ inline void dma16(rsrc_t r, int voff, int lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :

@@ -377,6 +377,9 @@ def main():
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the backward pass of the 32K causal-document workload "
                          "(for profiling runs); prints its own JSON line")
+    ap.add_argument("--only", default=None,
+                    help="time only this workload (a forward workload name, e.g. selected_key_128k) and print its "
+                         "own JSON line (for profiling runs)")
     ap.add_argument("--dense-only", action="store_true",
                     help="time only the dense-mask encode of the 8K causal-document mask (for profiling runs); "
                          "prints its own JSON line")
@@ -404,6 +407,9 @@ def main():
         return
     if args.dense_only:
         print(json.dumps(time_dense_encode(torch, fm, synth, "causal_doc_8k", args.steps)))
+        return
+    if args.only:
+        print(json.dumps(time_workload(torch, fm, synth, args.only, args.steps, args.warmup, args.min_warmup_s)))
         return
     # (--graph: steps of mask families whose encoder records kernel launches
     # only are replayed as one HIP graph; on this stack that measured slower

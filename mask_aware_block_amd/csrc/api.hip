@@ -554,7 +554,7 @@ fmask_status fmask_classify(const fmask_encoded* enc, int32_t bm, int32_t bn, vo
   if (e != hipSuccess) return hip_status(e, "classify kernel");
   e = launch_tile_lists(state, (int32_t)T.rows, (int32_t)T.nkt, list, count, s);
   if (e != hipSuccess) return hip_status(e, "tile list kernel");
-  e = launch_tile_order(count, (int32_t)T.rows, order, s);
+  e = launch_tile_order(count, (int32_t)T.rows, (int32_t)T.nqt, order, s);
   return hip_status(e, "tile order kernel");
 }
 
@@ -624,6 +624,15 @@ fmask_status fmask_attn_fwd(const fmask_attn_args* a, const void* q, const void*
   const int64_t items = (int64_t)enc->batch * enc->heads * tiles->nqt * p.expand;
   if (items > INT32_MAX / 2) return fail(FMASK_ERR_UNSUPPORTED, "grid too large");
   p.n_items = (int32_t)items;
+  {
+    // (K/V head, batch) sets dealt whole to the XCDs (o3 kernel) when they
+    // split evenly, every XCD's share holds all batch masks alike, and one set
+    // fills an XCD's workgroup slots (32 CUs x 3): with smaller sets the last
+    // set's longest rows would start when the XCD is nearly done
+    const int64_t sets = (int64_t)a->b * a->hkv;
+    p.set_major = sets % kXcds == 0 && enc->heads == 1 && (enc->batch == 1 || (sets / kXcds) % a->b == 0) &&
+                  (int64_t)tiles->nqt * group >= 96;
+  }
   p.kind = enc->kind;
   p.iv = enc->intervals;
   p.bstate = enc->blk_state; p.bindex = enc->blk_index; p.bbits = enc->blk_bits; p.pool_cap = enc->pool_cap;
@@ -831,7 +840,7 @@ fmask_status fmask_attn_bwd(const fmask_attn_args* a, const void* q, const void*
   // the tile table by key-tile column, and its longest-first order
   hipError_t ec = launch_tile_cols(tiles->state, enc->batch * enc->heads, tiles->nqt, tiles->nkt, col_list,
                                    col_count, s);
-  if (ec == hipSuccess) ec = launch_tile_order(col_count, (int32_t)L.cols, col_order, s);
+  if (ec == hipSuccess) ec = launch_tile_order(col_count, (int32_t)L.cols, (int32_t)L.cols, col_order, s);
   if (ec != hipSuccess) return hip_status(ec, "tile column kernels");
   return hip_status(launch_attn_bwd_bf16(p, a->d, s), "attention backward kernels");
 }

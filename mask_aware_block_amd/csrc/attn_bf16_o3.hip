@@ -114,6 +114,30 @@ __device__ inline int logical_item(int gsz) {
   return ((k / gsz) * kXcds + xcd) * gsz + (k % gsz);
 }
 
+// Set-major items: item l = ((kvh * b + batch) * nqt + t) * group + j is head
+// kvh * group + j of `batch` on the t-th longest tile row of its mask slice.
+// The blocks of XCD x (x = blockIdx % 8) take items [x n / 8, (x + 1) n / 8)
+// in turn, so an XCD works through whole (K/V head, batch) sets one after
+// another: the workgroups on one XCD at a time share one set's K and V, and
+// as each walks its keys in ascending order they reuse each other's tiles in
+// that XCD's L2.  (The round-robin deal of decode_item spreads every set over
+// all XCDs, so each XCD holds several sets' K and V at once.)
+__device__ inline Item set_item(const TileAttnParams& p, int l) {
+  Item it;
+  const int j = l % p.group;
+  int r = l / p.group;
+  const int t = r % p.nqt;
+  r /= p.nqt;
+  it.b = r % p.b;
+  it.kvh = r / p.b;
+  it.h = it.kvh * p.group + j;
+  it.mb = p.mb > 1 ? it.b : 0;
+  it.mh = p.mh > 1 ? it.h : 0;
+  it.row = p.order[(it.mb * p.mh + it.mh) * p.nqt + t];
+  it.qt = it.row % p.nqt;
+  return it;
+}
+
 // Block info of a 64 x 64 bitmap block: its pool index if PARTIAL, else
 // kBlkFull or kBlkSkip.
 constexpr int kBlkFull = -1, kBlkSkip = -2;
@@ -127,9 +151,16 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
   __shared__ __attribute__((aligned(1024))) char smem[G::END];
   __shared__ int32_t lst[kList];
 
-  const int l = logical_item(gsz);
-  if (l >= p.n_items) return;
-  const Item it = decode_item(p, l);
+  Item it;
+  if (p.set_major) {
+    const int per = p.n_items / kXcds, k = blockIdx.x / kXcds;
+    if (k >= per) return;
+    it = set_item(p, (int)(blockIdx.x % kXcds) * per + k);
+  } else {
+    const int l = logical_item(gsz);
+    if (l >= p.n_items) return;
+    it = decode_item(p, l);
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
@@ -489,7 +520,7 @@ template <int D, int KIND>
 hipError_t launch_d(const TileAttnParams& p, hipStream_t s) {
   const int gsz = (p.mh == 1) ? p.group : 1;
   if (p.n_items <= 0) return hipSuccess;
-  const int64_t unit = (int64_t)kXcds * gsz;
+  const int64_t unit = p.set_major ? kXcds : (int64_t)kXcds * gsz;
   const int64_t npad = (p.n_items + unit - 1) / unit * unit;
   hipLaunchKernelGGL((k_attn_o3<D, KIND>), dim3((unsigned)npad), dim3(NT), 0, s, p, gsz);
   return hipGetLastError();

@@ -173,32 +173,41 @@ __global__ void __launch_bounds__(256) k_tile_cols(const uint8_t* state, int32_t
   if (lane == 0) count[col] = running;
 }
 
-// Rank of every tile row under (count descending, index ascending); the rank
-// is unique, so order[rank] = row is a permutation.
-__global__ void __launch_bounds__(256) k_tile_order(const int32_t* count, int32_t rows,
+// Rank of every tile row within its slice of `seg` consecutive rows (one mask
+// slice of the tile table) under (count descending, index ascending), plus the
+// slice's first row: the rank is unique, so order[rank] = row is a permutation
+// that lists slice 0's rows longest first, then slice 1's, and so on.
+__global__ void __launch_bounds__(256) k_tile_order(const int32_t* count, int32_t rows, int32_t seg,
                                                     int32_t* order) {
   // Row y's key count[y] * 2^32 + (2^32 - 1 - y): the rank of row x is the
-  // number of larger keys (longer rows first, ties by index), one 64-bit
-  // compare per row.
+  // slice start plus the number of larger keys in its slice, one 64-bit
+  // compare per row of the slices this block's rows fall in.
   __shared__ __attribute__((aligned(16))) uint64_t key[512];
   const int x = blockIdx.x * blockDim.x + threadIdx.x;
   auto key_of = [](int32_t c, int y) -> uint64_t { return ((uint64_t)(uint32_t)c << 32) | (uint32_t)(~y); };
   const uint64_t kx = x < rows ? key_of(count[x], x) : 0ull;
-  int rank = 0;
-  for (int base = 0; base < rows; base += 512) {
+  const int lo = x / seg * seg, hi = min(lo + seg, rows);
+  const int first = blockIdx.x * blockDim.x;
+  const int last = min(first + (int)blockDim.x, rows) - 1;
+  const int scan_lo = first / seg * seg, scan_hi = min((last / seg + 1) * seg, rows);
+  int rank = lo;
+  for (int base = scan_lo; base < scan_hi; base += 512) {
     __syncthreads();
     uint64_t v[2];  // both loads in flight before the stores; padding keys are 0
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int y = base + threadIdx.x + 256 * k;
-      v[k] = y < rows ? key_of(count[y], y) : 0ull;
+      v[k] = y < scan_hi ? key_of(count[y], y) : 0ull;
     }
 #pragma unroll
     for (int k = 0; k < 2; ++k) key[threadIdx.x + 256 * k] = v[k];
     __syncthreads();
-    const int lim = min(512, rows - base);
+    const int lim = min(512, scan_hi - base);
 #pragma unroll 8
-    for (int i = 0; i < lim; ++i) rank += key[i] > kx;
+    for (int i = 0; i < lim; ++i) {
+      const int y = base + i;
+      rank += (key[i] > kx) & (y >= lo) & (y < hi);
+    }
   }
   if (x < rows) order[rank] = x;
 }
@@ -257,9 +266,11 @@ hipError_t launch_tile_cols(const uint8_t* state, int32_t nmask, int32_t nqt, in
   return hipGetLastError();
 }
 
-hipError_t launch_tile_order(const int32_t* count, int32_t rows, int32_t* order, hipStream_t s) {
+hipError_t launch_tile_order(const int32_t* count, int32_t rows, int32_t seg, int32_t* order,
+                             hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_tile_order, dim3((rows + 255) / 256), dim3(256), 0, s, count, rows, order);
+  if (seg <= 0 || seg > rows) seg = rows;
+  hipLaunchKernelGGL(k_tile_order, dim3((rows + 255) / 256), dim3(256), 0, s, count, rows, seg, order);
   return hipGetLastError();
 }
 

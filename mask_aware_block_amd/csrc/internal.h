@@ -107,7 +107,9 @@ hipError_t launch_tile_lists(const uint8_t* state, int32_t rows, int32_t nkt, in
                              int32_t* count, hipStream_t s);
 hipError_t launch_tile_cols(const uint8_t* state, int32_t nmask, int32_t nqt, int32_t nkt,
                             int32_t* list, int32_t* count, hipStream_t s);
-hipError_t launch_tile_order(const int32_t* count, int32_t rows, int32_t* order, hipStream_t s);
+// order[] of `rows` tile rows: slices of `seg` rows in turn, each longest first
+hipError_t launch_tile_order(const int32_t* count, int32_t rows, int32_t seg, int32_t* order,
+                             hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 struct TileAttnParams {
@@ -128,6 +130,7 @@ struct TileAttnParams {
   int32_t mb, mh;      // distinct masks along batch / heads
   int32_t expand;      // (b, h) pairs per tile row
   int32_t n_items;     // tile rows * expand
+  int32_t set_major;   // items dealt to the XCDs by (K/V head, batch) set (o3 kernel)
   // mask
   int32_t kind;        // FMASK_ENC_INTERVALS or FMASK_ENC_BITMAP
   const int32_t* iv;   // [mb][mh][4][skv]

@@ -165,11 +165,19 @@ def tile_lists(states):
     return lists.astype(np.uint32).view(np.int32), counts
 
 
-def tile_order(counts):
-    """Tile-row indices sorted by decreasing count, ties by increasing index."""
+def tile_order(counts, slice_rows=None):
+    """Tile-row indices by decreasing count, ties by increasing index, within
+    each slice of `slice_rows` consecutive rows (one mask slice of the table),
+    the slices in turn; one slice of all rows if slice_rows is None.  (The
+    pages fix no order of tile rows; any order computes the same result.)"""
     counts = np.asarray(counts, dtype=np.int64).ravel()
-    idx = np.arange(counts.size)
-    return np.lexsort((idx, -counts)).astype(np.int32)
+    n = counts.size
+    step = n if not slice_rows else int(slice_rows)
+    out = []
+    for lo in range(0, n, max(step, 1)):
+        idx = np.arange(lo, min(lo + step, n))
+        out.append(idx[np.lexsort((idx, -counts[idx]))])
+    return (np.concatenate(out) if out else np.zeros(0, np.int64)).astype(np.int32)
 
 
 def bitmap_from_dense(vis, blk=BLOCK):

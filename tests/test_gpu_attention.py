@@ -218,6 +218,31 @@ def test_bitmap_long_tile_rows():
         compare(w, o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"long rows bm {bm}")
 
 
+def test_xcd_set_major_items():
+    """Items dealt to the XCDs by whole (K/V head, batch) sets (16 sets of
+    6 tile rows x 16 heads, per-batch masks and one shared mask, ragged)."""
+    S, B, Hq, Hkv = 700, 2, 128, 8
+    w = _small("bf16", 64, S, S, Hq=Hq, Hkv=Hkv, B=B, seed=5)
+    rng = np.random.default_rng(8)
+    nb = -(-S // 64)
+    sts, ixs, pools, off = [], [], [], 0
+    for _ in range(B):
+        st, ix, bits = synth.block_pattern(rng, nb, nb, 0.2, 0.2)
+        sts.append(st)
+        ixs.append(np.where(ix >= 0, ix + off, -1))
+        pools.append(bits)
+        off += bits.shape[0]
+    spec = dict(family="block_bitmap", sq=S, skv=S, batch=B, heads=1,
+                blk_state=np.stack(sts)[:, None], blk_index=np.stack(ixs)[:, None].astype(np.int32),
+                blk_bits=np.concatenate(pools).reshape(-1, 64), force_diag=True)
+    _dense_check(w, spec, "set-major bitmap per batch")
+    raw = rng.integers(-10, S + 10, size=(B, 1, 4, S)).astype(np.int32)
+    _dense_check(w, dict(family="intervals", sq=S, skv=S, batch=B, heads=1, raw_intervals=raw),
+                 "set-major intervals per batch")
+    cu = np.array([0, 90, 300, 301, 640, S], dtype=np.int32)
+    _dense_check(w, dict(family="causal_document", sq=S, skv=S, cu_seg=cu), "set-major shared mask")
+
+
 def test_gqa_groups_and_batch():
     for Hq, Hkv in [(8, 1), (8, 8), (6, 2)]:
         w = _small("bf16", 128, 257, 257, Hq=Hq, Hkv=Hkv, B=2)

@@ -120,7 +120,7 @@ def test_raw_intervals_canonicalised():
             es = OE.tile_states(_dense_all(spec, b, h), 64, 64)
             np.testing.assert_array_equal(st[b, h], es)
             allc.append(OE.tile_lists(es)[1])
-    np.testing.assert_array_equal(od, OE.tile_order(np.concatenate(allc)))
+    np.testing.assert_array_equal(od, OE.tile_order(np.concatenate(allc), len(allc[0])))
 
 
 def _bitmap_expect(spec, b, h):
@@ -173,7 +173,7 @@ def test_block_bitmap_exact(S, K, diag):
             el, ec = OE.tile_lists(es)
             np.testing.assert_array_equal(ls[b, 0], el)
             allc.append(ec)
-        np.testing.assert_array_equal(od, OE.tile_order(np.concatenate(allc)))
+        np.testing.assert_array_equal(od, OE.tile_order(np.concatenate(allc), len(allc[0])))
 
 
 def test_tree_bfs_goes_bitmap_dfs_goes_intervals():
@@ -239,7 +239,7 @@ def test_full_size_tables(name):
         np.testing.assert_array_equal(ls[b, 0], el)
         np.testing.assert_array_equal(cn[b, 0], ec)
         allc.append(ec)
-    np.testing.assert_array_equal(od, OE.tile_order(np.concatenate(allc)))
+    np.testing.assert_array_equal(od, OE.tile_order(np.concatenate(allc), len(allc[0])))
     if enc.kind == fm.ENC_INTERVALS:
         np.testing.assert_array_equal(got_iv, OE.intervals_from_dense(colvis))
 

@@ -259,6 +259,10 @@ def test_tile_lists_and_order():
     assert (lists[2].view(np.uint32).tolist() == [0 | full, 1 | full, 2 | full, 3])
     assert (lists[3, :2].view(np.uint32).tolist() == [0, 3 | full])
     assert E.tile_order(counts).tolist() == [2, 0, 3, 1]
+    # per slice of 3 rows: slice [5, 1, 5] -> rows 0, 2 (tie, lower index
+    # first), 1; slice [0, 7] -> rows 4, 3 (the slices are not merged)
+    assert E.tile_order([5, 1, 5, 0, 7], 3).tolist() == [0, 2, 1, 4, 3]
+    assert E.tile_order([5, 1, 5, 0, 7]).tolist() == [4, 0, 2, 1, 3]
 
 
 def test_bitmap_round_trip():

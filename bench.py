@@ -77,7 +77,7 @@ def visible_pairs_bitmap(torch, enc):
 EV_EVERY = 4  # timed steps per sampled attention launch (each recorded event costs the stream microseconds)
 
 
-def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5, graph=False):
+def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5, graph=False, bm=None):
     w = synth.workload(name)
     q, k, v = (_bf16(torch, a) if w["dtype"] == "bf16" else torch.from_numpy(a).cuda()
                for a in synth.draw_qkv(w))
@@ -90,7 +90,9 @@ def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5, graph
     # the encoding and the tile table live in buffers the caller allocates once
     # (the library never allocates); every step re-runs the encoder and classifier
     enc0 = fm.encode(mi)
-    bufs = [enc0.buf, None if selected else fm.classify(enc0, dtype=w["dtype"], d=w["D"]).buf]
+    # (bm: tile rows of the table; None = the library's preferred tile)
+    tile = dict(bm=bm, bn=64) if bm else {}
+    bufs = [enc0.buf, None if selected else fm.classify(enc0, dtype=w["dtype"], d=w["D"], **tile).buf]
 
     def step(ev=None, attn_only=False):
         # (each recorded event costs the stream a few microseconds, so the timed
@@ -102,7 +104,7 @@ def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5, graph
         enc = fm.encode(mi, out=bufs[0])
         if ev and not attn_only:
             ev[1].record(stream)
-        tiles = None if selected else fm.classify(enc, dtype=w["dtype"], d=w["D"], out=bufs[1])
+        tiles = None if selected else fm.classify(enc, dtype=w["dtype"], d=w["D"], out=bufs[1], **tile)
         if ev:
             ev[2].record(stream)
         fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"], out=o, lse=lse)
@@ -296,7 +298,7 @@ def time_backward(torch, fm, synth, name, steps, warmup):
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_causal_doc_32k_hbm_bytes.txt")
 ATTN_SOURCES = [os.path.join(ROOT, "mask_aware_block_amd", "csrc", f)
-                for f in ("attn_bf16_o3.hip", "device_util.h")]
+                for f in ("attn_bf16_o3.hip", "attn_common.h", "device_util.h")]
 
 
 def measured_traffic():
@@ -380,6 +382,8 @@ def main():
     ap.add_argument("--only", default=None,
                     help="time only this workload (a forward workload name, e.g. selected_key_128k) and print its "
                          "own JSON line (for profiling runs)")
+    ap.add_argument("--bm", type=int, default=None,
+                    help="with --only: tile rows of the table (default: the library's preferred tile)")
     ap.add_argument("--dense-only", action="store_true",
                     help="time only the dense-mask encode of the 8K causal-document mask (for profiling runs); "
                          "prints its own JSON line")
@@ -409,7 +413,8 @@ def main():
         print(json.dumps(time_dense_encode(torch, fm, synth, "causal_doc_8k", args.steps)))
         return
     if args.only:
-        print(json.dumps(time_workload(torch, fm, synth, args.only, args.steps, args.warmup, args.min_warmup_s)))
+        print(json.dumps(time_workload(torch, fm, synth, args.only, args.steps, args.warmup, args.min_warmup_s,
+                                       bm=args.bm)))
         return
     # (--graph: steps of mask families whose encoder records kernel launches
     # only are replayed as one HIP graph; on this stack that measured slower
@@ -424,6 +429,11 @@ def main():
             others.append(time_workload(torch, fm, synth, name, max(3, args.steps // 2), 2,
                                         min(0.2, args.min_warmup_s), graph=name in graphable and args.graph))
             torch.cuda.empty_cache()
+        # the sparse block mask again on the 64 x 64 table (two block rows per
+        # workgroup, each walking its own list)
+        others.append(time_workload(torch, fm, synth, "block_bitmap_16k", max(3, args.steps // 2), 2,
+                                    min(0.2, args.min_warmup_s), bm=64))
+        torch.cuda.empty_cache()
         for name in ("causal_doc_8k", "causal_doc_32k"):
             others.append(time_backward(torch, fm, synth, name, max(3, args.steps // 4), 2))
             torch.cuda.empty_cache()

@@ -303,6 +303,12 @@ fmask_status fmask_classify(const fmask_encoded *enc, int32_t bm, int32_t bn, vo
  * SELECTED kind, whose kernel walks the lists directly).  Tile shapes with a
  * kernel: BF16 INTERVALS 128x64 (preferred), 256x64, 64x64; BF16 BITMAP 128x64
  * (preferred), 64x64; F32 64x64.  Other shapes return FMASK_ERR_UNSUPPORTED.
+ * BF16 BITMAP at 128x64 walks, per 128-row tile, the key tiles where either
+ * of its two 64-row blocks is non-empty (one K/V load serves both); at 64x64
+ * a workgroup takes two block rows and each walks only its own non-empty
+ * blocks, which suits sparse block patterns (few blocks shared by
+ * neighbouring block rows: the Binary Block Masking abstract's extremely
+ * sparse masks).
  * Supported: BF16 with d in {64, 128} on INTERVALS / BITMAP; F32 with d in
  * {64, 128} on INTERVALS / BITMAP; BF16 with d in {128, 256}, sel_cells == 32
  * and hq / hkv in {1, 2, 4, 8, 12, 16} on SELECTED.                             */

@@ -642,6 +642,8 @@ fmask_status fmask_attn_fwd(const fmask_attn_args* a, const void* q, const void*
   if (a->dtype == FMASK_F32) e = launch_attn_tile_f32(p, a->d, s);
   else if (bm == 128 && (enc->kind == FMASK_ENC_INTERVALS || (enc->kind == FMASK_ENC_BITMAP && enc->pool_cap <= ((int64_t)1 << 22))))
     e = launch_attn_o3_bf16(p, a->d, s);
+  else if (bm == 64 && enc->kind == FMASK_ENC_BITMAP && enc->pool_cap <= ((int64_t)1 << 22))
+    e = launch_attn_pair_bf16(p, a->d, s);
   else e = launch_attn_tile_bf16(p, a->d, s);
   return hip_status(e, "attention kernel");
 }

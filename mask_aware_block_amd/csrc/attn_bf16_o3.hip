@@ -24,22 +24,12 @@
 // and at the end O goes out through LDS (whole 128-byte row pieces per store).
 #include <float.h>
 
+#include "attn_common.h"
 #include "device_util.h"
 #include "internal.h"
 
 namespace fmask {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-
-#define LDS_AS FMASK_LDS_AS
-#define INLINE __attribute__((always_inline))
 
 constexpr int BN = 64;
 constexpr int NW = 4;
@@ -47,10 +37,6 @@ constexpr int NT = 64 * NW;
 constexpr int BM = 32 * NW;
 constexpr int kList = 256;  // tile-list entries staged in LDS
 constexpr int kBinfo = 128;  // bitmap: list entries whose block info is staged in LDS
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazyMax = 4294967296.f;  // 2^kLazyLog2 with kLazyLog2 = 32: bound on a lane's share of a row sum
-constexpr int kQkAhead = 3;  // K fragments read ahead of their MFMA
-constexpr int kPvAhead = 3;  // V^T fragments read ahead of their MFMA
 
 template <int D>
 struct Geo {
@@ -66,25 +52,6 @@ struct Geo {
   static constexpr int LOADS = BN * KCH / NT;
   static_assert(BN * KCH % NT == 0, "tile must split evenly over the workgroup");
 };
-
-template <int KCH>
-__device__ inline int kswz(int key) { return key & (KCH - 1); }
-template <int KCH>
-__device__ inline int vswz(int key) {
-  return KCH == 16 ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
-}
-
-// max / sum of x over lanes l and l ^ 32.  v_permlane32_swap of x with itself
-// leaves {x[l], x[l ^ 32]} in some order in the two results (no LDS round
-// trip, unlike a lane shuffle).
-__device__ inline float pair_max(float x) {
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-}
-__device__ inline float pair_sum(float x) {
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-}
 
 struct Item {
   int b, h, kvh, mb, mh, qt, row;
@@ -137,10 +104,6 @@ __device__ inline Item set_item(const TileAttnParams& p, int l) {
   it.qt = it.row % p.nqt;
   return it;
 }
-
-// Block info of a 64 x 64 bitmap block: its pool index if PARTIAL, else
-// kBlkFull or kBlkSkip.
-constexpr int kBlkFull = -1, kBlkSkip = -2;
 
 template <int D, int KIND>
 __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {

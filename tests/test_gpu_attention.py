@@ -218,6 +218,47 @@ def test_bitmap_long_tile_rows():
         compare(w, o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"long rows bm {bm}")
 
 
+def _tile_check(w, spec, bm, what):
+    arrays = synth.draw_qkv(w)
+    q, k, v = to_device(w, arrays)
+    enc = fm.encode(spec)
+    tiles = fm.classify(enc, bm, 64)
+    o, lse = fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"])
+    torch.cuda.synchronize()
+    qq, kk, vv = (to_f64(w, a) for a in arrays)
+    ro, rl = OA.attention_dense(qq, kk, vv, OA.spec_vis_fn(spec), w["scale"])
+    return compare(w, o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, what)
+
+
+def test_bitmap_pairs_per_head_masks():
+    """64 x 64 bitmap tables (two block rows per workgroup, each walking its
+    own list): per-(batch, head) block patterns of different densities, GQA,
+    ragged keys, one block row with an empty list."""
+    S, K, B, Hq, Hkv = 450, 515, 2, 4, 2
+    w = _small("bf16", 128, S, K, B=B, Hq=Hq, Hkv=Hkv, seed=31)
+    rng = np.random.default_rng(32)
+    nbq, nbk = -(-S // 64), -(-K // 64)
+    sts, ixs, pools, off = [], [], [], 0
+    for i in range(B * Hq):
+        pf = (0.05, 0.2, 0.5, 0.9)[i % 4]
+        st, ix, bits = synth.block_pattern(rng, nbq, nbk, pf, 0.1)
+        if i == 1:
+            st[3] = 0  # block row 3 of (batch 0, head 1): nothing visible
+            npart = int((st == 1).sum())
+            ix = np.full(st.shape, -1, dtype=np.int32)
+            ix[st == 1] = np.arange(npart, dtype=np.int32)
+            bits = np.resize(bits, (npart, 64))
+        sts.append(st)
+        ixs.append(np.where(ix >= 0, ix + off, -1))
+        pools.append(np.asarray(bits, dtype=np.uint64).reshape(-1, 64))
+        off += pools[-1].shape[0]
+    spec = dict(family="block_bitmap", sq=S, skv=K, batch=B, heads=Hq,
+                blk_state=np.stack(sts).reshape(B, Hq, nbq, nbk),
+                blk_index=np.stack(ixs).reshape(B, Hq, nbq, nbk).astype(np.int32),
+                blk_bits=np.concatenate(pools).reshape(-1, 64), force_diag=False)
+    _tile_check(w, spec, 64, "bitmap pairs, per-head masks")
+
+
 def test_xcd_set_major_items():
     """Items dealt to the XCDs by whole (K/V head, batch) sets (16 sets of
     6 tile rows x 16 heads, per-batch masks and one shared mask, ragged)."""
@@ -236,6 +277,8 @@ def test_xcd_set_major_items():
                 blk_state=np.stack(sts)[:, None], blk_index=np.stack(ixs)[:, None].astype(np.int32),
                 blk_bits=np.concatenate(pools).reshape(-1, 64), force_diag=True)
     _dense_check(w, spec, "set-major bitmap per batch")
+    # the 64 x 64 table: pairs of block rows (11 rows: the last pair has one)
+    _tile_check(w, spec, 64, "set-major bitmap per batch, 64-row pairs")
     raw = rng.integers(-10, S + 10, size=(B, 1, 4, S)).astype(np.int32)
     _dense_check(w, dict(family="intervals", sq=S, skv=S, batch=B, heads=1, raw_intervals=raw),
                  "set-major intervals per batch")

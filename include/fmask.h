@@ -220,7 +220,8 @@ typedef struct fmask_encoded {
  * visible, FULL if all are, PARTIAL otherwise (exact, element by element).
  * list[b][h][qt][0..count) holds the non-SKIP kt in ascending order, with
  * FMASK_LIST_FULL_BIT set for FULL tiles.  order[] lists the batch*heads*nqt
- * tile rows (index (b*heads + h)*nqt + qt) by decreasing count, ties by index.   */
+ * tile rows (index (b*heads + h)*nqt + qt): the nqt rows of mask slice (b, h)
+ * occupy order[(b*heads + h)*nqt ...] in decreasing count, ties by index.      */
 typedef struct fmask_tiles {
   int32_t bm, bn;
   int32_t nqt, nkt;
@@ -276,8 +277,9 @@ size_t fmask_classify_bytes(const fmask_encoded *enc, int32_t bm, int32_t bn);
 
 /* Reduce an INTERVALS or BITMAP encoding to the exact per-tile SKIP / PARTIAL /
  * FULL table at tile size bm x bn, plus per-row compact lists of the non-SKIP
- * tiles and a longest-first order of tile rows (tile classifier).  bm and bn are
- * multiples of 16 in [16, 256]; the BITMAP kind needs multiples of 64.
+ * tiles and a per-slice longest-first order of tile rows (tile classifier).
+ * bm and bn are multiples of 16 in [16, 256]; the BITMAP kind needs multiples
+ * of 64.
  * Defining passages: the FlashMask rebuttal ("Response to Weaknesses and
  * Questions": the kernel's tiling block size is separate from the mask's
  * block size, and fully masked blocks are not computed); the Binary Block

@@ -203,10 +203,15 @@ __global__ void __launch_bounds__(256) k_tile_order(const int32_t* count, int32_
     for (int k = 0; k < 2; ++k) key[threadIdx.x + 256 * k] = v[k];
     __syncthreads();
     const int lim = min(512, scan_hi - base);
+    if (scan_hi - scan_lo <= seg) {  // the block's rows lie in one slice: every key counts
 #pragma unroll 8
-    for (int i = 0; i < lim; ++i) {
-      const int y = base + i;
-      rank += (key[i] > kx) & (y >= lo) & (y < hi);
+      for (int i = 0; i < lim; ++i) rank += key[i] > kx;
+    } else {
+#pragma unroll 8
+      for (int i = 0; i < lim; ++i) {
+        const int y = base + i;
+        rank += (key[i] > kx) & (y >= lo) & (y < hi);
+      }
     }
   }
   if (x < rows) order[rank] = x;

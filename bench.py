@@ -77,7 +77,7 @@ def visible_pairs_bitmap(torch, enc):
 EV_EVERY = 4  # timed steps per sampled attention launch (each recorded event costs the stream microseconds)
 
 
-def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5, graph=False, bm=None):
+def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5, graph=False, bm=None, blocks=False):
     w = synth.workload(name)
     q, k, v = (_bf16(torch, a) if w["dtype"] == "bf16" else torch.from_numpy(a).cuda()
                for a in synth.draw_qkv(w))
@@ -93,6 +93,10 @@ def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5, graph
     # (bm: tile rows of the table; None = the library's preferred tile)
     tile = dict(bm=bm, bn=64) if bm else {}
     bufs = [enc0.buf, None if selected else fm.classify(enc0, dtype=w["dtype"], d=w["D"], **tile).buf]
+    # (blocks: selected-key lists run in the block-major form, its workspace
+    # allocated once like the other buffers)
+    ws = (torch.empty(fm.attn_blocks_workspace_bytes(q, k, v, enc0), dtype=torch.uint8, device="cuda")
+          if blocks else None)
 
     def step(ev=None, attn_only=False):
         # (each recorded event costs the stream a few microseconds, so the timed
@@ -107,7 +111,10 @@ def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5, graph
         tiles = None if selected else fm.classify(enc, dtype=w["dtype"], d=w["D"], out=bufs[1], **tile)
         if ev:
             ev[2].record(stream)
-        fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"], out=o, lse=lse)
+        if blocks:
+            fm.attn_fwd_blocks(q, k, v, enc, scale=w["scale"], out=o, lse=lse, workspace=ws)
+        else:
+            fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"], out=o, lse=lse)
         if ev:
             ev[3].record(stream)
         return enc, tiles
@@ -167,6 +174,7 @@ def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5, graph
                step_launch="hip graph replay" if graph else "eager",
                attn_ms_median=float(np.median(att)), attn_ms_min=float(np.min(att)))
     if selected:
+        rec["form"] = "block-major" if blocks else "per-query"
         ls, cn = enc.lists()
         cells = int(cn.sum().item()) * w["mask"]["sel_cells"]  # listed cells per (b, query)
         nvis = cells * w["Hq"]                                 # every head of the query
@@ -382,6 +390,8 @@ def main():
     ap.add_argument("--only", default=None,
                     help="time only this workload (a forward workload name, e.g. selected_key_128k) and print its "
                          "own JSON line (for profiling runs)")
+    ap.add_argument("--blocks", action="store_true",
+                    help="with --only on a selected-key workload: the block-major form")
     ap.add_argument("--bm", type=int, default=None,
                     help="with --only: tile rows of the table (default: the library's preferred tile)")
     ap.add_argument("--dense-only", action="store_true",
@@ -414,7 +424,7 @@ def main():
         return
     if args.only:
         print(json.dumps(time_workload(torch, fm, synth, args.only, args.steps, args.warmup, args.min_warmup_s,
-                                       bm=args.bm)))
+                                       bm=args.bm, blocks=args.blocks)))
         return
     # (--graph: steps of mask families whose encoder records kernel launches
     # only are replayed as one HIP graph; on this stack that measured slower
@@ -430,9 +440,13 @@ def main():
                                         min(0.2, args.min_warmup_s), graph=name in graphable and args.graph))
             torch.cuda.empty_cache()
         # the sparse block mask again on the 64 x 64 table (two block rows per
-        # workgroup, each walking its own list)
+        # workgroup, each walking its own list), and the selected-key lists in
+        # the block-major form
         others.append(time_workload(torch, fm, synth, "block_bitmap_16k", max(3, args.steps // 2), 2,
                                     min(0.2, args.min_warmup_s), bm=64))
+        torch.cuda.empty_cache()
+        others.append(time_workload(torch, fm, synth, "selected_key_128k", max(3, args.steps // 2), 2,
+                                    min(0.2, args.min_warmup_s), blocks=True))
         torch.cuda.empty_cache()
         for name in ("causal_doc_8k", "causal_doc_32k"):
             others.append(time_backward(torch, fm, synth, name, max(3, args.steps // 4), 2))

@@ -353,6 +353,33 @@ fmask_status fmask_attn_fwd_split_noalloc(const fmask_attn_args *args, const voi
                                           const void *v, void *o, float *lse,
                                           const fmask_encoded *enc, int32_t splits, void *stream);
 
+/* Bytes of device workspace fmask_attn_fwd_blocks needs; 0 if the arguments
+ * are invalid.  About b * sq * sel_n * hq * (2 d + 8) bytes: a partial state
+ * per (batch, query, list entry, query head).                                  */
+size_t fmask_attn_blocks_workspace_bytes(const fmask_attn_args *args, const fmask_encoded *enc);
+
+/* Block-major form of fmask_attn_fwd for the SELECTED kind, meant for many
+ * queries (prefill over a selected-key context).  Defining passage: the
+ * selected-key PR (visibility only from each query's list of 32-cell blocks,
+ * an empty list giving a zero row; the split-K merge of partial states with
+ * factors exp(m_s - max m), an empty part carrying m = -FLT_MAX).  Same
+ * result as fmask_attn_fwd up to rounding: the lists are inverted into, per
+ * block, the (query, entry) pairs that name it; each block's K and V are then
+ * read once per K/V head and scored against the Q rows of those queries, which
+ * gives one partial state (maximum, sum, O / sum rounded to bf16) per
+ * (batch, query, entry, head) in `workspace`; a second kernel merges each
+ * query's partials in entry order.  The result does not depend on the order
+ * in which pairs reach a block.
+ * Supported: BF16, d in {128, 256}, sel_cells == 32, hq / hkv in
+ * {1, 2, 4, 8, 12, 16}, sq < 2^23.  workspace: device, 256-byte aligned, at
+ * least fmask_attn_blocks_workspace_bytes(args, enc) bytes (else
+ * FMASK_ERR_CAPACITY before any launch); its contents on entry do not
+ * matter.  Kernels only, asynchronous on `stream`; calls that share a
+ * workspace must be ordered by the caller.                                     */
+fmask_status fmask_attn_fwd_blocks(const fmask_attn_args *args, const void *q, const void *k,
+                                   const void *v, void *o, float *lse, const fmask_encoded *enc,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
 /* Bytes of device workspace fmask_attn_bwd needs: two floats per (batch, q
  * head, query row) and the tile table by key-tile column (per column the
  * non-SKIP query tiles, their count, and a longest-first order of the

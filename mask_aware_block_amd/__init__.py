@@ -85,7 +85,7 @@ class AttnArgs(ctypes.Structure):
 
 EXPORTS = ("fmask_encode_bytes", "fmask_encode", "fmask_classify_bytes", "fmask_classify",
            "fmask_attn_fwd", "fmask_attn_split_workspace_bytes", "fmask_attn_fwd_split",
-           "fmask_attn_fwd_split_noalloc",
+           "fmask_attn_fwd_split_noalloc", "fmask_attn_blocks_workspace_bytes", "fmask_attn_fwd_blocks",
            "fmask_attn_bwd_workspace_bytes", "fmask_attn_bwd",
            "fmask_preferred_tile", "fmask_status_str", "fmask_last_error")
 
@@ -128,6 +128,11 @@ def lib():
         L.fmask_attn_fwd_split_noalloc.argtypes = [ctypes.POINTER(AttnArgs), _vp, _vp, _vp, _vp, _vp,
                                                    ctypes.POINTER(Encoded), ctypes.c_int32, _vp]
         L.fmask_attn_fwd_split_noalloc.restype = ctypes.c_int32
+        L.fmask_attn_blocks_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(Encoded)]
+        L.fmask_attn_blocks_workspace_bytes.restype = ctypes.c_size_t
+        L.fmask_attn_fwd_blocks.argtypes = [ctypes.POINTER(AttnArgs), _vp, _vp, _vp, _vp, _vp,
+                                            ctypes.POINTER(Encoded), _vp, ctypes.c_size_t, _vp]
+        L.fmask_attn_fwd_blocks.restype = ctypes.c_int32
         L.fmask_attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(Tiles)]
         L.fmask_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.fmask_attn_bwd.argtypes = [ctypes.POINTER(AttnArgs)] + [_vp] * 10 + [
@@ -451,6 +456,36 @@ def attn_fwd_split_noalloc(q, k, v, enc, splits=0, scale=None, out=None, lse=Non
     a = attn_args(q, k, v, out, scale)
     st = L.fmask_attn_fwd_split_noalloc(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                         ctypes.byref(enc.struct), int(splits), _stream_handle(stream))
+    _check(st)
+    return out, lse
+
+
+def attn_blocks_workspace_bytes(q, k, v, enc):
+    """Bytes of device workspace attn_fwd_blocks needs (fmask_attn_blocks_workspace_bytes)."""
+    return lib().fmask_attn_blocks_workspace_bytes(ctypes.byref(attn_args(q, k, v, q, 1.0)),
+                                                   ctypes.byref(enc.struct))
+
+
+def attn_fwd_blocks(q, k, v, enc, scale=None, out=None, lse=None, workspace=None, stream=None):
+    """Block-major form of attn_fwd for selected-key lists (fmask_attn_fwd_blocks):
+    each listed block's K and V are read once per K/V head and scored against
+    the queries that name it; the per-entry partial states are merged per query.
+    workspace: optional uint8 device buffer of attn_blocks_workspace_bytes bytes."""
+    torch = _torch()
+    L = lib()
+    if scale is None:
+        scale = 1.0 / float(q.shape[-1]) ** 0.5
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    a = attn_args(q, k, v, out, scale)
+    nbytes = L.fmask_attn_blocks_workspace_bytes(ctypes.byref(a), ctypes.byref(enc.struct))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = L.fmask_attn_fwd_blocks(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                 ctypes.byref(enc.struct), _ptr(workspace), workspace.numel(),
+                                 _stream_handle(stream))
     _check(st)
     return out, lse
 

@@ -748,6 +748,55 @@ fmask_status fmask_attn_fwd_split_noalloc(const fmask_attn_args* a, const void* 
                    stream);
 }
 
+size_t fmask_attn_blocks_workspace_bytes(const fmask_attn_args* a, const fmask_encoded* enc) {
+  if (!a || !enc || enc->kind != FMASK_ENC_SELECTED || a->b < 1 || a->hkv < 1 || a->hq < 1 ||
+      a->hq % a->hkv || a->sq < 0 || a->sq > kMaxSeq || a->skv < 0 || a->skv > kMaxSeq ||
+      (a->d != 128 && a->d != 256) || enc->sel_n < 0 || enc->batch < 1)
+    return 0;
+  SelAttnParams p{};
+  p.b = a->b; p.hq = a->hq; p.hkv = a->hkv; p.sq = (int32_t)a->sq; p.skv = (int32_t)a->skv;
+  p.n = enc->sel_n; p.mb = enc->batch;
+  return std::max<size_t>(selected_blocks_layout(p, a->d).total, kAlign);
+}
+
+fmask_status fmask_attn_fwd_blocks(const fmask_attn_args* a, const void* q, const void* k, const void* v,
+                                   void* o, float* lse, const fmask_encoded* enc, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!a || !enc) return fail(FMASK_ERR_INVALID, "null args or encoding");
+  if (enc->kind != FMASK_ENC_SELECTED) return fail(FMASK_ERR_UNSUPPORTED, "block-major form: SELECTED encoding only");
+  if (a->b < 1 || a->hq < 1 || a->hkv < 1 || a->hq % a->hkv)
+    return fail(FMASK_ERR_INVALID, "need b, hq, hkv >= 1 and hq %% hkv == 0");
+  if (a->sq < 0 || a->skv < 0 || a->sq > kMaxSeq || a->skv > kMaxSeq)
+    return fail(FMASK_ERR_INVALID, "sq / skv out of range");
+  if (a->sq != enc->sq || a->skv != enc->skv) return fail(FMASK_ERR_INVALID, "sq / skv differ from the encoding");
+  if (!(enc->batch == 1 || enc->batch == a->b)) return fail(FMASK_ERR_INVALID, "encoding batch must be 1 or b");
+  if (a->sq >= ((int64_t)1 << 23)) return fail(FMASK_ERR_UNSUPPORTED, "block-major form: fewer than 2^23 queries");
+  if (!q || !k || !v || !o) return fail(FMASK_ERR_INVALID, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(FMASK_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
+  for (int i = 0; i < 3; ++i) {
+    if (a->q_stride[i] % 8 || a->k_stride[i] % 8 || a->v_stride[i] % 8 || a->o_stride[i] % 8)
+      return fail(FMASK_ERR_UNSUPPORTED, "strides must be multiples of 8 elements");
+    if (a->q_stride[i] < 0 || a->k_stride[i] < 0 || a->v_stride[i] < 0 || a->o_stride[i] < 0)
+      return fail(FMASK_ERR_INVALID, "negative stride");
+  }
+  {  // 32-bit buffer offsets inside one (batch, K/V head)
+    const int64_t lim = ((int64_t)1 << 31) - 1;
+    if ((a->skv + 32) * a->k_stride[2] * 2 > lim || (a->skv + 32) * a->v_stride[2] * 2 > lim)
+      return fail(FMASK_ERR_UNSUPPORTED, "one K/V head must span less than 2 GiB");
+  }
+  SelAttnParams p{};
+  const fmask_status st = selected_params(a, q, k, v, o, lse, enc, &p);
+  if (st != FMASK_OK) return st;
+  const size_t need = fmask_attn_blocks_workspace_bytes(a, enc);
+  if (!workspace || ((uintptr_t)workspace % 256)) return fail(FMASK_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(FMASK_ERR_CAPACITY, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  return hip_status(launch_attn_selected_blocks_bf16(p, a->d, workspace, (hipStream_t)stream),
+                    "selected-key block-major kernels");
+}
+
 }  // extern "C"
 
 namespace {

@@ -196,4 +196,14 @@ hipError_t launch_attn_selected_bf16(const SelAttnParams& p, int32_t d, int32_t 
 bool selected_group_supported(int32_t group);
 size_t selected_split_ws_floats(const SelAttnParams& p, int32_t d, int32_t nsplit);
 
+// Block-major form of the selected-key forward: workspace pieces (byte offsets)
+// for the block index, the per-(batch, query, entry, head) partial states
+// and their bf16 outputs.
+struct BlkLayout {
+  int32_t nblk = 0;
+  size_t hist = 0, off = 0, inv = 0, pm = 0, po = 0, total = 0;
+};
+BlkLayout selected_blocks_layout(const SelAttnParams& p, int32_t d);
+hipError_t launch_attn_selected_blocks_bf16(const SelAttnParams& p, int32_t d, void* ws, hipStream_t s);
+
 }  // namespace fmask

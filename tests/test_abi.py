@@ -161,6 +161,18 @@ def test_split_backward_varlen_dense_host_validation():
     assert L.fmask_attn_fwd_split_noalloc(ctypes.byref(a), p, p, p, p, None, None, 0, None) == fm.ERR_INVALID
     assert L.fmask_attn_split_workspace_bytes(ctypes.byref(a), ctypes.byref(iv_enc), 4) == 0
     assert L.fmask_attn_split_workspace_bytes(ctypes.byref(a), ctypes.byref(sel), 4) > 0
+    # block-major selected form: SELECTED encodings only, a workspace of at least the queried size
+    assert L.fmask_attn_blocks_workspace_bytes(ctypes.byref(a), ctypes.byref(iv_enc)) == 0
+    sel.blk = 32
+    need_b = L.fmask_attn_blocks_workspace_bytes(ctypes.byref(a), ctypes.byref(sel))
+    assert need_b >= 512 * 64 * 8 * (2 * 128 + 8)
+    assert L.fmask_attn_fwd_blocks(ctypes.byref(a), p, p, p, p, None, ctypes.byref(iv_enc), p, need_b,
+                                   None) == fm.ERR_UNSUPPORTED
+    assert L.fmask_attn_fwd_blocks(ctypes.byref(a), p, p, p, p, None, ctypes.byref(sel), p, need_b - 256,
+                                   None) == fm.ERR_CAPACITY
+    assert L.fmask_attn_fwd_blocks(None, p, p, p, p, None, ctypes.byref(sel), p, need_b, None) == fm.ERR_INVALID
+    assert L.fmask_attn_fwd_blocks(ctypes.byref(a), p, p, p, p, None, ctypes.byref(sel), None, need_b,
+                                   None) == fm.ERR_INVALID
     # backward: bf16 only, 128 x 64 tables, workspace at least the queried size
     t = fm.Tiles()
     t.bm, t.bn, t.nqt, t.nkt, t.batch, t.heads = 128, 64, 4, 8, 1, 1

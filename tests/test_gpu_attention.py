@@ -358,7 +358,7 @@ def test_poison_masked_kv_does_not_leak():
 
 
 def test_poison_unselected_blocks_do_not_leak():
-    """Selected-key lists (one-pass and split forms): NaN in every K/V block that
+    """Selected-key lists (one-pass, split and block-major forms): NaN in every K/V block that
     no query lists must not reach the output (those blocks are never gathered;
     the selected-key PR's poison cases).  The lists hold -1 entries, duplicates
     and an out-of-range index; the last block is ragged."""
@@ -378,11 +378,12 @@ def test_poison_unselected_blocks_do_not_leak():
         q_, k_, v_ = to_device(w, arr)
         o1, l1 = fm.attn_fwd(q_, k_, v_, enc, None, scale=w["scale"])
         o2, l2 = fm.attn_fwd_split(q_, k_, v_, enc, splits=3, scale=w["scale"])
+        o3, l3 = fm.attn_fwd_blocks(q_, k_, v_, enc, scale=w["scale"])
         torch.cuda.synchronize()
-        outs.append([t.float().cpu().numpy() for t in (o1, l1, o2, l2)])
+        outs.append([t.float().cpu().numpy() for t in (o1, l1, o2, l2, o3, l3)])
     for a, b in zip(*outs):
         np.testing.assert_array_equal(a, b)
-    assert np.isfinite(outs[1][0]).all()
+    assert np.isfinite(outs[1][0]).all() and np.isfinite(outs[1][4]).all()
 
 
 @pytest.mark.parametrize("bm", [128, 64])

@@ -75,9 +75,60 @@ def visible_pairs_bitmap(torch, enc):
 
 
 EV_EVERY = 4  # timed steps per sampled attention launch (each recorded event costs the stream microseconds)
+DATASHEET_SCLK_MHZ = 2400.0  # the clock PEAK_BF16_TFLOPS assumes
 
 
-def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5, graph=False, bm=None, blocks=False):
+class ClockMonitor:
+    """The GPU's graphics clock in MHz, sampled every ~2 ms from sysfs
+    (pp_dpm_sclk: the level marked current) in a daemon thread between start()
+    and stop().  Under sustained MFMA load the clock settles well below the
+    datasheet's 2.4 GHz, so the bench also reports the fraction of the peak at
+    the clock measured over the timed steps.  Inactive where the file is absent."""
+
+    def __init__(self):
+        import glob
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if paths else None
+        self.samples = []
+        self._stop = False
+        self._thread = None
+
+    def _read(self):
+        with open(self.path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):  # e.g. "1: 1749Mhz *"
+                    return float(line.split(":")[1].strip().lower().split("mhz")[0])
+        return None
+
+    def _run(self):
+        while not self._stop:
+            try:
+                v = self._read()
+            except (OSError, ValueError, IndexError):
+                v = None
+            if v:
+                self.samples.append(v)
+            time.sleep(0.002)
+
+    def start(self):
+        if self.path:
+            import threading
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        self._stop = True
+        if self._thread:
+            self._thread.join()
+        if not self.samples:
+            return None
+        a = np.array(self.samples)
+        return dict(mean=float(a.mean()), min=float(a.min()), max=float(a.max()), samples=int(a.size),
+                    source=self.path)
+
+
+def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5, graph=False, bm=None, blocks=False,
+                  clock=False):
     w = synth.workload(name)
     q, k, v = (_bf16(torch, a) if w["dtype"] == "bf16" else torch.from_numpy(a).cuda()
                for a in synth.draw_qkv(w))
@@ -130,12 +181,16 @@ def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5, graph
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
+    mon = ClockMonitor() if clock else None
+    if mon:
+        mon.start()
     t0 = time.perf_counter()
     for i in range(steps):
         # (events around every EV_EVERY-th attention launch of the timed region)
         enc, tiles = step(evs[i] if i % EV_EVERY == 0 else None, attn_only=True)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
+    sclk = mon.stop() if mon else None
     eager_wall = wall
     att = [a[2].elapsed_time(a[3]) for i, a in enumerate(evs) if i % EV_EVERY == 0]
     # breakdown pass (not timed): encoder and classifier launches
@@ -173,6 +228,8 @@ def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5, graph
                classify_ms=float(t_cls), attn_ms=float(t_att), eager_ms_per_step=eager_wall * 1e3,
                step_launch="hip graph replay" if graph else "eager",
                attn_ms_median=float(np.median(att)), attn_ms_min=float(np.min(att)))
+    if sclk:
+        rec["sclk_mhz"] = sclk
     if selected:
         rec["form"] = "block-major" if blocks else "per-query"
         ls, cn = enc.lists()
@@ -431,7 +488,7 @@ def main():
     # than launching them eagerly, so eager is the default.)
     graphable = {"causal_doc_32k", "causal_doc_8k", "shared_question_32k", "band_32k", "band_neg_4k"}
     head = time_workload(torch, fm, synth, "causal_doc_32k", args.steps, args.warmup, args.min_warmup_s,
-                         graph=args.graph)
+                         graph=args.graph, clock=True)
     others = []
     if not args.headline_only:
         for name in ("causal_doc_8k", "shared_question_32k", "band_32k", "band_neg_4k", "varlen_prefill_32k",
@@ -480,8 +537,16 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "k_attn_o3<128> (128x64 tiles, intervals)",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic()},
+        # the same peak scaled to the graphics clock measured over the timed steps
+        # (null where the clock cannot be read)
+        "sclk_mhz": head.get("sclk_mhz"),
         "workloads": others,
     }
+    if head.get("sclk_mhz"):
+        f = head["sclk_mhz"]["mean"] / DATASHEET_SCLK_MHZ
+        out["roofline"]["peak_at_sclk"] = PEAK_BF16_TFLOPS * f
+        out["roofline"]["frac_at_sclk"] = achieved / (PEAK_BF16_TFLOPS * f)
+        out["fraction_of_peak_at_sclk"] = head["effective_tflops"] / (PEAK_BF16_TFLOPS * f)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(synth, "causal_doc_32k", args.cpu_rows, args.cpu_heads)
     print(json.dumps(out))

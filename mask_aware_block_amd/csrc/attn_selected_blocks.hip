@@ -33,6 +33,16 @@ namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));  // (m, l) of a partial state
 
+// Direct-to-LDS 16-byte load (as dma16 in device_util.h: M0, one wait state,
+// the load) with the non-temporal hint, for data read once: streamed past L2
+// rather than evicting what is read again.
+__device__ inline void dma16_nt(rsrc_t r, int voff, int lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :
+               : "s"(lds), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+
 constexpr int CELLS = 32;
 constexpr int NW = 4;
 constexpr int NT = 64 * NW;

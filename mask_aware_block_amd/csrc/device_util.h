@@ -51,14 +51,6 @@ __device__ inline void dma16s(rsrc_t r, int voff, int soff, int lds) {
                : "s"(lds), "v"(voff), "s"(r), "s"(soff)
                : "memory", "m0");
 }
-// Same with the non-temporal hint, for data read once (streamed past L2
-// rather than evicting data that is read again).
-__device__ inline void dma16_nt(rsrc_t r, int voff, int lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
-               :
-               : "s"(lds), "v"(voff), "s"(r)
-               : "memory", "m0");
-}
 __device__ inline void dma4(rsrc_t r, int voff, int lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :

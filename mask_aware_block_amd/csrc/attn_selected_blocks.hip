@@ -391,17 +391,17 @@ hipError_t launch_attn_selected_blocks_bf16(const SelAttnParams& p, int32_t d, v
   const int64_t nh = (int64_t)p.mb * L.nblk;
   const int64_t ne = (int64_t)p.mb * p.sq * p.n;
   auto grid = [](int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 65535 * 4); };
-  hipLaunchKernelGGL(k_blk_clear, dim3(grid(nh)), dim3(256), 0, s, hist, nh);
+  if (nh > 0) hipLaunchKernelGGL(k_blk_clear, dim3(grid(nh)), dim3(256), 0, s, hist, nh);
   hipLaunchKernelGGL(k_blk_hist, dim3(grid(ne)), dim3(256), 0, s, p.list, p.count, p.mb, p.sq, p.n, L.nblk, hist);
   hipLaunchKernelGGL(k_blk_scan, dim3((unsigned)p.mb), dim3(1024), 0, s, hist, L.nblk, off);
   hipLaunchKernelGGL(k_blk_scatter, dim3(grid(ne)), dim3(256), 0, s, p.list, p.count, p.mb, p.sq, p.n, L.nblk,
                      off, hist, inv);
-  const int64_t items = (int64_t)p.hkv * p.b * L.nblk;
+  const int64_t items = (int64_t)p.hkv * p.b * L.nblk;  // 0 without keys: every list is empty
   const int64_t per = (items + kXcds - 1) / kXcds;
-  if (d == 256)
+  if (items > 0 && d == 256)
     hipLaunchKernelGGL((k_blk_partial<256>), dim3((unsigned)(per * kXcds)), dim3(NT), 0, s, p, L.nblk, items, off,
                        inv, pm, po);
-  else
+  else if (items > 0)
     hipLaunchKernelGGL((k_blk_partial<128>), dim3((unsigned)(per * kXcds)), dim3(NT), 0, s, p, L.nblk, items, off,
                        inv, pm, po);
   const unsigned nbq = (unsigned)((int64_t)p.b * p.sq);

@@ -11,6 +11,7 @@ blocks listed; the full 128K workload on sampled rows; bit-identical results
 on a second call (the scatter's atomics order the pairs differently).
 """
 
+import ctypes
 import math
 
 import numpy as np
@@ -112,3 +113,29 @@ def test_blocks_full_size_sampled():
                                        decode=OA.bf16_bits_to_f64)
     idx = tuple(np.array(samples).T)
     compare(w, o.float().cpu().numpy()[idx], lse.cpu().numpy()[idx], ro, rl, "selected_key_128k blocks")
+
+
+def test_blocks_degenerate_sizes():
+    """One key, one query; and no key at all (every list empty: O = 0 and
+    LSE = -inf, with no partial-state kernel launched)."""
+    for sq, skv in ((5, 1), (1, 33)):
+        _check_all_rows(_workload(1, sq, skv, 128, 4, 2, 59 + skv, per_batch=True, n=8), f"blocks sq {sq} skv {skv}")
+    # skv = 0 through the C ABI (a zero-row tensor has no device pointer in the
+    # binding): valid one-row K and V buffers, skv set to 0 in the arguments
+    sq = 7
+    spec = dict(family="selected_key", sq=sq, skv=0, batch=1, sel=np.full((1, sq, 8), -1, np.int32), sel_cells=32)
+    enc = fm.encode(spec)
+    q = torch.randn(1, 4, sq, 128, device="cuda").to(torch.bfloat16)
+    kv = torch.zeros(1, 2, 1, 128, dtype=torch.bfloat16, device="cuda")
+    o = torch.full_like(q, 5.0)
+    lse = torch.zeros(1, 4, sq, dtype=torch.float32, device="cuda")
+    a = fm.attn_args(q, kv, kv, o, 1 / math.sqrt(128))
+    a.skv = 0
+    L = fm.lib()
+    need = L.fmask_attn_blocks_workspace_bytes(ctypes.byref(a), ctypes.byref(enc.struct))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    st = L.fmask_attn_fwd_blocks(ctypes.byref(a), fm._ptr(q), fm._ptr(kv), fm._ptr(kv), fm._ptr(o), fm._ptr(lse),
+                                 ctypes.byref(enc.struct), fm._ptr(ws), need, None)
+    torch.cuda.synchronize()
+    assert st == fm.OK
+    assert bool((o == 0).all()) and bool(torch.isneginf(lse).all())

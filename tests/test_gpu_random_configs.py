@@ -104,7 +104,7 @@ def _case(seed):
     return w, spec, rng
 
 
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", range(96))
 def test_random_configuration(seed):
     w, spec, rng = _case(seed)
     desc = (f"seed {seed}: {spec['family']} B{w['B']} Hq{w['Hq']} Hkv{w['Hkv']} Sq{w['Sq']} Skv{w['Skv']} "

@@ -253,6 +253,11 @@ def time_workload(torch, fm, synth, name, steps, warmup, min_warmup_s=0.5, graph
                    tiles=dict(bm=tiles.struct.bm, bn=tiles.struct.bn,
                               skip=int((st == 0).sum().item()), partial=int((st == 1).sum().item()),
                               full=int((st == 2).sum().item())))
+        if enc.kind == fm.ENC_INTERVALS:
+            # the mask as the kernels read it (four int32 per key column and mask
+            # slice) against a dense bool mask of the same slices
+            rec["mask_bytes"] = dict(intervals=int(enc.intervals().numel() * 4),
+                                     dense_bool=int(enc.struct.batch * enc.struct.heads * w["Sq"] * w["Skv"]))
         if "doc_lengths" in w:
             exp = sum(L * (L + 1) // 2 for L in w["doc_lengths"]) * w["B"] * w["Hq"]
             assert exp == nvis, (exp, nvis)
@@ -530,7 +535,7 @@ def main():
         "config": {"workload": "causal_document_32k", "step_launch": head["step_launch"],
                    "eager_ms_per_step": head["eager_ms_per_step"], "batch": 1, "q_heads": 32, "kv_heads": 8,
                    "seq_len": 32768, "head_dim": 128, "doc_lengths": head["doc_lengths"],
-                   "visible_pairs": head["visible_pairs"]},
+                   "visible_pairs": head["visible_pairs"], "mask_bytes": head.get("mask_bytes")},
         "fraction_of_peak": head["effective_tflops"] / PEAK_BF16_TFLOPS,
         "step_breakdown_ms": {"encode": head["encode_ms"], "classify": head["classify_ms"],
                               "attention": head["attn_ms"]},

@@ -428,6 +428,44 @@ __global__ void __launch_bounds__(256) k_bitmap_state(BitmapSrc s, uint8_t* stat
   if (r == 0) state[blk] = any ? (all ? FMASK_FULL : FMASK_PARTIAL) : FMASK_SKIP;
 }
 
+// Caller bitmaps (kind 0): one wave per 64 consecutive blocks, lane = block.
+// A block whose input state is FULL stays FULL (its words are all visible, on
+// ragged edges too) and one that is neither FULL nor PARTIAL stays SKIP (its
+// words are zero), unless force_diag puts diagonal cells into it; the rest
+// (PARTIAL input, diagonal blocks) are decided exactly from their 64 row words
+// by the whole wave, one block at a time.  Same states as k_bitmap_state, with
+// one wave per 64 blocks instead of one per block.
+__global__ void __launch_bounds__(256) k_bitmap_state_lanes(BitmapSrc s, uint8_t* state) {
+  const int64_t nblocks = (int64_t)s.nmask * s.nbq * s.nbk;
+  const int64_t b0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;
+  const int lane = threadIdx.x & 63;
+  if (b0 >= nblocks) return;  // whole wave leaves together
+  const int64_t b = b0 + lane;
+  bool exact = false;
+  if (b < nblocks) {
+    const int bj = (int)(b % s.nbk);
+    const int bi = (int)((b / s.nbk) % s.nbq);
+    const uint8_t st = s.state[b];
+    if (st == FMASK_FULL) state[b] = FMASK_FULL;
+    else if (st == FMASK_PARTIAL || (s.force_diag && bi == bj)) exact = true;
+    else state[b] = FMASK_SKIP;
+  }
+  uint64_t todo = __ballot(exact);
+  while (todo) {
+    const int64_t blk = b0 + __builtin_ctzll(todo);
+    todo &= todo - 1;
+    const int bj = (int)(blk % s.nbk);
+    const int bi = (int)((blk / s.nbk) % s.nbq);
+    const int m = (int)(blk / ((int64_t)s.nbk * s.nbq));
+    const uint64_t w = source_word(s, m, bi, bj, lane);
+    const bool row_valid = (int64_t)bi * kBlk + lane < s.sq;
+    const bool full = !row_valid || w == col_mask(s.skv, bj);
+    const bool any = __any(w != 0);
+    const bool all = __all(full);
+    if (lane == 0) state[blk] = any ? (all ? FMASK_FULL : FMASK_PARTIAL) : FMASK_SKIP;
+  }
+}
+
 // One wave per block row: row-local rank of every PARTIAL block, and the count.
 __global__ void __launch_bounds__(256) k_bitmap_row_rank(const uint8_t* state, int32_t rows,
                                                          int32_t nbk, int32_t* index,
@@ -491,6 +529,30 @@ __global__ void __launch_bounds__(256) k_bitmap_words(BitmapSrc s, BitmapOut o) 
   __builtin_amdgcn_wave_barrier();
   if (r == 0) o.index[blk] = (int32_t)g;
   if (g < o.cap) o.bits[g * kBlk + r] = source_word(s, m, bi, bj, r);
+}
+
+// Caller bitmaps: one wave per 64 consecutive blocks; the wave writes the
+// pool words of its PARTIAL blocks one block at a time (lane = row), as
+// k_bitmap_words does with one wave per block.
+__global__ void __launch_bounds__(256) k_bitmap_words_lanes(BitmapSrc s, BitmapOut o) {
+  const int64_t nblocks = (int64_t)s.nmask * s.nbq * s.nbk;
+  const int64_t b0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;
+  const int lane = threadIdx.x & 63;
+  if (b0 >= nblocks) return;  // whole wave leaves together
+  const int32_t local = b0 + lane < nblocks ? o.index[b0 + lane] : -1;
+  uint64_t todo = __ballot(local >= 0);
+  while (todo) {
+    const int src = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    const int64_t blk = b0 + src;
+    const int bj = (int)(blk % s.nbk);
+    const int64_t row = blk / s.nbk;
+    const int bi = (int)(row % s.nbq);
+    const int m = (int)(row / s.nbq);
+    const int64_t g = (int64_t)o.row_offset[row] + __shfl(local, src);
+    if (lane == 0) o.index[blk] = (int32_t)g;  // every lane read its index before the loop
+    if (g < o.cap) o.bits[g * kBlk + lane] = source_word(s, m, bi, bj, lane);
+  }
 }
 
 // ------------------------------------------------------------------ selected
@@ -559,12 +621,15 @@ hipError_t launch_encode_bitmap(const BitmapSrc& src, const BitmapOut& out, hipS
   int32_t rows = src.nmask * src.nbq;
   if (nblocks <= 0) return hipSuccess;
   int g4 = (int)((nblocks + 3) / 4);
-  hipLaunchKernelGGL(k_bitmap_state, dim3(g4), dim3(256), 0, s, src, out.state);
+  const int g256 = (int)((nblocks + 255) / 256);
+  if (src.kind == 0) hipLaunchKernelGGL(k_bitmap_state_lanes, dim3(g256), dim3(256), 0, s, src, out.state);
+  else hipLaunchKernelGGL(k_bitmap_state, dim3(g4), dim3(256), 0, s, src, out.state);
   hipLaunchKernelGGL(k_bitmap_row_rank, dim3((rows + 3) / 4), dim3(256), 0, s, out.state, rows,
                      src.nbk, out.index, out.row_count);
   hipLaunchKernelGGL(k_exclusive_scan, dim3(1), dim3(1024), 0, s, out.row_count, rows,
                      out.row_offset, out.pool_count);
-  hipLaunchKernelGGL(k_bitmap_words, dim3(g4), dim3(256), 0, s, src, out);
+  if (src.kind == 0) hipLaunchKernelGGL(k_bitmap_words_lanes, dim3(g256), dim3(256), 0, s, src, out);
+  else hipLaunchKernelGGL(k_bitmap_words, dim3(g4), dim3(256), 0, s, src, out);
   return hipGetLastError();
 }
 

@@ -377,3 +377,28 @@ def test_caller_buffers_reused_across_calls():
         assert tg.buf.data_ptr() == tbuf.data_ptr()
         for x, y in zip(tr.arrays(), tg.arrays()):
             assert torch.equal(x, y)
+
+
+def test_tile_order_per_slice_at_scale():
+    """The per-slice longest-first order when slices do not align with the
+    order kernel's 256-row blocks: 2 x 2 mask slices of 300 tile rows each
+    (64 x 64 tiles), raw intervals with row-dependent lengths; the order must
+    equal the oracle's tile_order of the same counts, slice by slice."""
+    rng = np.random.default_rng(77)
+    B, H, S, K = 2, 2, 300 * 64, 5 * 64 + 9
+    raw = np.zeros((B, H, 4, K), dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            # column c masks rows [c_lo, c_hi): per-column random runs give rows
+            # a spread of list lengths, with ties
+            lo = rng.integers(0, S, size=K)
+            raw[b, h, 0] = lo
+            raw[b, h, 1] = np.minimum(S, lo + rng.integers(0, S // 2, size=K))
+            raw[b, h, 2] = S
+            raw[b, h, 3] = S
+    enc = fm.encode(dict(family="intervals", sq=S, skv=K, batch=B, heads=H, raw_intervals=raw))
+    t = fm.classify(enc, 64, 64)
+    st, ls, cn, od = [x.cpu().numpy() for x in t.arrays()]
+    assert cn.shape == (B, H, 300)
+    np.testing.assert_array_equal(od, OE.tile_order(cn.ravel(), 300))
+    assert sorted(od.tolist()) == list(range(B * H * 300))

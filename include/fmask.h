@@ -371,7 +371,9 @@ size_t fmask_attn_blocks_workspace_bytes(const fmask_attn_args *args, const fmas
  * query's partials in entry order.  The result does not depend on the order
  * in which pairs reach a block.
  * Supported: BF16, d in {128, 256}, sel_cells == 32, hq / hkv in
- * {1, 2, 4, 8, 12, 16}, sq < 2^23.  workspace: device, 256-byte aligned, at
+ * {1, 2, 4, 8, 12, 16}, sq < 2^23, 1 <= sel_n <= FMASK_MAX_SEL_N (checked
+ * here too, for encodings not made by fmask_encode: FMASK_ERR_INVALID).
+ * workspace: device, 256-byte aligned, at
  * least fmask_attn_blocks_workspace_bytes(args, enc) bytes (else
  * FMASK_ERR_CAPACITY before any launch); its contents on entry do not
  * matter.  Kernels only, asynchronous on `stream`; calls that share a

@@ -751,7 +751,7 @@ fmask_status fmask_attn_fwd_split_noalloc(const fmask_attn_args* a, const void* 
 size_t fmask_attn_blocks_workspace_bytes(const fmask_attn_args* a, const fmask_encoded* enc) {
   if (!a || !enc || enc->kind != FMASK_ENC_SELECTED || a->b < 1 || a->hkv < 1 || a->hq < 1 ||
       a->hq % a->hkv || a->sq < 0 || a->sq > kMaxSeq || a->skv < 0 || a->skv > kMaxSeq ||
-      (a->d != 128 && a->d != 256) || enc->sel_n < 0 || enc->batch < 1)
+      (a->d != 128 && a->d != 256) || enc->sel_n < 0 || enc->sel_n > FMASK_MAX_SEL_N || enc->batch < 1)
     return 0;
   SelAttnParams p{};
   p.b = a->b; p.hq = a->hq; p.hkv = a->hkv; p.sq = (int32_t)a->sq; p.skv = (int32_t)a->skv;
@@ -772,6 +772,10 @@ fmask_status fmask_attn_fwd_blocks(const fmask_attn_args* a, const void* q, cons
   if (a->sq != enc->sq || a->skv != enc->skv) return fail(FMASK_ERR_INVALID, "sq / skv differ from the encoding");
   if (!(enc->batch == 1 || enc->batch == a->b)) return fail(FMASK_ERR_INVALID, "encoding batch must be 1 or b");
   if (a->sq >= ((int64_t)1 << 23)) return fail(FMASK_ERR_UNSUPPORTED, "block-major form: fewer than 2^23 queries");
+  // (the merge gives each list entry one lane of a wave; an encoding filled in
+  // by hand must keep fmask_encode's limit)
+  if (enc->sel_n < 1 || enc->sel_n > FMASK_MAX_SEL_N)
+    return fail(FMASK_ERR_INVALID, "sel_n must be in [1, %d]", FMASK_MAX_SEL_N);
   if (!q || !k || !v || !o) return fail(FMASK_ERR_INVALID, "null tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(FMASK_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");

@@ -173,6 +173,13 @@ def test_split_backward_varlen_dense_host_validation():
     assert L.fmask_attn_fwd_blocks(None, p, p, p, p, None, ctypes.byref(sel), p, need_b, None) == fm.ERR_INVALID
     assert L.fmask_attn_fwd_blocks(ctypes.byref(a), p, p, p, p, None, ctypes.byref(sel), None, need_b,
                                    None) == fm.ERR_INVALID
+    # a hand-filled encoding with lists past FMASK_MAX_SEL_N (the merge has one lane per entry)
+    sel.sel_n = 65
+    assert L.fmask_attn_blocks_workspace_bytes(ctypes.byref(a), ctypes.byref(sel)) == 0
+    assert L.fmask_attn_fwd_blocks(ctypes.byref(a), p, p, p, p, None, ctypes.byref(sel), p, need_b,
+                                   None) == fm.ERR_INVALID
+    assert b"sel_n" in L.fmask_last_error()
+    sel.sel_n = 64
     # backward: bf16 only, 128 x 64 tables, workspace at least the queried size
     t = fm.Tiles()
     t.bm, t.bn, t.nqt, t.nkt, t.batch, t.heads = 128, 64, 4, 8, 1, 1

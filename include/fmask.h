@@ -33,6 +33,10 @@
  *    FMASK_ERR_UNSUPPORTED instead.
  *  - fmask_last_error() gives a human-readable detail of the last failure on the
  *    calling thread.
+ *  - Sizes: sq and skv at most 2^30, batch * heads at most 2^31 - 1 masks.  A
+ *    problem whose encoding, tile table or workspace would exceed 2^44 bytes is
+ *    refused with FMASK_ERR_UNSUPPORTED, and the matching *_bytes query returns
+ *    0 for it (size arithmetic never wraps).
  */
 #ifndef FMASK_H
 #define FMASK_H

@@ -67,5 +67,47 @@ def build(extra=(), verbose=False):
     return LIB
 
 
+# Host-only build for the sanitizers: the host side of every source (argument
+# checks, size arithmetic, descriptor validation) under AddressSanitizer and
+# UndefinedBehaviorSanitizer, with no device code at all, so that it loads and
+# runs where there is no GPU.  Each -fsanitize= applies to the host pass only.
+# Each object embeds an empty GPU binary where the device pass would put the
+# kernels' code object, so the library links and loads with no kernel in it.
+SANITIZE_HOST = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+]
+CLANGXX = os.environ.get("CLANGXX", "/opt/rocm/llvm/bin/clang++")
+
+
+def build_host_sanitized(outdir):
+    """Compile the host side of every source with ASan and UBSan into
+    outdir/libfmask_host_san.so (no device code); returns its path."""
+    os.makedirs(outdir, exist_ok=True)
+    empty = os.path.join(outdir, "no_kernels.bin")
+    open(empty, "wb").close()
+
+    def comp(src):
+        obj = os.path.join(outdir, os.path.basename(src) + ".o")
+        cmd = [HIPCC, *FLAGS, "--offload-host-only", "-Xclang", "-fcuda-include-gpubinary", "-Xclang", empty,
+               *SANITIZE_HOST, "-g", "-O1", "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"host-only compile failed on {src}:\n{r.stderr}")
+        return obj
+
+    srcs = sources()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(comp, srcs))
+    lib = os.path.join(outdir, "libfmask_host_san.so")
+    # (host objects only: linked by the host compiler with the sanitizer runtimes)
+    link = [CLANGXX, "-shared", "-fsanitize=address,undefined", *objs, "-L/opt/rocm/lib", "-lamdhip64",
+            "-Wl,-rpath,/opt/rocm/lib", "-o", lib]
+    r = subprocess.run(link, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
     build(extra=sys.argv[1:], verbose=True)

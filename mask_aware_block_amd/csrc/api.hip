@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <initializer_list>
 #include <mutex>
 #include <vector>
 
@@ -36,6 +37,23 @@ constexpr int64_t kMaxSeq = (int64_t)1 << 30;
 constexpr int32_t kMaxTree = 4096;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Every buffer the library sizes stays below 2^44 bytes (far past any GPU's
+// memory), so that the size arithmetic below never overflows.
+constexpr int64_t kMaxBytes = (int64_t)1 << 44;
+
+// Product of non-negative factors when it is at most lim, else -1; no partial
+// product overflows (a zero factor gives 0 whatever the others are).
+int64_t bounded_prod(std::initializer_list<int64_t> xs, int64_t lim) {
+  for (int64_t x : xs)
+    if (x == 0) return 0;
+  int64_t r = 1;
+  for (int64_t x : xs) {
+    if (x < 0 || r > lim / x) return -1;
+    r *= x;
+  }
+  return r;
+}
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -78,11 +96,30 @@ fmask_status tree_check(const fmask_mask_desc* d, bool* contiguous) {
   return FMASK_OK;
 }
 
+fmask_status check_family(const fmask_mask_desc* d, int* kind);
+
 fmask_status check_desc(const fmask_mask_desc* d, int* kind) {
   if (!d) return fail(FMASK_ERR_INVALID, "null mask descriptor");
   if (d->sq < 0 || d->skv < 0 || d->sq > kMaxSeq || d->skv > kMaxSeq)
     return fail(FMASK_ERR_INVALID, "sq / skv out of range [0, 2^30]");
   if (d->batch < 1 || d->heads < 1) return fail(FMASK_ERR_INVALID, "batch and heads must be >= 1");
+  const int64_t nmask = (int64_t)d->batch * d->heads;
+  if (nmask > INT32_MAX) return fail(FMASK_ERR_UNSUPPORTED, "batch * heads: at most 2^31 - 1 masks");
+  const fmask_status st = check_family(d, kind);
+  if (st != FMASK_OK) return st;
+  // storage of the encoding (the automatic dense form reserves both forms)
+  const bool dense_auto = d->family == FMASK_DENSE && d->dense_form == 0;
+  bool fits = true;
+  if (*kind == FMASK_ENC_INTERVALS) fits = bounded_prod({nmask, d->skv, 16}, kMaxBytes) >= 0;
+  if (*kind == FMASK_ENC_BITMAP || dense_auto)
+    fits = fits && bounded_prod({nmask, ceil_div(d->sq, kBlk), ceil_div(d->skv, kBlk), kBlk * 8 + 8}, kMaxBytes) >= 0;
+  if (*kind == FMASK_ENC_SELECTED) fits = bounded_prod({d->batch, d->sq, d->sel_n, 4}, kMaxBytes) >= 0;
+  if (!fits) return fail(FMASK_ERR_UNSUPPORTED, "the encoding would exceed 2^44 bytes");
+  return FMASK_OK;
+}
+
+// Family-specific checks of a descriptor; sets the kind it encodes to.
+fmask_status check_family(const fmask_mask_desc* d, int* kind) {
   const int f = d->family;
   if (is_param_family(f) && (d->batch != 1 || d->heads != 1))
     return fail(FMASK_ERR_INVALID, "family %d describes one mask: batch = heads = 1", f);
@@ -161,7 +198,7 @@ fmask_status check_desc(const fmask_mask_desc* d, int* kind) {
       if (d->sq > 0 && d->skv > 0 && !d->dense) return fail(FMASK_ERR_INVALID, "dense mask missing");
       if (d->dense_form != 0 && d->dense_form != FMASK_ENC_INTERVALS && d->dense_form != FMASK_ENC_BITMAP)
         return fail(FMASK_ERR_INVALID, "dense_form must be 0, FMASK_ENC_INTERVALS or FMASK_ENC_BITMAP");
-      if ((int64_t)d->batch * d->heads * d->sq * d->skv > ((int64_t)1 << 40) ||
+      if (bounded_prod({(int64_t)d->batch * d->heads, d->sq, d->skv}, (int64_t)1 << 40) < 0 ||
           (int64_t)d->batch * d->heads * ceil_div(d->skv, 64) > INT32_MAX)
         return fail(FMASK_ERR_UNSUPPORTED, "dense mask too large");
       // the interval form is tried first unless the bitmap form is asked for
@@ -244,6 +281,9 @@ fmask_status check_tiles_args(const fmask_encoded* e, int32_t bm, int32_t bn) {
     return fail(FMASK_ERR_INVALID, "BITMAP tiles must be multiples of 64");
   if (e->batch < 1 || e->heads < 1 || e->sq < 0 || e->skv < 0 || e->sq > kMaxSeq || e->skv > kMaxSeq)
     return fail(FMASK_ERR_INVALID, "malformed encoding");
+  const int64_t rows = bounded_prod({(int64_t)e->batch * e->heads, ceil_div(e->sq, bm)}, INT32_MAX);
+  if (rows < 0 || bounded_prod({rows, ceil_div(e->skv, bn)}, (int64_t)1 << 40) < 0)
+    return fail(FMASK_ERR_UNSUPPORTED, "tile table too large");
   return FMASK_OK;
 }
 
@@ -298,7 +338,8 @@ fmask_status selected_params(const fmask_attn_args* a, const void* q, const void
   p->sq = (int32_t)a->sq; p->skv = (int32_t)a->skv; p->scale = a->scale;
   p->list = enc->sel_list; p->count = enc->sel_count;
   p->n = enc->sel_n; p->cells = enc->blk; p->mb = enc->batch;
-  if ((int64_t)a->hkv * a->b * a->sq * 16 > INT32_MAX) return fail(FMASK_ERR_UNSUPPORTED, "grid too large");
+  if (bounded_prod({(int64_t)a->hkv * a->b, a->sq, 16}, INT32_MAX) < 0)
+    return fail(FMASK_ERR_UNSUPPORTED, "grid too large");
   return FMASK_OK;
 }
 
@@ -357,7 +398,7 @@ fmask_status fmask_encode(const fmask_mask_desc* desc, void* out, size_t out_byt
   hipStream_t s = (hipStream_t)stream;
   const int f = desc->family;
   const int32_t sq = (int32_t)desc->sq, skv = (int32_t)desc->skv;
-  const int32_t nmask = desc->batch * desc->heads;
+  const int32_t nmask = (int32_t)((int64_t)desc->batch * desc->heads);  // <= 2^31 - 1 (check_desc)
 
   memset(enc, 0, sizeof(*enc));
   enc->kind = kind;
@@ -525,8 +566,6 @@ fmask_status fmask_classify(const fmask_encoded* enc, int32_t bm, int32_t bn, vo
   if (!out || ((uintptr_t)out % kAlign)) return fail(FMASK_ERR_INVALID, "out must be 256-byte aligned");
   const TileLayout T = tile_layout(enc, bm, bn);
   if (out_bytes < T.total) return fail(FMASK_ERR_CAPACITY, "out has %zu bytes, %zu needed", out_bytes, T.total);
-  if (T.rows > INT32_MAX || T.rows * T.nkt > ((int64_t)1 << 40))
-    return fail(FMASK_ERR_UNSUPPORTED, "tile table too large");
   hipStream_t s = (hipStream_t)stream;
   memset(tiles, 0, sizeof(*tiles));
   tiles->bm = bm;
@@ -543,7 +582,7 @@ fmask_status fmask_classify(const fmask_encoded* enc, int32_t bm, int32_t bn, vo
   tiles->list = list;
   tiles->count = count;
   tiles->order = order;
-  const int32_t nmask = enc->batch * enc->heads;
+  const int32_t nmask = (int32_t)((int64_t)enc->batch * enc->heads);  // rows <= 2^31 - 1 (check_tiles_args)
   hipError_t e;
   if (enc->kind == FMASK_ENC_INTERVALS)
     e = launch_classify_intervals(enc->intervals, nmask, (int32_t)enc->sq, (int32_t)enc->skv, bm, bn,
@@ -620,9 +659,10 @@ fmask_status fmask_attn_fwd(const fmask_attn_args* a, const void* q, const void*
   p.list = tiles->list; p.count = tiles->count; p.order = tiles->order;
   p.nqt = tiles->nqt; p.nkt = tiles->nkt; p.bm = bm; p.bn = bn;
   p.mb = enc->batch; p.mh = enc->heads;
-  p.expand = (enc->batch == 1 ? a->b : 1) * (enc->heads == 1 ? a->hq : 1);
-  const int64_t items = (int64_t)enc->batch * enc->heads * tiles->nqt * p.expand;
-  if (items > INT32_MAX / 2) return fail(FMASK_ERR_UNSUPPORTED, "grid too large");
+  const int64_t expand = (int64_t)(enc->batch == 1 ? a->b : 1) * (enc->heads == 1 ? a->hq : 1);
+  const int64_t items = bounded_prod({(int64_t)enc->batch * enc->heads, tiles->nqt, expand}, INT32_MAX / 2);
+  if (items < 0) return fail(FMASK_ERR_UNSUPPORTED, "grid too large");
+  p.expand = (int32_t)expand;
   p.n_items = (int32_t)items;
   {
     // (K/V head, batch) sets dealt whole to the XCDs (o3 kernel) when they
@@ -652,9 +692,11 @@ size_t fmask_attn_split_workspace_bytes(const fmask_attn_args* a, const fmask_en
   if (!a || !enc || enc->kind != FMASK_ENC_SELECTED || splits < 0 || a->b < 1 || a->hkv < 1 ||
       a->hq < 1 || a->hq % a->hkv || a->sq < 0 || a->sq > kMaxSeq)
     return 0;
+  if (a->d < 1 || bounded_prod({(int64_t)a->hq * a->b, a->sq, 4}, kMaxBytes) < 0) return 0;
   const int32_t ns = splits == 0 ? auto_splits(a, enc->sel_n) : splits;
-  const size_t floats = (size_t)a->hkv * a->b * a->sq * ns * (size_t)(a->hq / a->hkv) * (a->d + 2);
-  return std::max<size_t>(floats * sizeof(float), kAlign);
+  // a partial (m, l, O) per (batch, query head, query, split): d + 2 floats
+  const int64_t bytes = bounded_prod({(int64_t)a->hq * a->b, a->sq, ns, (int64_t)a->d + 2, 4}, kMaxBytes);
+  return bytes < 0 ? 0 : std::max<size_t>((size_t)bytes, kAlign);
 }
 
 }  // extern "C"
@@ -689,6 +731,7 @@ fmask_status split_fwd(const fmask_attn_args* a, const void* q, const void* k, c
   if (st != FMASK_OK) return st;
   const int32_t ns = splits == 0 ? auto_splits(a, enc->sel_n) : splits;
   const size_t need = fmask_attn_split_workspace_bytes(a, enc, ns);
+  if (need == 0) return fail(FMASK_ERR_UNSUPPORTED, "split form: partial states would exceed 2^44 bytes");
   if (ns > 1) {
     if (!workspace || ((uintptr_t)workspace % 16)) return fail(FMASK_ERR_INVALID, "%s must be 16-byte aligned", what_ws);
     if (workspace_bytes < need)
@@ -753,6 +796,7 @@ size_t fmask_attn_blocks_workspace_bytes(const fmask_attn_args* a, const fmask_e
       a->hq % a->hkv || a->sq < 0 || a->sq > kMaxSeq || a->skv < 0 || a->skv > kMaxSeq ||
       (a->d != 128 && a->d != 256) || enc->sel_n < 0 || enc->sel_n > FMASK_MAX_SEL_N || enc->batch < 1)
     return 0;
+  if (bounded_prod({(int64_t)a->b * a->hq, a->sq, enc->sel_n, 2 * a->d + 8}, kMaxBytes) < 0) return 0;
   SelAttnParams p{};
   p.b = a->b; p.hq = a->hq; p.hkv = a->hkv; p.sq = (int32_t)a->sq; p.skv = (int32_t)a->skv;
   p.n = enc->sel_n; p.mb = enc->batch;
@@ -794,6 +838,7 @@ fmask_status fmask_attn_fwd_blocks(const fmask_attn_args* a, const void* q, cons
   const fmask_status st = selected_params(a, q, k, v, o, lse, enc, &p);
   if (st != FMASK_OK) return st;
   const size_t need = fmask_attn_blocks_workspace_bytes(a, enc);
+  if (need == 0) return fail(FMASK_ERR_UNSUPPORTED, "block-major form: partial states would exceed 2^44 bytes");
   if (!workspace || ((uintptr_t)workspace % 256)) return fail(FMASK_ERR_INVALID, "workspace must be 256-byte aligned");
   if (workspace_bytes < need)
     return fail(FMASK_ERR_CAPACITY, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
@@ -826,6 +871,10 @@ extern "C" {
 size_t fmask_attn_bwd_workspace_bytes(const fmask_attn_args* a, const fmask_tiles* t) {
   if (!a || !t || a->b < 1 || a->hq < 1 || a->sq < 0 || a->sq > kMaxSeq || t->batch < 1 || t->heads < 1 ||
       t->nqt < 0 || t->nkt < 0)
+    return 0;
+  const int64_t cols = bounded_prod({(int64_t)t->batch * t->heads, t->nkt}, INT32_MAX);
+  if (bounded_prod({(int64_t)a->b * a->hq, a->sq, 8}, kMaxBytes) < 0 || cols < 0 ||
+      bounded_prod({cols, (int64_t)t->nqt + 2, 4}, kMaxBytes) < 0)
     return 0;
   return bwd_layout(a, t).total;
 }
@@ -863,6 +912,7 @@ fmask_status fmask_attn_bwd(const fmask_attn_args* a, const void* q, const void*
       return fail(FMASK_ERR_INVALID, "negative stride");
   }
   const size_t need = fmask_attn_bwd_workspace_bytes(a, tiles);
+  if (need == 0) return fail(FMASK_ERR_UNSUPPORTED, "backward: workspace would exceed 2^44 bytes");
   if (!workspace || ((uintptr_t)workspace % 16)) return fail(FMASK_ERR_INVALID, "workspace must be 16-byte aligned");
   if (workspace_bytes < need)
     return fail(FMASK_ERR_CAPACITY, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
@@ -870,7 +920,8 @@ fmask_status fmask_attn_bwd(const fmask_attn_args* a, const void* q, const void*
   if ((a->skv + 64) * a->k_stride[2] * 2 > lim || (a->skv + 64) * a->v_stride[2] * 2 > lim ||
       (a->sq + 128) * a->q_stride[2] * 2 > lim || (a->sq + 128) * a->o_stride[2] * 2 > lim)
     return fail(FMASK_ERR_UNSUPPORTED, "one head must span less than 2 GiB");
-  if ((int64_t)a->b * a->hq * a->sq > INT32_MAX / 4) return fail(FMASK_ERR_UNSUPPORTED, "problem too large");
+  if (bounded_prod({(int64_t)a->b * a->hq, a->sq}, INT32_MAX / 4) < 0)
+    return fail(FMASK_ERR_UNSUPPORTED, "problem too large");
   BwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
   p.dq = dq; p.dk = dk; p.dv = dv;

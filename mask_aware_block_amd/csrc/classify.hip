@@ -177,20 +177,25 @@ __global__ void __launch_bounds__(256) k_tile_cols(const uint8_t* state, int32_t
 // slice of the tile table) under (count descending, index ascending), plus the
 // slice's first row: the rank is unique, so order[rank] = row is a permutation
 // that lists slice 0's rows longest first, then slice 1's, and so on.
+// A workgroup ranks 64 rows (lane = row); its four waves count the larger keys
+// in four quarters of each 512-key chunk of the slices those rows fall in, and
+// the quarters' counts are summed through LDS.
 __global__ void __launch_bounds__(256) k_tile_order(const int32_t* count, int32_t rows, int32_t seg,
                                                     int32_t* order) {
   // Row y's key count[y] * 2^32 + (2^32 - 1 - y): the rank of row x is the
-  // slice start plus the number of larger keys in its slice, one 64-bit
-  // compare per row of the slices this block's rows fall in.
+  // slice start plus the number of larger keys in its slice.
   __shared__ __attribute__((aligned(16))) uint64_t key[512];
-  const int x = blockIdx.x * blockDim.x + threadIdx.x;
+  __shared__ int32_t part[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int x = blockIdx.x * 64 + lane;
   auto key_of = [](int32_t c, int y) -> uint64_t { return ((uint64_t)(uint32_t)c << 32) | (uint32_t)(~y); };
   const uint64_t kx = x < rows ? key_of(count[x], x) : 0ull;
   const int lo = x / seg * seg, hi = min(lo + seg, rows);
-  const int first = blockIdx.x * blockDim.x;
-  const int last = min(first + (int)blockDim.x, rows) - 1;
+  const int first = blockIdx.x * 64;
+  const int last = min(first + 64, rows) - 1;
   const int scan_lo = first / seg * seg, scan_hi = min((last / seg + 1) * seg, rows);
-  int rank = lo;
+  const bool one_slice = scan_hi - scan_lo <= seg;  // every key scanned is in the slice of every row here
+  int rank = 0;
   for (int base = scan_lo; base < scan_hi; base += 512) {
     __syncthreads();
     uint64_t v[2];  // both loads in flight before the stores; padding keys are 0
@@ -203,18 +208,21 @@ __global__ void __launch_bounds__(256) k_tile_order(const int32_t* count, int32_
     for (int k = 0; k < 2; ++k) key[threadIdx.x + 256 * k] = v[k];
     __syncthreads();
     const int lim = min(512, scan_hi - base);
-    if (scan_hi - scan_lo <= seg) {  // the block's rows lie in one slice: every key counts
+    const int q = (lim + 3) / 4, i0 = w * q, i1 = min(lim, i0 + q);  // this wave's quarter
+    if (one_slice) {
 #pragma unroll 8
-      for (int i = 0; i < lim; ++i) rank += key[i] > kx;
+      for (int i = i0; i < i1; ++i) rank += key[i] > kx;
     } else {
 #pragma unroll 8
-      for (int i = 0; i < lim; ++i) {
+      for (int i = i0; i < i1; ++i) {
         const int y = base + i;
         rank += (key[i] > kx) & (y >= lo) & (y < hi);
       }
     }
   }
-  if (x < rows) order[rank] = x;
+  part[w][lane] = rank;
+  __syncthreads();
+  if (w == 0 && x < rows) order[lo + part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane]] = x;
 }
 
 inline int grid_for(int64_t n, int per_block, int cap = 65535 * 16) {
@@ -275,7 +283,7 @@ hipError_t launch_tile_order(const int32_t* count, int32_t rows, int32_t seg, in
                              hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (seg <= 0 || seg > rows) seg = rows;
-  hipLaunchKernelGGL(k_tile_order, dim3((rows + 255) / 256), dim3(256), 0, s, count, rows, seg, order);
+  hipLaunchKernelGGL(k_tile_order, dim3((rows + 63) / 64), dim3(256), 0, s, count, rows, seg, order);
   return hipGetLastError();
 }
 

@@ -91,3 +91,58 @@ def test_every_row_full_size(name):
     for form, _, _ in forms:
         assert total[form] / n <= tol["mean_abs"], f"{name} ({form}): mean abs err {total[form] / n:.3e}"
         print(f"{name} ({form}): every row, max abs {worst[form]:.3e}, mean abs {total[form] / n:.3e}")
+
+
+def _reference_backward(q, k, v, do, spec, b, scale, G):
+    """fp32 dQ [Hq, Sq, D], dK and dV [Hkv, Skv, D] of one batch entry from the
+    definition: P = softmax(scale Q K^T) on visible cells, O = P V,
+    D_i = sum_d dO_id O_id, dS = P (dO V^T - D); dQ = scale dS K,
+    dK = scale dS^T Q, dV = P^T dO (dK, dV summed over each group's heads)."""
+    Hq, Sq, _ = q.shape
+    dq = torch.empty_like(q)
+    dk = torch.zeros_like(k)
+    dv = torch.zeros_like(v)
+    for r0 in range(0, Sq, CHUNK):
+        rows = np.arange(r0, min(Sq, r0 + CHUNK))
+        masked = ~torch.from_numpy(np.ascontiguousarray(OM.dense_vis(spec, b, 0, rows))).cuda()
+        for g in range(Hq // G):
+            qc = q[g * G:(g + 1) * G, r0:r0 + len(rows)]
+            dc = do[g * G:(g + 1) * G, r0:r0 + len(rows)]
+            s = torch.matmul(qc, k[g].t().contiguous()) * scale
+            s.masked_fill_(masked, float("-inf"))
+            p = torch.nan_to_num(torch.exp(s - torch.logsumexp(s, dim=-1, keepdim=True)), nan=0.0)
+            del s
+            o = torch.matmul(p, v[g])
+            ds = p * (torch.matmul(dc, v[g].t().contiguous()) - (dc * o).sum(-1, keepdim=True))
+            dq[g * G:(g + 1) * G, r0:r0 + len(rows)] = scale * torch.matmul(ds, k[g])
+            dk[g] += scale * torch.matmul(ds.transpose(1, 2).contiguous(), qc).sum(0)
+            dv[g] += torch.matmul(p.transpose(1, 2).contiguous(), dc).sum(0)
+            del p, ds, o
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("name", ["causal_doc_32k", "shared_question_32k"])
+def test_backward_every_row_full_size(name):
+    """dQ, dK and dV of every row and key at full size, against the fp32
+    evaluation above, within the backward's bounds (max abs 2e-2 and mean abs
+    2e-3 of the largest reference magnitude, as in the other backward tests)."""
+    w = synth.workload(name)
+    spec = w["mask"]
+    assert w["B"] == 1 and spec.get("heads", 1) == 1
+    q, k, v = to_device(w, synth.draw_qkv(w))
+    do = torch.from_numpy(synth.draw_dout(w).view(np.int16)).view(torch.bfloat16).cuda()
+    enc = fm.encode(spec)
+    tiles = fm.classify(enc, 128, 64)
+    o, lse = fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"])
+    dq, dk, dv = fm.attn_bwd(q, k, v, o, lse, do, enc, tiles, scale=w["scale"])
+    torch.cuda.synchronize()
+    G = w["Hq"] // w["Hkv"]
+    ref = _reference_backward(*(t[0].float().contiguous() for t in (q, k, v, do)), spec, 0, w["scale"], G)
+    for what, got, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        g = got[0].float()
+        assert bool(torch.isfinite(g).all()), f"{name}: {what} not finite"
+        mag = max(float(r.abs().max()), 1e-6)
+        err = (g - r).abs()
+        print(f"{name} {what}: max abs {float(err.max()):.3e}, mean abs {float(err.mean()):.3e} (ref max {mag:.3e})")
+        assert float(err.max()) <= 2e-2 * mag, f"{name}: {what} max abs err {float(err.max()):.3e}"
+        assert float(err.mean()) <= 2e-3 * mag, f"{name}: {what} mean abs err {float(err.mean()):.3e}"

@@ -504,6 +504,25 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
       const int cm = overlap(ra, ra + na, us, ue) + overlap(ra, ra + na, ls, le);
       const bool wskip = __ballot(!(key < p.skv) || cm == na) == ~0ull;
       const bool full = (e & (int)FMASK_LIST_FULL_BIT) && (kt + 1) * BN <= p.skv && na == 64;
+      // PARTIAL: bit r of `keep` says row ra + r (r < 64, after the shift by
+      // 4 half the bit of the row 4 half + r) is visible to this lane's key;
+      // built once per query tile from the key's two runs and the end of Q
+      uint64_t keep = 0;
+      if (!wskip && !full) {
+        auto rows = [&](int a, int b) -> uint64_t {  // bits [a - ra, b - ra) within [0, 64)
+          const int lo = min(max(a - ra, 0), 64), hi = min(max(b - ra, 0), 64);
+          const uint64_t below_hi = hi >= 64 ? ~0ull : ((1ull << hi) - 1ull);
+          const uint64_t below_lo = lo >= 64 ? ~0ull : ((1ull << lo) - 1ull);
+          return below_hi & ~below_lo;
+        };
+        keep = ~(rows(us, ue) | rows(ls, le) | rows(p.sq, ra + 64)) >> (4 * half);
+      }
+      // 0 where row offset `pos` of this lane (pos = 32 rb + 8 (r / 4) + r % 4)
+      // is masked, all ones where it is visible
+      auto keep_bits = [&](int pos) INLINE -> int32_t {
+        const uint32_t wd = pos < 32 ? (uint32_t)keep : (uint32_t)(keep >> 32);
+        return __builtin_amdgcn_sbfe((int32_t)wd, pos & 31, 1);
+      };
       if (!wskip) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
@@ -551,16 +570,14 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
               }
             }
             // element masks of a PARTIAL tile, in one pass over the 8 values
-            // (one uniform branch rather than one per element)
+            // (one uniform branch rather than one per element): a masked
+            // value's bits are cleared, i.e. it becomes +0
             if (!full) {
 #pragma unroll
               for (int j = 0; j < 8; ++j) {
-                const int grow = qt * BM + lr0 + 8 * (2 * tp + j / 4) + 4 * half + j % 4;
-                // (| rather than ||: three compares, no branches)
-                const bool masked = ((uint32_t)(grow - us) < (uint32_t)(ue - us)) |
-                                    ((uint32_t)(grow - ls) < (uint32_t)(le - ls)) | (grow >= p.sq);
-                xp[j] = masked ? 0.f : xp[j];
-                xs[j] = masked ? 0.f : xs[j];
+                const int32_t k = keep_bits(32 * rb + 8 * (2 * tp + j / 4) + j % 4);
+                xp[j] = __int_as_float(__float_as_int(xp[j]) & k);
+                xs[j] = __int_as_float(__float_as_int(xs[j]) & k);
               }
             }
             pb[tp] = __builtin_convertvector(xp, bf16x8);

@@ -50,8 +50,10 @@ __global__ void __launch_bounds__(256) k_classify_intervals(const int32_t* iv, i
 
 // The same rule with one wave per (mask, key tile, kQtPerWave query tiles)
 // when the tile is 64 keys wide: lane = key column, whose intervals are read
-// once; per query tile two ballots give "every column fully masked" (SKIP) and
-// "no column masked" (FULL), and lane qt % kQtPerWave keeps that tile's state
+// once.  For a power-of-two tile height every lane computes the tiles its runs
+// cover and touch directly and one AND over the wave settles all 16 tiles;
+// otherwise per query tile two ballots give "every column fully masked" (SKIP)
+// and "no column masked" (FULL).  Lane qt % kQtPerWave keeps that tile's state
 // for one store at the end.
 constexpr int kQtPerWave = 16;
 __global__ void __launch_bounds__(256) k_classify_intervals_cols(const int32_t* iv, int32_t nmask, int32_t sq,
@@ -72,10 +74,39 @@ __global__ void __launch_bounds__(256) k_classify_intervals_cols(const int32_t* 
   // Rows [r0, r1) of a column are all masked iff they lie inside one of its
   // runs (canonical runs neither overlap nor abut), and none is masked iff
   // neither (non-empty) run meets them: comparisons only, combined as lane masks.
-  const uint64_t cols = __ballot(col);
-  const uint64_t ne_u = __ballot(us < ue), ne_l = __ballot(ls < le);  // non-empty runs
   uint8_t mine = FMASK_SKIP;
   const int32_t q0 = qg * kQtPerWave, q1 = min(nqt, q0 + kQtPerWave);
+  if ((bm & (bm - 1)) == 0) {
+    // Power-of-two tile height: each lane turns its column's two runs into the
+    // tiles q0 .. q0 + 15 that they cover entirely (bits 0..15: SKIP needs this
+    // for every column) and the tiles they touch (bits 16..31 hold the tiles
+    // they leave untouched: FULL needs this for every column); one AND over
+    // the wave gives both.  Tile qt holds rows [qt bm, min(sq, (qt + 1) bm)).
+    static_assert(kQtPerWave == 16, "two 16-bit tile sets per word");
+    const int sh = __builtin_ctz(bm);
+    auto span = [&](int lo, int hi) -> uint32_t {  // tiles lo..hi, as bits relative to q0
+      const int a = max(lo - q0, 0), b = min(hi - q0 + 1, kQtPerWave);
+      return a < b ? ((1u << b) - 1u) & ~((1u << a) - 1u) : 0u;
+    };
+    auto covered = [&](int s0, int e0) -> uint32_t {  // every row of the tile in [s0, e0)
+      if (s0 >= e0) return 0u;
+      return span((s0 + bm - 1) >> sh, e0 >= sq ? nqt - 1 : (e0 >> sh) - 1);
+    };
+    auto touched = [&](int s0, int e0) -> uint32_t {  // some row of the tile in [s0, e0)
+      if (s0 >= e0 || s0 >= sq) return 0u;
+      return span(s0 >> sh, (min(e0, sq) - 1) >> sh);
+    };
+    uint32_t w = 0xffffffffu;  // columns past skv leave both sets whole
+    if (col) w = (covered(us, ue) | covered(ls, le)) | ((~(touched(us, ue) | touched(ls, le)) & 0xffffu) << 16);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) w &= (uint32_t)__shfl_xor((int)w, o);
+    if (lane < kQtPerWave)
+      mine = ((w >> lane) & 1u) ? FMASK_SKIP : (((w >> (16 + lane)) & 1u) ? FMASK_FULL : FMASK_PARTIAL);
+    if (q0 + lane < q1) state[(m * nqt + q0 + lane) * (int64_t)nkt + kt] = mine;
+    return;
+  }
+  const uint64_t cols = __ballot(col);
+  const uint64_t ne_u = __ballot(us < ue), ne_l = __ballot(ls < le);  // non-empty runs
   for (int32_t qt = q0; qt < q1; ++qt) {
     const int32_t r0 = qt * bm, r1 = min(sq, r0 + bm);
     // (one compare per ballot: the masks combine on the scalar unit)

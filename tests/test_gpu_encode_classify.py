@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 fm = pytest.importorskip("mask_aware_block_amd")
 
-TILE_SHAPES_IV = [(128, 64), (64, 64), (32, 48), (16, 16), (256, 128), (48, 208)]
+TILE_SHAPES_IV = [(128, 64), (64, 64), (256, 64), (16, 64), (48, 64), (32, 48), (16, 16), (256, 128), (48, 208)]
 TILE_SHAPES_BM = [(128, 64), (64, 64), (64, 128), (256, 192)]
 
 

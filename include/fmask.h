@@ -403,8 +403,11 @@ size_t fmask_attn_bwd_workspace_bytes(const fmask_attn_args *args, const fmask_t
  * Layouts: dQ like Q (q_stride), dK like K (k_stride), dV like V (v_stride),
  * O and dO share o_stride; LSE float [b][hq][sq] contiguous, as the forward
  * writes it.  workspace: device buffer of fmask_attn_bwd_workspace_bytes
- * bytes (16-byte aligned); its contents are rewritten by every call.  Supported: BF16, d in {64, 128}, INTERVALS encoding, the tile table
- * at 128 x 64 (fmask_preferred_tile); otherwise FMASK_ERR_UNSUPPORTED.         */
+ * bytes (16-byte aligned); its contents are rewritten by every call.
+ * Supported: BF16, d in {64, 128}, INTERVALS or BITMAP encodings (every
+ * family but selected-key lists; the bitmap form holds tree, block and dense
+ * masks), the tile table at 128 x 64 (fmask_preferred_tile); otherwise
+ * FMASK_ERR_UNSUPPORTED.                                                       */
 fmask_status fmask_attn_bwd(const fmask_attn_args *args, const void *q, const void *k,
                             const void *v, const void *o, const float *lse, const void *dout,
                             void *dq, void *dk, void *dv, void *workspace,

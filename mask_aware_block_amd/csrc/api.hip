@@ -287,6 +287,21 @@ fmask_status check_tiles_args(const fmask_encoded* e, int32_t bm, int32_t bn) {
   return FMASK_OK;
 }
 
+// The mask data the interval and bitmap kernels index: present, and for the
+// bitmap the block grid that sq and skv imply (a hand-filled descriptor with
+// another grid would send the kernels outside the block arrays).
+fmask_status check_mask_data(const fmask_encoded* e) {
+  if (e->kind == FMASK_ENC_INTERVALS) {
+    if (e->skv > 0 && !e->intervals) return fail(FMASK_ERR_INVALID, "null interval array");
+  } else if (e->kind == FMASK_ENC_BITMAP) {
+    if (e->blk != kBlk || e->nbq != ceil_div(e->sq, kBlk) || e->nbk != ceil_div(e->skv, kBlk))
+      return fail(FMASK_ERR_INVALID, "bitmap block grid does not match sq / skv");
+    if (e->nbq * e->nbk > 0 && (!e->blk_state || !e->blk_index || !e->blk_bits))
+      return fail(FMASK_ERR_INVALID, "null bitmap array");
+  }
+  return FMASK_OK;
+}
+
 TileLayout tile_layout(const fmask_encoded* e, int32_t bm, int32_t bn) {
   TileLayout T;
   Carve c;
@@ -561,6 +576,7 @@ fmask_status fmask_classify(const fmask_encoded* enc, int32_t bm, int32_t bn, vo
                             fmask_tiles* tiles, void* stream) {
   g_err[0] = 0;
   fmask_status st = check_tiles_args(enc, bm, bn);
+  if (st == FMASK_OK) st = check_mask_data(enc);
   if (st != FMASK_OK) return st;
   if (!tiles) return fail(FMASK_ERR_INVALID, "null fmask_tiles");
   if (!out || ((uintptr_t)out % kAlign)) return fail(FMASK_ERR_INVALID, "out must be 256-byte aligned");
@@ -635,6 +651,7 @@ fmask_status fmask_attn_fwd(const fmask_attn_args* a, const void* q, const void*
     return fail(FMASK_ERR_UNSUPPORTED, "tile kernels: d in {64, 128}");
   bm = tiles->bm;
   bn = tiles->bn;
+  if (check_mask_data(enc) != FMASK_OK) return FMASK_ERR_INVALID;
   if (!tile_supported(a->dtype, enc->kind, bm, bn)) {
     int32_t pbm = 0, pbn = 0;
     preferred(a->dtype, a->d, enc->kind, &pbm, &pbn);
@@ -887,7 +904,8 @@ fmask_status fmask_attn_bwd(const fmask_attn_args* a, const void* q, const void*
   if (!a || !enc || !tiles) return fail(FMASK_ERR_INVALID, "null args, encoding or tile table");
   if (a->dtype != FMASK_BF16) return fail(FMASK_ERR_UNSUPPORTED, "backward: bf16 only");
   if (a->d != 64 && a->d != 128) return fail(FMASK_ERR_UNSUPPORTED, "backward: d in {64, 128}");
-  if (enc->kind != FMASK_ENC_INTERVALS) return fail(FMASK_ERR_UNSUPPORTED, "backward: INTERVALS encoding only");
+  if (enc->kind != FMASK_ENC_INTERVALS && enc->kind != FMASK_ENC_BITMAP)
+    return fail(FMASK_ERR_UNSUPPORTED, "backward: INTERVALS or BITMAP encodings");
   if (a->b < 1 || a->hq < 1 || a->hkv < 1 || a->hq % a->hkv)
     return fail(FMASK_ERR_INVALID, "need b, hq, hkv >= 1 and hq %% hkv == 0");
   if (a->sq < 0 || a->skv < 0 || a->sq > kMaxSeq || a->skv > kMaxSeq)
@@ -900,6 +918,7 @@ fmask_status fmask_attn_bwd(const fmask_attn_args* a, const void* q, const void*
   if (tiles->nqt != ceil_div(a->sq, 128) || tiles->nkt != ceil_div(a->skv, 64) ||
       tiles->batch != enc->batch || tiles->heads != enc->heads)
     return fail(FMASK_ERR_INVALID, "tile table does not match the encoding");
+  if (check_mask_data(enc) != FMASK_OK) return FMASK_ERR_INVALID;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
     return fail(FMASK_ERR_INVALID, "null tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
@@ -941,7 +960,10 @@ fmask_status fmask_attn_bwd(const fmask_attn_args* a, const void* q, const void*
   p.col_list = col_list; p.col_count = col_count; p.col_order = col_order;
   p.nqt = tiles->nqt; p.nkt = tiles->nkt; p.bm = tiles->bm; p.bn = tiles->bn;
   p.mb = enc->batch; p.mh = enc->heads;
+  p.kind = enc->kind;
   p.iv = enc->intervals;
+  p.bstate = enc->blk_state; p.bindex = enc->blk_index; p.bbits = enc->blk_bits;
+  p.nbq = (int32_t)enc->nbq; p.nbk = (int32_t)enc->nbk;
   hipStream_t s = (hipStream_t)stream;
   // the tile table by key-tile column, and its longest-first order
   hipError_t ec = launch_tile_cols(tiles->state, enc->batch * enc->heads, tiles->nqt, tiles->nkt, col_list,

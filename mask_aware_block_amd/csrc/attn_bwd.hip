@@ -1,5 +1,6 @@
 // Backward pass of the masked attention forward, bf16 inputs, fp32
-// accumulation, gfx950 MFMA (interval encoding, 128 x 64 tile table).
+// accumulation, gfx950 MFMA (interval and 64 x 64 bitmap encodings, 128 x 64
+// tile table).
 //
 // With P_ij = exp(s_ij - LSE_i) on visible cells, D_i = sum_d dO_id O_id and
 // dS = P * (dO V^T - D):  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
@@ -18,7 +19,10 @@
 //                halves are summed through LDS at the end.  Query tiles are
 //                double-buffered in LDS.
 // Tiles whose rows and keys a wave does not see at all are skipped per wave;
-// FULL tiles run without element masks.  Operand fragments that are read
+// FULL tiles run without element masks.  With a bitmap mask each wave's rows
+// lie in one 64 x 64 block of the key tile: the dQ kernel masks with its row's
+// word of the block (bit = key), the dK/dV kernel with its key's column of the
+// block, gathered from the row words by one ballot per key.  Operand fragments that are read
 // both row-wise (16-byte reads) and transposed (ds_read_b64_tr_b16) live in
 // LDS under a swizzle that keeps both access patterns free of bank conflicts,
 // and every MFMA operand read from LDS is read kAhead MFMAs ahead into a ring
@@ -98,6 +102,16 @@ __device__ inline int logical_item(int gsz) {
   return ((k / gsz) * kXcds + xcd) * gsz + (k % gsz);
 }
 
+// Bitmap masks: state of 64 x 64 block (bi, bj) of mask slice `slice`
+// (FMASK_SKIP past the mask's blocks) and, when PARTIAL, its pool entry.
+__device__ inline int block_state(const BwdParams& p, int slice, int bi, int bj, int* pool) {
+  if (bi >= p.nbq || bj >= p.nbk) return FMASK_SKIP;
+  const int64_t x = ((int64_t)slice * p.nbq + bi) * p.nbk + bj;
+  const int st = p.bstate[x];
+  if (st == FMASK_PARTIAL) *pool = p.bindex[x];
+  return st;
+}
+
 // ------------------------------------------------------------------ rows
 // One 16-lane (D = 128) or 8-lane (D = 64) group per row.
 template <int D>
@@ -139,7 +153,7 @@ struct GeoQ {
   static constexpr int LOADS = BN * KCH / 256;
 };
 
-template <int D>
+template <int D, int KIND>
 __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdParams p, int expand, int n_items, int gsz) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using G = GeoQ<D>;
@@ -166,7 +180,7 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdParams p, int expand, int 
   const int32_t* list = p.list + (int64_t)row * p.nkt;
   const int cnt = p.count[row];
   const int64_t ks2 = p.ks[2], vs2 = p.vs[2];
-  const int32_t* ivcol = p.iv + ((size_t)mb * p.mh + mh) * 4 * (size_t)p.skv;
+  const int32_t* ivcol = KIND == FMASK_ENC_BITMAP ? p.iv : p.iv + ((size_t)mb * p.mh + mh) * 4 * (size_t)p.skv;
   const __bf16* Q = (const __bf16*)p.q + b * p.qs[0] + h * p.qs[1];
   const __bf16* dO = (const __bf16*)p.dout + b * p.os[0] + h * p.os[1];
   const __bf16* K = (const __bf16*)p.k + b * p.ks[0] + kvh * p.ks[1];
@@ -226,7 +240,7 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdParams p, int expand, int 
     for (int n = 0; n < G::LOADS; ++n) dma16(krs, kgo[n] + kt * kstep, base + n * 1024);
 #pragma unroll
     for (int n = 0; n < G::LOADS; ++n) dma16(vrs, vgo[n] + kt * vstep, base + G::TILE + n * 1024);
-    dma4(irs, (w * p.skv + kt * BN + lane) * 4, lds_iv + buf * G::STAGE);
+    if constexpr (KIND != FMASK_ENC_BITMAP) dma4(irs, (w * p.skv + kt * BN + lane) * 4, lds_iv + buf * G::STAGE);
   };
 
   uint32_t* rmask = (uint32_t*)(smem + G::RM0) + w * BN;
@@ -247,7 +261,20 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdParams p, int expand, int 
       const bool ragged = (kt + 1) * BN > p.skv;
       bool need_mask = !(e_cur & (int)FMASK_LIST_FULL_BIT) || ragged;
       bool skip = false;
-      if (need_mask) {
+      // Bitmap: this wave's 32 rows lie in one 64 x 64 block of the key tile;
+      // bit c of `vis` says key kt BN + c is visible to this lane's row
+      uint64_t vis = ~0ull;
+      if constexpr (KIND == FMASK_ENC_BITMAP) {
+        int pool = 0;
+        const int st = block_state(p, mb * p.mh + mh, 2 * qt + (w >> 1), kt, &pool);
+        skip = st == FMASK_SKIP;
+        need_mask = !skip && (st == FMASK_PARTIAL || ragged);
+        if (need_mask) {
+          if (st == FMASK_PARTIAL) vis = p.bbits[(int64_t)pool * 64 + (w & 1) * 32 + l32];
+          const int nk = p.skv - kt * BN;  // keys of this tile below skv
+          if (nk < 64) vis &= (1ull << nk) - 1ull;
+        }
+      } else if (need_mask) {
         const int key = kt * BN + lane;
         int us = raw[lane], ue = raw[BN + lane], ls = raw[2 * BN + lane], le = raw[3 * BN + lane];
         if (key >= p.skv) { us = 0; ue = 0x7fffffff; ls = 0; le = 0; }
@@ -294,6 +321,8 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdParams p, int expand, int 
         for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
           for (int tp = 0; tp < 2; ++tp) {
+            // bitmap: the keys of this half (32 kh ..), from bit 4 half on
+            const uint32_t vw = (uint32_t)(vis >> (32 * kh)) >> (4 * half);
             f32x8 x;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -308,7 +337,13 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdParams p, int expand, int 
               for (int j = 0; j < 8; ++j) {
                 const int r = 8 * tp + j;
                 const int kl = kh * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                x[j] = ((rmask[kl] >> l32) & 1u) ? 0.f : x[j];
+                if constexpr (KIND == FMASK_ENC_BITMAP) {
+                  // all ones where the key is visible: keep the value's bits
+                  const int32_t kb = __builtin_amdgcn_sbfe((int32_t)vw, 8 * (r >> 2) + (r & 3), 1);
+                  x[j] = __int_as_float(__float_as_int(x[j]) & kb);
+                } else {
+                  x[j] = ((rmask[kl] >> l32) & 1u) ? 0.f : x[j];
+                }
               }
             }
             dsf[kh * 2 + tp] = __builtin_convertvector(x, bf16x8);
@@ -363,7 +398,7 @@ struct GeoKV {
   static constexpr int LOADS = BM * KCH / 256;
 };
 
-template <int D>
+template <int D, int KIND>
 __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, int n_items) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using G = GeoKV<D>;
@@ -480,7 +515,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
       // intervals of this lane's key for the current head's mask (loaded
       // before the next stage's loads are in flight)
       const int mhh = p.mh == 1 ? 0 : g * p.group + hi;
-      if (mhh != iv_head) {
+      if (KIND != FMASK_ENC_BITMAP && mhh != iv_head) {
         iv_head = mhh;
         if (key < p.skv) {
           const int32_t* ivcol = p.iv + ((size_t)mb * p.mh + mhh) * 4 * (size_t)p.skv;
@@ -501,21 +536,47 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
       // this wave: keys key (lane), rows qt*BM + rw*64 + [0, 64)
       const int ra = qt * BM + rw * 64;
       const int na = min(max(p.sq - ra, 0), 64);
-      const int cm = overlap(ra, ra + na, us, ue) + overlap(ra, ra + na, ls, le);
-      const bool wskip = __ballot(!(key < p.skv) || cm == na) == ~0ull;
-      const bool full = (e & (int)FMASK_LIST_FULL_BIT) && (kt + 1) * BN <= p.skv && na == 64;
       // PARTIAL: bit r of `keep` says row ra + r (r < 64, after the shift by
       // 4 half the bit of the row 4 half + r) is visible to this lane's key;
-      // built once per query tile from the key's two runs and the end of Q
+      // built once per query tile
+      bool wskip, full;
       uint64_t keep = 0;
-      if (!wskip && !full) {
-        auto rows = [&](int a, int b) -> uint64_t {  // bits [a - ra, b - ra) within [0, 64)
-          const int lo = min(max(a - ra, 0), 64), hi = min(max(b - ra, 0), 64);
-          const uint64_t below_hi = hi >= 64 ? ~0ull : ((1ull << hi) - 1ull);
-          const uint64_t below_lo = lo >= 64 ? ~0ull : ((1ull << lo) - 1ull);
-          return below_hi & ~below_lo;
-        };
-        keep = ~(rows(us, ue) | rows(ls, le) | rows(p.sq, ra + 64)) >> (4 * half);
+      if constexpr (KIND == FMASK_ENC_BITMAP) {
+        // the wave's 64 rows are one block row: its 64 x 64 block of this key tile
+        int pool = 0;
+        const int st = block_state(p, mb * p.mh + mhh, 2 * qt + rw, kt, &pool);
+        wskip = st == FMASK_SKIP;
+        full = st == FMASK_FULL && (kt + 1) * BN <= p.skv && na == 64;
+        if (!wskip && !full) {
+          uint64_t colw = 0;  // the rows that see this lane's key
+          if (st == FMASK_PARTIAL) {
+            // lane r holds the block's row word r; one ballot per key of this
+            // wave's half gathers that key's column
+            const uint64_t roww = p.bbits[(int64_t)pool * 64 + lane];
+#pragma unroll 4
+            for (int kk = 0; kk < 32; ++kk) {
+              const uint64_t cw = __ballot((roww >> (kw * 32 + kk)) & 1ull);
+              colw = l32 == kk ? cw : colw;
+            }
+          } else {  // FULL block with rows past sq or keys past skv
+            colw = key < p.skv ? (na >= 64 ? ~0ull : ((1ull << na) - 1ull)) : 0ull;
+          }
+          keep = colw >> (4 * half);
+        }
+      } else {
+        // from the key's two runs and the end of Q
+        const int cm = overlap(ra, ra + na, us, ue) + overlap(ra, ra + na, ls, le);
+        wskip = __ballot(!(key < p.skv) || cm == na) == ~0ull;
+        full = (e & (int)FMASK_LIST_FULL_BIT) && (kt + 1) * BN <= p.skv && na == 64;
+        if (!wskip && !full) {
+          auto rows = [&](int a, int b) -> uint64_t {  // bits [a - ra, b - ra) within [0, 64)
+            const int lo = min(max(a - ra, 0), 64), hi = min(max(b - ra, 0), 64);
+            const uint64_t below_hi = hi >= 64 ? ~0ull : ((1ull << hi) - 1ull);
+            const uint64_t below_lo = lo >= 64 ? ~0ull : ((1ull << lo) - 1ull);
+            return below_hi & ~below_lo;
+          };
+          keep = ~(rows(us, ue) | rows(ls, le) | rows(p.sq, ra + 64)) >> (4 * half);
+        }
       }
       // 0 where row offset `pos` of this lane (pos = 32 rb + 8 (r / 4) + r % 4)
       // is masked, all ones where it is visible
@@ -655,7 +716,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
 #endif
 }
 
-template <int D>
+template <int D, int KIND>
 hipError_t launch_d(const BwdParams& p, hipStream_t s) {
   // (With no query row the dK / dV kernel still runs: its empty column lists
   // write zeros.  With no key the dQ kernel's empty lists do the same.)
@@ -673,7 +734,7 @@ hipError_t launch_d(const BwdParams& p, hipStream_t s) {
     const int64_t unit = (int64_t)kXcds * gsz;
     const int64_t npad = (n + unit - 1) / unit * unit;
     if (n > 0)
-      hipLaunchKernelGGL((k_bwd_dq<D>), dim3((unsigned)npad), dim3(256), 0, s, p, expand, (int)n, gsz);
+      hipLaunchKernelGGL((k_bwd_dq<D, KIND>), dim3((unsigned)npad), dim3(256), 0, s, p, expand, (int)n, gsz);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -688,7 +749,7 @@ hipError_t launch_d(const BwdParams& p, hipStream_t s) {
       expand = 1;
       n = (int64_t)p.b * p.hkv * p.nkt;
     }
-    if (n > 0) hipLaunchKernelGGL((k_bwd_dkdv<D>), dim3((unsigned)n), dim3(256), 0, s, p, expand, (int)n);
+    if (n > 0) hipLaunchKernelGGL((k_bwd_dkdv<D, KIND>), dim3((unsigned)n), dim3(256), 0, s, p, expand, (int)n);
     e = hipGetLastError();
   }
   return e;
@@ -698,8 +759,13 @@ hipError_t launch_d(const BwdParams& p, hipStream_t s) {
 
 hipError_t launch_attn_bwd_bf16(const BwdParams& p, int32_t d, hipStream_t s) {
   if (p.bm != BM || p.bn != BN) return hipErrorInvalidValue;
-  if (d == 128) return launch_d<128>(p, s);
-  if (d == 64) return launch_d<64>(p, s);
+  if (p.kind == FMASK_ENC_BITMAP) {
+    if (d == 128) return launch_d<128, FMASK_ENC_BITMAP>(p, s);
+    if (d == 64) return launch_d<64, FMASK_ENC_BITMAP>(p, s);
+    return hipErrorInvalidValue;
+  }
+  if (d == 128) return launch_d<128, FMASK_ENC_INTERVALS>(p, s);
+  if (d == 64) return launch_d<64, FMASK_ENC_INTERVALS>(p, s);
   return hipErrorInvalidValue;
 }
 

@@ -169,7 +169,12 @@ struct BwdParams {
   const int32_t* col_order;
   int32_t nqt, nkt, bm, bn;
   int32_t mb, mh;
-  const int32_t* iv;   // [mb][mh][4][skv]
+  int32_t kind;             // FMASK_ENC_INTERVALS or FMASK_ENC_BITMAP
+  const int32_t* iv;        // INTERVALS: [mb][mh][4][skv]
+  const uint8_t* bstate;    // BITMAP: [mb][mh][nbq][nbk] 64x64 block states
+  const int32_t* bindex;    // BITMAP: pool entry of each PARTIAL block
+  const uint64_t* bbits;    // BITMAP: [pool][64] row words (bit c: key 64 bj + c)
+  int32_t nbq, nbk;
 };
 
 hipError_t launch_attn_bwd_bf16(const BwdParams& p, int32_t d, hipStream_t s);

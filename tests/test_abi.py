@@ -186,6 +186,9 @@ def test_split_backward_varlen_dense_host_validation():
     need = L.fmask_attn_bwd_workspace_bytes(ctypes.byref(a), ctypes.byref(t))
     assert need >= 8 * 512 * 8
     args = [ctypes.byref(a)] + [p] * 4 + [ctypes.cast(p, ctypes.c_void_p)] + [p] * 4
+    assert L.fmask_attn_bwd(*args, p, need, ctypes.byref(iv_enc), ctypes.byref(t), None) == fm.ERR_INVALID
+    assert b"interval array" in L.fmask_last_error()  # a hand-filled encoding without its mask data
+    iv_enc.intervals = p.value
     assert L.fmask_attn_bwd(*args, p, need - 16, ctypes.byref(iv_enc), ctypes.byref(t), None) == fm.ERR_CAPACITY
     t64 = fm.Tiles()
     t64.bm, t64.bn, t64.nqt, t64.nkt, t64.batch, t64.heads = 64, 64, 8, 8, 1, 1
@@ -194,6 +197,24 @@ def test_split_backward_varlen_dense_host_validation():
     assert L.fmask_attn_bwd(*args, p, need, ctypes.byref(iv_enc), ctypes.byref(t), None) == fm.ERR_UNSUPPORTED
     a.dtype = 1
     assert L.fmask_attn_bwd(*args, p, need, ctypes.byref(sel), ctypes.byref(t), None) == fm.ERR_UNSUPPORTED
+    # a bitmap encoding is checked against the block grid that sq and skv imply (8 x 8 blocks of 64)
+    bmp = fm.Encoded()
+    bmp.kind, bmp.batch, bmp.heads, bmp.sq, bmp.skv, bmp.blk = fm.ENC_BITMAP, 1, 1, 512, 512, 64
+    bmp.blk_state = bmp.blk_index = bmp.blk_bits = bmp.blk_pool_count = p.value
+    for nbq, nbk, blk in ((7, 8, 64), (8, 9, 64), (8, 8, 32)):
+        bmp.nbq, bmp.nbk, bmp.blk = nbq, nbk, blk
+        assert L.fmask_attn_bwd(*args, p, need, ctypes.byref(bmp), ctypes.byref(t), None) == fm.ERR_INVALID
+        assert L.fmask_attn_fwd(ctypes.byref(a), p, p, p, p, None, ctypes.byref(bmp), ctypes.byref(t),
+                                None) == fm.ERR_INVALID
+        assert b"block grid" in L.fmask_last_error()
+        assert L.fmask_classify(ctypes.byref(bmp), 128, 64, p, 1 << 30, ctypes.byref(fm.Tiles()),
+                                None) == fm.ERR_INVALID
+    bmp.nbq, bmp.nbk, bmp.blk = 8, 8, 64
+    bmp.blk_bits = None
+    assert L.fmask_attn_bwd(*args, p, need, ctypes.byref(bmp), ctypes.byref(t), None) == fm.ERR_INVALID
+    assert b"bitmap array" in L.fmask_last_error()
+    bmp.blk_bits = p.value
+    assert L.fmask_attn_bwd(*args, p, need - 16, ctypes.byref(bmp), ctypes.byref(t), None) == fm.ERR_CAPACITY
     # varlen: segment lengths must add up, modes must be known
     enc = fm.Encoded()
     cu = np.array([0, 100, 300], dtype=np.int32)

@@ -103,6 +103,38 @@ def test_gqa_batch_and_per_head_masks():
     _grad_check(w8, dict(family="causal", sq=257, skv=257), "gqa 8/1")
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_bitmap_masks(D):
+    """Masks in the 64 x 64 bitmap form: a BFS-numbered tree (subtrees that
+    are not contiguous), a random block pattern per batch entry with the
+    diagonal forced visible, and a random dense mask; ragged sizes, GQA 4/2."""
+    rng = np.random.default_rng(31 + D)
+    n, prefix = 70, 150
+    S = prefix + n
+    spec = dict(family="tree", sq=S, skv=S, tree_prefix=prefix,
+                tree_parent=synth.random_tree(rng, n, order="bfs"))
+    assert fm.encode(spec).kind == fm.ENC_BITMAP
+    _grad_check(_small(D, S, S, seed=31), spec, f"tree (bfs) D{D}")
+    S, K = 300, 270
+    nbq, nbk = -(-S // 64), -(-K // 64)
+    sts, ixs, pools, off = [], [], [], 0
+    for _ in range(2):
+        st, ix, bits = synth.block_pattern(rng, nbq, nbk, 0.3, 0.3)
+        sts.append(st)
+        ixs.append(np.where(ix >= 0, ix + off, -1))
+        pools.append(np.asarray(bits, dtype=np.uint64).reshape(-1, 64))
+        off += pools[-1].shape[0]
+    spec = dict(family="block_bitmap", sq=S, skv=K, batch=2, heads=1,
+                blk_state=np.stack(sts).reshape(2, 1, nbq, nbk),
+                blk_index=np.stack(ixs).reshape(2, 1, nbq, nbk).astype(np.int32),
+                blk_bits=np.concatenate(pools) if off else np.zeros((1, 64), np.uint64), force_diag=True)
+    _grad_check(_small(D, S, K, B=2, seed=32), spec, f"block pattern per batch D{D}")
+    dense = (rng.random((1, 1, S, K)) < 0.3).astype(np.uint8)
+    spec = dict(family="dense", sq=S, skv=K, dense=dense)
+    assert fm.encode(spec).kind == fm.ENC_BITMAP
+    _grad_check(_small(D, S, K, seed=33), spec, f"random dense (bitmap form) D{D}")
+
+
 def test_full_size_causal_doc_8k_one_group():
     w = synth.workload("causal_doc_8k")
     _grad_check(w, w["mask"], "causal_doc_8k heads 0..3", heads=(0, 4))

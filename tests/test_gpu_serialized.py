@@ -1,8 +1,8 @@
 """Serialized-launch debug mode gives the same bits as normal launches.
 
 A child process runs the seeded random configurations of
-tests/test_gpu_random_configs.py (every mask family; the backward on interval
-masks; the one-pass, block-major and split forms of the selected-key path)
+tests/test_gpu_random_configs.py (every mask family; the backward on interval and
+bitmap masks; the one-pass, block-major and split forms of the selected-key path)
 and prints a hash of every output.  It runs twice: as is, and with
 AMD_SERIALIZE_KERNEL=3 and HIP_LAUNCH_BLOCKING=1, where every launch waits for
 the previous one and returns only when it has finished.  All of the library's
@@ -49,7 +49,7 @@ for seed in range(int(sys.argv[2])):
         tiles = fm.classify(enc, 128, 64)
         o, lse = fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"])
         res += [o, lse]
-        if enc.kind == fm.ENC_INTERVALS:
+        if enc.kind in (fm.ENC_INTERVALS, fm.ENC_BITMAP):
             do = torch.from_numpy(synth.draw_dout(w).view(np.int16)).view(torch.bfloat16).cuda()
             res += fm.attn_bwd(q, k, v, o, lse, do, enc, tiles, scale=w["scale"])
     torch.cuda.synchronize()

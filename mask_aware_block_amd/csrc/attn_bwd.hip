@@ -13,11 +13,14 @@
 //                dQ^T += K^T dS^T.
 //   k_bwd_dkdv   one 64-key tile per workgroup walking its column list of
 //                128-row query tiles, for every query head of the K/V head:
-//                S = Q K^T and dP = dO V^T with K, V in registers, then
-//                dV^T += dO^T P and dK^T += Q^T dS.  Waves split the keys (2 x
-//                32) and the rows of each query tile (2 x 64); the two row
-//                halves are summed through LDS at the end.  Query tiles are
-//                double-buffered in LDS.
+//                S = Q K^T and dP = dO V^T, then dV^T += dO^T P and
+//                dK^T += Q^T dS.  Query tiles are double-buffered in LDS.
+//                D = 64: four waves split the keys (2 x 32) and the rows of
+//                each query tile (2 x 64), with K and V in registers; the two
+//                row halves are summed through LDS at the end.
+//   k_bwd_dkdv8  the D = 128 form: eight waves (2 x 32 keys, 4 x 32 rows),
+//                two per SIMD, with K in registers and V staged in LDS; the
+//                four row quarters are summed through LDS in two rounds.
 // Tiles whose rows and keys a wave does not see at all are skipped per wave;
 // FULL tiles run without element masks.  With a bitmap mask each wave's rows
 // lie in one 64 x 64 block of the key tile: the dQ kernel masks with its row's
@@ -26,8 +29,8 @@
 // both row-wise (16-byte reads) and transposed (ds_read_b64_tr_b16) live in
 // LDS under a swizzle that keeps both access patterns free of bank conflicts,
 // and every MFMA operand read from LDS is read kAhead MFMAs ahead into a ring
-// of registers (the dK/dV kernel runs one wave per SIMD, so nothing else hides
-// the LDS latency).  The file is compiled with VGPR-form MFMAs (build.py).
+// of registers (the four-wave dK/dV kernel runs one wave per SIMD, so nothing
+// else hides the LDS latency).  The file is compiled with VGPR-form MFMAs (build.py).
 #include <float.h>
 
 #include "device_util.h"
@@ -398,6 +401,25 @@ struct GeoKV {
   static constexpr int LOADS = BM * KCH / 256;
 };
 
+// dK/dV work item l -> (mask column, batch, K/V head).  With one mask for all
+// heads the columns come longest first, each expanded over (batch if the mask
+// is shared along it) x K/V head; with per-head masks items are (batch, K/V
+// head, key tile) in natural order, and the column is that of the head group's
+// first head (the kernels walk the group's heads).
+__device__ inline void kv_item(const BwdParams& p, int expand, int l, int* col, int* b, int* g) {
+  if (p.mh == 1) {
+    *col = p.col_order[l / expand];
+    const int e = l % expand;
+    if (p.mb == 1) { *b = e / p.hkv; *g = e % p.hkv; }
+    else { *b = *col / p.nkt; *g = e; }
+  } else {
+    const int kt0 = l % p.nkt;
+    *g = (l / p.nkt) % p.hkv;
+    *b = l / (p.nkt * p.hkv);
+    *col = ((p.mb == 1 ? 0 : *b) * p.mh) * p.nkt + kt0;
+  }
+}
+
 template <int D, int KIND>
 __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, int n_items) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -407,21 +429,8 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
 
   const int l = blockIdx.x;
   if (l >= n_items) return;
-  // item -> (mask column, batch, K/V head)
   int col, b, g;
-  if (p.mh == 1) {
-    col = p.col_order[l / expand];
-    const int e = l % expand;  // (batch if the mask is shared along it) x K/V head
-    const int mbm = col / p.nkt;
-    if (p.mb == 1) { b = e / p.hkv; g = e % p.hkv; }
-    else { b = mbm; g = e; }
-  } else {
-    // per-head masks: items are (batch, K/V head, key tile) in natural order
-    const int kt0 = l % p.nkt;
-    g = (l / p.nkt) % p.hkv;
-    b = l / (p.nkt * p.hkv);
-    col = ((p.mb == 1 ? 0 : b) * p.mh) * p.nkt + kt0;  // column of the first head (fixed below)
-  }
+  kv_item(p, expand, l, &col, &b, &g);
   const int kt = col % p.nkt;
   const int mb = (p.mb == 1) ? 0 : b;
 
@@ -716,6 +725,338 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
 #endif
 }
 
+// Eight-wave form: 2 key halves x 4 row quarters of each query tile, two waves
+// per SIMD.  K stays in registers as the B operand of S = Q K^T; V is staged
+// once into LDS and read as the B operand of dP = dO V^T, which leaves each
+// wave within 256 registers (the four-wave form keeps V in registers too and
+// needs more than 256).  The four row quarters' dK and dV are summed through
+// LDS at the end, in two rounds.
+template <int D>
+struct GeoKV8 {
+  static constexpr int KCH = D / 8;
+  static constexpr int TILE = BM * D * 2;        // one [128 rows][D] bf16 tile
+  static constexpr int Q0 = 0, DO0 = TILE;       // Q tile, dO tile
+  static constexpr int RW0 = 2 * TILE;           // [128 rows] x {D_i, LSE2_i}
+  static constexpr int STAGE = RW0 + BM * 8;     // two stages (double-buffered)
+  static constexpr int V0 = 2 * STAGE;           // V tile [64 keys][D]
+  static constexpr int END = V0 + BN * D * 2;
+  static constexpr int LOADS = BM * KCH / 512;   // 16-byte loads per wave and tile
+  static constexpr int RED = 2 * 2 * 2 * (D / 32) * 16 * 64 * 4;  // 2 quarters x 2 key halves x dK, dV
+};
+static_assert(GeoKV8<128>::END <= 160 * 1024 && GeoKV8<128>::RED <= GeoKV8<128>::END, "LDS");
+static_assert(GeoKV8<64>::RED <= GeoKV8<64>::END, "LDS");
+
+template <int D, int KIND>
+__global__ void __launch_bounds__(512, 1) k_bwd_dkdv8(BwdParams p, int expand, int n_items) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  using G = GeoKV8<D>;
+  constexpr int DB = D / 32, KT = D / 16;
+  constexpr int kA = 2, kV = 2;  // read-ahead of the A fragments and of the V fragments
+  __shared__ __attribute__((aligned(1024))) char smem[G::END];
+
+  const int l = blockIdx.x;
+  if (l >= n_items) return;
+  int col, b, g;
+  kv_item(p, expand, l, &col, &b, &g);
+  const int kt = col % p.nkt;
+  const int mb = (p.mb == 1) ? 0 : b;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = w & 1, rw = w >> 1;  // key half (32 keys), 32-row quarter of each query tile
+  const int half = lane >> 5, l32 = lane & 31;
+  const int key = kt * BN + kw * 32 + l32;  // this lane's key (as MFMA column)
+
+  const __bf16* K = (const __bf16*)p.k + b * p.ks[0] + g * p.ks[1];
+  const __bf16* V = (const __bf16*)p.v + b * p.vs[0] + g * p.vs[1];
+
+  // V tile into LDS under the row swizzle (zeros past skv)
+  char* vt = smem + G::V0;
+  for (int idx = tid; idx < BN * G::KCH; idx += 512) {
+    const int r = idx / G::KCH, ch = idx % G::KCH, kk = kt * BN + r;
+    i32x4 x = i32x4{0, 0, 0, 0};
+    if (kk < p.skv) x = *(const i32x4*)(V + kk * p.vs[2] + ch * 8);
+    *(i32x4*)(vt + chunk_off<D>(r, ch)) = x;
+  }
+  // K as the B operand of S = Q K^T (lane: key, 8 d)
+  bf16x8 kf[KT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t)
+    kf[t] = key < p.skv ? *(const bf16x8*)(K + key * p.ks[2] + 16 * t + 8 * half) : bf16x8{};
+  wait_all();
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dk[i] = dv[i] = f32x16{};
+  const float c = p.scale * kLog2e;
+  int tlo[DB], thi[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    tlo[db] = tr_off<D>(lane, db, 0);
+    thi[db] = tr_off<D>(lane, db, 1);
+  }
+  const int lds_w = __builtin_amdgcn_readfirstlane(lds_addr(smem) + w * G::LOADS * 1024);
+  const int lds_rw = __builtin_amdgcn_readfirstlane(lds_addr(smem) + G::RW0);
+  constexpr int RPI = 64 / G::KCH;
+  constexpr int PER = 16 / RPI;
+
+  auto col_of = [&](int hi) INLINE -> int {
+    return (mb * p.mh + (p.mh == 1 ? 0 : g * p.group + hi)) * p.nkt + kt;
+  };
+  auto count_of = [&](int hi) INLINE -> int { return p.col_count[col_of(hi)]; };
+  auto stage = [&](int hi, int i, int buf) INLINE {
+    const int h = g * p.group + hi;
+    const int qt = p.col_list[(int64_t)col_of(hi) * p.nqt + i] & 0x7fffffff;
+    const __bf16* Q = (const __bf16*)p.q + b * p.qs[0] + h * p.qs[1];
+    const __bf16* dO = (const __bf16*)p.dout + b * p.os[0] + h * p.os[1];
+    const float* ws = p.ws + ((int64_t)b * p.hq + h) * p.sq * 2;
+    const rsrc_t qrs = make_rsrc(Q, ((int64_t)(p.sq - 1) * p.qs[2] + D) * 2);
+    const rsrc_t ors = make_rsrc(dO, ((int64_t)(p.sq - 1) * p.os[2] + D) * 2);
+    const rsrc_t wrs = make_rsrc(ws, (int64_t)p.sq * 8);
+    const int base = lds_w + buf * G::STAGE;
+#pragma unroll
+    for (int n = 0; n < G::LOADS; ++n) {
+      const int rs = qt * BM + (w * G::LOADS + n - n % PER) * RPI;
+      const int tr = (n % PER) * RPI + lane / G::KCH;
+      const int tc = ((lane % G::KCH) ^ sw<G::KCH>(tr)) * 16;
+      dma16s(qrs, (int)(tr * p.qs[2] * 2) + tc, (int)(rs * p.qs[2] * 2), base + G::Q0 + n * 1024);
+      dma16s(ors, (int)(tr * p.os[2] * 2) + tc, (int)(rs * p.os[2] * 2), base + G::DO0 + n * 1024);
+    }
+    if (w == 0) dma16(wrs, (qt * BM * 2 + lane * 4) * 4, lds_rw + buf * G::STAGE);
+  };
+
+  int hi = 0;
+  while (hi < p.group && count_of(hi) == 0) ++hi;
+  int us = 0, ue = 0x7fffffff, ls = 0, le = 0;  // this lane's key column (past skv: all masked)
+  int iv_head = -1;
+  if (hi < p.group) {
+    int i = 0, buf = 0;
+    stage(hi, i, 0);
+    wait_all();
+    barrier();
+    while (true) {
+      int nh = hi, ni = i + 1;
+      while (nh < p.group && ni >= count_of(nh)) { ++nh; ni = 0; }
+      const bool more = nh < p.group;
+      const int mhh = p.mh == 1 ? 0 : g * p.group + hi;
+      if (KIND != FMASK_ENC_BITMAP && mhh != iv_head) {
+        iv_head = mhh;
+        if (key < p.skv) {
+          const int32_t* ivcol = p.iv + ((size_t)mb * p.mh + mhh) * 4 * (size_t)p.skv;
+          us = ivcol[key];
+          ue = ivcol[p.skv + key];
+          ls = ivcol[2 * (size_t)p.skv + key];
+          le = ivcol[3 * (size_t)p.skv + key];
+        }
+        wait_all();
+      }
+      const int e = p.col_list[(int64_t)col_of(hi) * p.nqt + i];
+      if (more) stage(nh, ni, buf ^ 1);
+      const int qt = e & 0x7fffffff;
+
+      const char* qb = smem + buf * G::STAGE + G::Q0;
+      const char* ob = smem + buf * G::STAGE + G::DO0;
+      const float* rv = (const float*)(smem + buf * G::STAGE + G::RW0);
+      // this wave: keys key (lane), rows ra + [0, 32)
+      const int ra = qt * BM + rw * 32;
+      const int na = min(max(p.sq - ra, 0), 32);
+      // PARTIAL: bit 8 (j / 4) + j % 4 of `keep` says whether value j of this
+      // lane (row ra + 8 (j / 4) + 4 half + j % 4) is visible to its key
+      bool wskip, full;
+      uint32_t keep = 0;
+      if constexpr (KIND == FMASK_ENC_BITMAP) {
+        // the wave's 32 rows are one half of a 64-row block row
+        int pool = 0;
+        const int st = block_state(p, mb * p.mh + mhh, 2 * qt + (rw >> 1), kt, &pool);
+        wskip = st == FMASK_SKIP || na == 0;
+        full = st == FMASK_FULL && (kt + 1) * BN <= p.skv && na == 32;
+        if (!wskip && !full) {
+          uint64_t colw = 0;  // the block's rows that see this lane's key
+          if (st == FMASK_PARTIAL) {
+            const uint64_t roww = p.bbits[(int64_t)pool * 64 + lane];
+#pragma unroll 4
+            for (int kk = 0; kk < 32; ++kk) {
+              const uint64_t cw = __ballot((roww >> (kw * 32 + kk)) & 1ull);
+              colw = l32 == kk ? cw : colw;
+            }
+          } else {  // FULL block with rows past sq or keys past skv
+            colw = key < p.skv ? ((na >= 32 ? 0xffffffffull : ((1ull << na) - 1ull)) << (32 * (rw & 1))) : 0ull;
+          }
+          keep = (uint32_t)(colw >> (32 * (rw & 1))) >> (4 * half);
+        }
+      } else {
+        const int cm = overlap(ra, ra + na, us, ue) + overlap(ra, ra + na, ls, le);
+        wskip = __ballot(!(key < p.skv) || cm == na) == ~0ull;
+        full = (e & (int)FMASK_LIST_FULL_BIT) && (kt + 1) * BN <= p.skv && na == 32;
+        if (!wskip && !full) {
+          auto rows = [&](int a, int b) -> uint32_t {  // bits [a - ra, b - ra) within [0, 32)
+            const int lo = min(max(a - ra, 0), 32), hi = min(max(b - ra, 0), 32);
+            const uint32_t below_hi = hi >= 32 ? ~0u : ((1u << hi) - 1u);
+            const uint32_t below_lo = lo >= 32 ? ~0u : ((1u << lo) - 1u);
+            return below_hi & ~below_lo;
+          };
+          keep = ~(rows(us, ue) | rows(ls, le) | rows(p.sq, ra + 32)) >> (4 * half);
+        }
+      }
+      if (!wskip) {
+        const int lr0 = rw * 32;  // first tile row of this wave
+        // S = Q K^T, then dP = dO V^T: A fragments read kA MFMAs ahead, V
+        // fragments kV ahead
+        f32x16 s = f32x16{}, dp = f32x16{};
+        {
+          auto afrag = [&](int n) INLINE -> bf16x8 {
+            const char* tb = n < KT ? qb : ob;
+            return *(const bf16x8*)(tb + chunk_off<D>(lr0 + l32, 2 * (n % KT) + half));
+          };
+          auto vfrag = [&](int j) INLINE -> bf16x8 {
+            return *(const bf16x8*)(vt + chunk_off<D>(kw * 32 + l32, 2 * j + half));
+          };
+          bf16x8 fr[kA], vr[kV];
+#pragma unroll
+          for (int n = 0; n < kA; ++n) fr[n] = afrag(n);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int n = 0; n < 2 * KT; ++n) {
+            const bf16x8 a = fr[n % kA];
+            if (n < KT) {
+              s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[n], s, 0, 0, 0);
+            } else {
+              const int j = n - KT;
+              dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vr[j % kV], dp, 0, 0, 0);
+              if (j + kV < KT) vr[j % kV] = vfrag(j + kV);
+            }
+            if (n + kA < 2 * KT) fr[n % kA] = afrag(n + kA);
+            if (n + kV == KT) {
+#pragma unroll
+              for (int j = 0; j < kV; ++j) vr[j] = vfrag(j);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        // P, dS: lane = key, rows lr0 + 8 (r / 4) + 4 half + r % 4
+        bf16x8 pb[2], sb[2];
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+          f32x8 xp, xs;
+#pragma unroll
+          for (int j4 = 0; j4 < 2; ++j4) {
+            const int rl = lr0 + 8 * (2 * tp + j4) + 4 * half;  // 4 consecutive rows
+            const f32x4 d4 = *(const f32x4*)(rv + 2 * rl);       // {D, LSE2} x 2
+            const f32x4 d5 = *(const f32x4*)(rv + 2 * rl + 4);
+            const float dl[4] = {d4[0], d4[2], d5[0], d5[2]};
+            const float ll[4] = {d4[1], d4[3], d5[1], d5[3]};
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int r = 8 * tp + 4 * j4 + q4;
+              const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -ll[q4]));
+              xp[4 * j4 + q4] = pr;
+              xs[4 * j4 + q4] = pr * (dp[r] - dl[q4]);
+            }
+          }
+          // element masks of a PARTIAL tile in one pass over the 8 values: a
+          // masked value's bits are cleared (it becomes +0)
+          if (!full) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int32_t k = __builtin_amdgcn_sbfe((int32_t)keep, 8 * (2 * tp + j / 4) + j % 4, 1);
+              xp[j] = __int_as_float(__float_as_int(xp[j]) & k);
+              xs[j] = __int_as_float(__float_as_int(xs[j]) & k);
+            }
+          }
+          pb[tp] = __builtin_convertvector(xp, bf16x8);
+          sb[tp] = __builtin_convertvector(xs, bf16x8);
+        }
+        // dV^T += dO^T P,  dK^T += Q^T dS  (contraction over the 32 rows;
+        // MFMA m: db = m / 4, ks = m / 2 % 2, dV for even m and dK for odd m)
+        {
+          auto frag = [&](int m) INLINE -> bf16x8 {
+            const int db = m / 4, ks = (m / 2) % 2;
+            return tr_frag<D>((m & 1) ? qb : ob, lr0 + 16 * ks, tlo[db], thi[db]);
+          };
+          bf16x8 fr[kAhead];
+#pragma unroll
+          for (int m = 0; m < kAhead; ++m) fr[m] = frag(m);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int m = 0; m < 4 * DB; ++m) {
+            const int db = m / 4, ks = (m / 2) % 2;
+            const bf16x8 a = fr[m % kAhead];
+            if (m & 1) dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[ks], dk[db], 0, 0, 0);
+            else dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], dv[db], 0, 0, 0);
+            if (m + kAhead < 4 * DB) fr[m % kAhead] = frag(m + kAhead);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      wait_all();  // the next pair landed; every wave is done with this one
+      barrier();
+      if (!more) break;
+      hi = nh;
+      i = ni;
+      buf ^= 1;
+    }
+  }
+
+  // Sum the four row quarters (waves kw, kw + 2, kw + 4, kw + 6) through LDS
+  // in two rounds, then write.
+  float* red = (float*)smem;  // [2 quarters][2 kw][2 tensors][DB][16][64] floats
+  auto slot = [&](int q, int t, int db, int r) INLINE -> float& {
+    return red[((((q * 2 + kw) * 2 + t) * DB + db) * 16 + r) * 64 + lane];
+  };
+  __syncthreads();
+  if (rw >= 2) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        slot(rw - 2, 0, db, r) = dk[db][r];
+        slot(rw - 2, 1, db, r) = dv[db][r];
+      }
+  }
+  __syncthreads();
+  if (rw < 2) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dk[db][r] += slot(rw, 0, db, r);
+        dv[db][r] += slot(rw, 1, db, r);
+      }
+  }
+  __syncthreads();
+  if (rw == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        slot(0, 0, db, r) = dk[db][r];
+        slot(0, 1, db, r) = dv[db][r];
+      }
+  }
+  __syncthreads();
+  if (rw == 0 && key < p.skv) {
+    __bf16* dK = (__bf16*)p.dk + b * p.ks[0] + g * p.ks[1] + key * p.ks[2];
+    __bf16* dV = (__bf16*)p.dv + b * p.vs[0] + g * p.vs[1] + key * p.vs[2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        f32x4 xk, xv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * rg + j;
+          xk[j] = (dk[db][r] + slot(0, 0, db, r)) * p.scale;
+          xv[j] = dv[db][r] + slot(0, 1, db, r);
+        }
+        const int d0 = db * 32 + 8 * rg + 4 * half;
+        *(bf16x4*)(dK + d0) = __builtin_convertvector(xk, bf16x4);
+        *(bf16x4*)(dV + d0) = __builtin_convertvector(xv, bf16x4);
+      }
+    }
+  }
+#endif
+}
+
 template <int D, int KIND>
 hipError_t launch_d(const BwdParams& p, hipStream_t s) {
   // (With no query row the dK / dV kernel still runs: its empty column lists
@@ -749,7 +1090,14 @@ hipError_t launch_d(const BwdParams& p, hipStream_t s) {
       expand = 1;
       n = (int64_t)p.b * p.hkv * p.nkt;
     }
-    if (n > 0) hipLaunchKernelGGL((k_bwd_dkdv<D, KIND>), dim3((unsigned)n), dim3(256), 0, s, p, expand, (int)n);
+    // D = 128: eight waves (two per SIMD, V in LDS); D = 64: four waves, whose
+    // 66 KB of LDS already let two workgroups share a CU
+    if (n > 0) {
+      if constexpr (D == 128)
+        hipLaunchKernelGGL((k_bwd_dkdv8<D, KIND>), dim3((unsigned)n), dim3(512), 0, s, p, expand, (int)n);
+      else
+        hipLaunchKernelGGL((k_bwd_dkdv<D, KIND>), dim3((unsigned)n), dim3(256), 0, s, p, expand, (int)n);
+    }
     e = hipGetLastError();
   }
   return e;

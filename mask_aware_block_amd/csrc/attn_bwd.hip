@@ -444,6 +444,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
   const __bf16* V = (const __bf16*)p.v + b * p.vs[0] + g * p.vs[1];
 
   for (int i = tid; i < G::END / 16; i += 256) ((i32x4*)smem)[i] = i32x4{0, 0, 0, 0};
+  __syncthreads();  // every wave's clearing stores done before any tile load lands
 
   // K and V as B operands of S = Q K^T and dP = dO V^T (lane: key, 8 d)
   bf16x8 kf[KT], vf[KT];

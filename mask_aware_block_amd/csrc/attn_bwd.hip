@@ -105,16 +105,6 @@ __device__ inline int logical_item(int gsz) {
   return ((k / gsz) * kXcds + xcd) * gsz + (k % gsz);
 }
 
-// Bitmap masks: state of 64 x 64 block (bi, bj) of mask slice `slice`
-// (FMASK_SKIP past the mask's blocks) and, when PARTIAL, its pool entry.
-__device__ inline int block_state(const BwdParams& p, int slice, int bi, int bj, int* pool) {
-  if (bi >= p.nbq || bj >= p.nbk) return FMASK_SKIP;
-  const int64_t x = ((int64_t)slice * p.nbq + bi) * p.nbk + bj;
-  const int st = p.bstate[x];
-  if (st == FMASK_PARTIAL) *pool = p.bindex[x];
-  return st;
-}
-
 // ------------------------------------------------------------------ rows
 // One 16-lane (D = 128) or 8-lane (D = 64) group per row.
 template <int D>
@@ -166,7 +156,8 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdParams p, int expand, int 
   const int l = logical_item(gsz);
   if (l >= n_items) return;
   // item -> (mask row, batch, head), as the forward orders them
-  const int row = p.order[l / expand], e = l % expand;
+  // (the row uniform, so that its list entries are read with scalar loads)
+  const int row = __builtin_amdgcn_readfirstlane(p.order[l / expand]), e = l % expand;
   const int qt = row % p.nqt, mh = (row / p.nqt) % p.mh, mb = row / (p.nqt * p.mh);
   int b, h;
   if (p.mb == 1 && p.mh == 1) { b = e / p.hq; h = e % p.hq; }
@@ -181,7 +172,7 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdParams p, int expand, int 
   const int r0 = qt * BM + w * 32;
   const int qrow = r0 + l32;
   const int32_t* list = p.list + (int64_t)row * p.nkt;
-  const int cnt = p.count[row];
+  const int cnt = sload_wait(p.count + row);
   const int64_t ks2 = p.ks[2], vs2 = p.vs[2];
   const int32_t* ivcol = KIND == FMASK_ENC_BITMAP ? p.iv : p.iv + ((size_t)mb * p.mh + mh) * 4 * (size_t)p.skv;
   const __bf16* Q = (const __bf16*)p.q + b * p.qs[0] + h * p.qs[1];
@@ -237,25 +228,48 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdParams p, int expand, int 
     thi[db] = tr_off<D>(lane, db, 1);
   }
 
+  int st_next = FMASK_SKIP;  // bitmap: this wave's block state of the tile last issued
   auto issue = [&](int kt, int buf) INLINE {
     const int base = lds_w + buf * G::STAGE;
 #pragma unroll
     for (int n = 0; n < G::LOADS; ++n) dma16(krs, kgo[n] + kt * kstep, base + n * 1024);
 #pragma unroll
     for (int n = 0; n < G::LOADS; ++n) dma16(vrs, vgo[n] + kt * vstep, base + G::TILE + n * 1024);
-    if constexpr (KIND != FMASK_ENC_BITMAP) dma4(irs, (w * p.skv + kt * BN + lane) * 4, lds_iv + buf * G::STAGE);
+    if constexpr (KIND != FMASK_ENC_BITMAP) {
+      dma4(irs, (w * p.skv + kt * BN + lane) * 4, lds_iv + buf * G::STAGE);
+    } else {
+      // this wave's 64 x 64 block of key tile kt (state read with a scalar
+      // load of its aligned word: the encoder pads the state array) and, when
+      // PARTIAL, the row words of its 32 rows, loaded into this wave's share
+      // of the stage's interval area (which the bitmap form does not use)
+      const int bi = 2 * qt + (w >> 1);
+      int st = FMASK_SKIP;
+      if (bi < p.nbq) {
+        const int64_t x = ((int64_t)(mb * p.mh + mh) * p.nbq + bi) * p.nbk + kt;
+        const int wd = sload_wait((const int32_t*)(p.bstate + (x & ~(int64_t)3)));
+        st = (wd >> (8 * (int)(x & 3))) & 0xff;
+        if (st == FMASK_PARTIAL) {
+          const int pool = sload_wait(p.bindex + x);
+          dma4(make_rsrc(p.bbits + (int64_t)pool * 64 + (w & 1) * 32, 256), lane * 4, lds_iv + buf * G::STAGE);
+        }
+      }
+      st_next = st;
+    }
   };
 
   uint32_t* rmask = (uint32_t*)(smem + G::RM0) + w * BN;
   __syncthreads();
   if (cnt > 0) {
-    int e_cur = list[0];
+    // (list entries by scalar loads: they wait on the scalar counter only,
+    // never on the vector-memory counter that the tile loads in flight hold up)
+    int e_cur = sload_wait(list);
     issue(e_cur & 0x7fffffff, 0);
+    int st_cur = st_next;
     wait_all();
     barrier();
     for (int i = 0; i < cnt; ++i) {
       const bool more = i + 1 < cnt;
-      const int e_next = more ? list[i + 1] : 0;
+      const int e_next = more ? sload_wait(list + i + 1) : 0;
       if (more) issue(e_next & 0x7fffffff, (i + 1) & 1);
       const int kt = e_cur & 0x7fffffff;
       const char* kb = smem + (i & 1) * G::STAGE;
@@ -268,12 +282,11 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdParams p, int expand, int 
       // bit c of `vis` says key kt BN + c is visible to this lane's row
       uint64_t vis = ~0ull;
       if constexpr (KIND == FMASK_ENC_BITMAP) {
-        int pool = 0;
-        const int st = block_state(p, mb * p.mh + mh, 2 * qt + (w >> 1), kt, &pool);
+        const int st = st_cur;
         skip = st == FMASK_SKIP;
         need_mask = !skip && (st == FMASK_PARTIAL || ragged);
         if (need_mask) {
-          if (st == FMASK_PARTIAL) vis = p.bbits[(int64_t)pool * 64 + (w & 1) * 32 + l32];
+          if (st == FMASK_PARTIAL) vis = *(const uint64_t*)((const char*)raw + w * BN * 4 + l32 * 8);
           const int nk = p.skv - kt * BN;  // keys of this tile below skv
           if (nk < 64) vis &= (1ull << nk) - 1ull;
         }
@@ -370,6 +383,7 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdParams p, int expand, int 
       wait_all();  // tile i+1 landed; every wave is done with tile i
       barrier();
       e_cur = e_next;
+      st_cur = st_next;
     }
   }
 
@@ -397,7 +411,8 @@ struct GeoKV {
   static constexpr int Q0 = 0, DO0 = TILE;       // Q tile, dO tile
   static constexpr int RW0 = 2 * TILE;           // [128 rows] x {D_i, LSE2_i}
   static constexpr int STAGE = RW0 + BM * 8;     // two stages (double-buffered)
-  static constexpr int END = 2 * STAGE;
+  static constexpr int BW0 = 2 * STAGE;          // bitmap: [2 stages][4 waves] x 64 row words
+  static constexpr int END = BW0 + 2 * 4 * 512;
   static constexpr int LOADS = BM * KCH / 256;
 };
 
@@ -431,6 +446,10 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
   if (l >= n_items) return;
   int col, b, g;
   kv_item(p, expand, l, &col, &b, &g);
+  // (uniform, so that list and block-state reads below are scalar loads)
+  col = __builtin_amdgcn_readfirstlane(col);
+  b = __builtin_amdgcn_readfirstlane(b);
+  g = __builtin_amdgcn_readfirstlane(g);
   const int kt = col % p.nkt;
   const int mb = (p.mb == 1) ? 0 : b;
 
@@ -484,10 +503,18 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
   auto col_of = [&](int hi) INLINE -> int {
     return (mb * p.mh + (p.mh == 1 ? 0 : g * p.group + hi)) * p.nkt + kt;
   };
-  auto count_of = [&](int hi) INLINE -> int { return p.col_count[col_of(hi)]; };
+  // (list, count and block-state entries by scalar loads, as in k_bwd_dkdv8)
+  auto count_of = [&](int hi) INLINE -> int { return sload_wait(p.col_count + col_of(hi)); };
+  auto entry_of = [&](int hi, int i) INLINE -> int {
+    return sload_wait(p.col_list + (int64_t)col_of(hi) * p.nqt + i);
+  };
+  // Bitmap: this wave's 64 x 64 block of the staged pair and, when PARTIAL,
+  // its 64 row words loaded into the stage's slot of this wave.
+  int st_next = FMASK_SKIP;
+  const int lds_bw = __builtin_amdgcn_readfirstlane(lds_addr(smem) + G::BW0 + w * 512);
   auto stage = [&](int hi, int i, int buf) INLINE {
     const int h = g * p.group + hi;
-    const int qt = p.col_list[(int64_t)col_of(hi) * p.nqt + i] & 0x7fffffff;
+    const int qt = entry_of(hi, i) & 0x7fffffff;
     const __bf16* Q = (const __bf16*)p.q + b * p.qs[0] + h * p.qs[1];
     const __bf16* dO = (const __bf16*)p.dout + b * p.os[0] + h * p.os[1];
     const float* ws = p.ws + ((int64_t)b * p.hq + h) * p.sq * 2;
@@ -507,6 +534,20 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
     }
     // 128 rows x 8 bytes = 1 KB of row values, one 16-byte load per lane of wave 0
     if (w == 0) dma16(wrs, (qt * BM * 2 + lane * 4) * 4, lds_rw + buf * G::STAGE);
+    if constexpr (KIND == FMASK_ENC_BITMAP) {
+      const int bi = 2 * qt + rw;
+      int st = FMASK_SKIP;
+      if (bi < p.nbq) {
+        const int64_t x = ((int64_t)(mb * p.mh + (p.mh == 1 ? 0 : h)) * p.nbq + bi) * p.nbk + kt;
+        const int wd = sload_wait((const int32_t*)(p.bstate + (x & ~(int64_t)3)));
+        st = (wd >> (8 * (int)(x & 3))) & 0xff;
+        if (st == FMASK_PARTIAL) {
+          const int pool = sload_wait(p.bindex + x);
+          if (lane < 32) dma16(make_rsrc(p.bbits + (int64_t)pool * 64, 512), lane * 16, lds_bw + buf * 4 * 512);
+        }
+      }
+      st_next = st;
+    }
   };
 
   int hi = 0;
@@ -516,6 +557,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
   if (hi < p.group) {
     int i = 0, buf = 0;
     stage(hi, i, 0);
+    int st_cur = st_next;
     wait_all();
     barrier();
     while (true) {
@@ -536,7 +578,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
         }
         wait_all();
       }
-      const int e = p.col_list[(int64_t)col_of(hi) * p.nqt + i];
+      const int e = entry_of(hi, i);
       if (more) stage(nh, ni, buf ^ 1);
       const int qt = e & 0x7fffffff;
 
@@ -553,8 +595,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
       uint64_t keep = 0;
       if constexpr (KIND == FMASK_ENC_BITMAP) {
         // the wave's 64 rows are one block row: its 64 x 64 block of this key tile
-        int pool = 0;
-        const int st = block_state(p, mb * p.mh + mhh, 2 * qt + rw, kt, &pool);
+        const int st = st_cur;
         wskip = st == FMASK_SKIP;
         full = st == FMASK_FULL && (kt + 1) * BN <= p.skv && na == 64;
         if (!wskip && !full) {
@@ -562,7 +603,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
           if (st == FMASK_PARTIAL) {
             // lane r holds the block's row word r; one ballot per key of this
             // wave's half gathers that key's column
-            const uint64_t roww = p.bbits[(int64_t)pool * 64 + lane];
+            const uint64_t roww = *(const uint64_t*)(smem + G::BW0 + (buf * 4 + w) * 512 + lane * 8);
 #pragma unroll 4
             for (int kk = 0; kk < 32; ++kk) {
               const uint64_t cw = __ballot((roww >> (kw * 32 + kk)) & 1ull);
@@ -684,6 +725,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
       hi = nh;
       i = ni;
       buf ^= 1;
+      st_cur = st_next;
     }
   }
 
@@ -740,7 +782,8 @@ struct GeoKV8 {
   static constexpr int RW0 = 2 * TILE;           // [128 rows] x {D_i, LSE2_i}
   static constexpr int STAGE = RW0 + BM * 8;     // two stages (double-buffered)
   static constexpr int V0 = 2 * STAGE;           // V tile [64 keys][D]
-  static constexpr int END = V0 + BN * D * 2;
+  static constexpr int BW0 = V0 + BN * D * 2;    // bitmap: [2 stages][8 waves] x 64 row words
+  static constexpr int END = BW0 + 2 * 8 * 512;
   static constexpr int LOADS = BM * KCH / 512;   // 16-byte loads per wave and tile
   static constexpr int RED = 2 * 2 * 2 * (D / 32) * 16 * 64 * 4;  // 2 quarters x 2 key halves x dK, dV
 };
@@ -752,13 +795,17 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkdv8(BwdParams p, int expand, i
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using G = GeoKV8<D>;
   constexpr int DB = D / 32, KT = D / 16;
-  constexpr int kA = 2, kV = 2;  // read-ahead of the A fragments and of the V fragments
+  constexpr int kA = 2, kV = 1;  // read-ahead of the A fragments and of the V fragments
   __shared__ __attribute__((aligned(1024))) char smem[G::END];
 
   const int l = blockIdx.x;
   if (l >= n_items) return;
   int col, b, g;
   kv_item(p, expand, l, &col, &b, &g);
+  // (uniform, so that list and block-state reads below are scalar loads)
+  col = __builtin_amdgcn_readfirstlane(col);
+  b = __builtin_amdgcn_readfirstlane(b);
+  g = __builtin_amdgcn_readfirstlane(g);
   const int kt = col % p.nkt;
   const int mb = (p.mb == 1) ? 0 : b;
 
@@ -790,12 +837,9 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkdv8(BwdParams p, int expand, i
 #pragma unroll
   for (int i = 0; i < DB; ++i) dk[i] = dv[i] = f32x16{};
   const float c = p.scale * kLog2e;
-  int tlo[DB], thi[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    tlo[db] = tr_off<D>(lane, db, 0);
-    thi[db] = tr_off<D>(lane, db, 1);
-  }
+  // transposing-read offsets of d-block 0; d-block db's are these XOR
+  // db << 6 (the swizzle only XORs chunk bits, and db is chunk bits 2 - 3)
+  const int tlo0 = tr_off<D>(lane, 0, 0), thi0 = tr_off<D>(lane, 0, 1);
   const int lds_w = __builtin_amdgcn_readfirstlane(lds_addr(smem) + w * G::LOADS * 1024);
   const int lds_rw = __builtin_amdgcn_readfirstlane(lds_addr(smem) + G::RW0);
   constexpr int RPI = 64 / G::KCH;
@@ -804,10 +848,21 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkdv8(BwdParams p, int expand, i
   auto col_of = [&](int hi) INLINE -> int {
     return (mb * p.mh + (p.mh == 1 ? 0 : g * p.group + hi)) * p.nkt + kt;
   };
-  auto count_of = [&](int hi) INLINE -> int { return p.col_count[col_of(hi)]; };
+  // List and count entries are read with scalar loads: they wait on the
+  // scalar counter only, never on the vector-memory counter that the tile
+  // loads in flight hold up.
+  auto count_of = [&](int hi) INLINE -> int { return sload_wait(p.col_count + col_of(hi)); };
+  auto entry_of = [&](int hi, int i) INLINE -> int {
+    return sload_wait(p.col_list + (int64_t)col_of(hi) * p.nqt + i);
+  };
+  // Bitmap: this wave's 64 x 64 block of the staged pair (state, read with a
+  // scalar load of its aligned word: the encoder pads the state array) and,
+  // when PARTIAL, its 64 row words loaded into the stage's slot of this wave.
+  int st_next = FMASK_SKIP;
+  const int lds_bw = __builtin_amdgcn_readfirstlane(lds_addr(smem) + G::BW0 + w * 512);
   auto stage = [&](int hi, int i, int buf) INLINE {
     const int h = g * p.group + hi;
-    const int qt = p.col_list[(int64_t)col_of(hi) * p.nqt + i] & 0x7fffffff;
+    const int qt = entry_of(hi, i) & 0x7fffffff;
     const __bf16* Q = (const __bf16*)p.q + b * p.qs[0] + h * p.qs[1];
     const __bf16* dO = (const __bf16*)p.dout + b * p.os[0] + h * p.os[1];
     const float* ws = p.ws + ((int64_t)b * p.hq + h) * p.sq * 2;
@@ -824,6 +879,22 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkdv8(BwdParams p, int expand, i
       dma16s(ors, (int)(tr * p.os[2] * 2) + tc, (int)(rs * p.os[2] * 2), base + G::DO0 + n * 1024);
     }
     if (w == 0) dma16(wrs, (qt * BM * 2 + lane * 4) * 4, lds_rw + buf * G::STAGE);
+    if constexpr (KIND == FMASK_ENC_BITMAP) {
+      const int slice = mb * p.mh + (p.mh == 1 ? 0 : h);
+      const int bi = 2 * qt + (rw >> 1);
+      int st = FMASK_SKIP;
+      if (bi < p.nbq) {
+        const int64_t x = ((int64_t)slice * p.nbq + bi) * p.nbk + kt;
+        const int wd = sload_wait((const int32_t*)(p.bstate + (x & ~(int64_t)3)));
+        st = (wd >> (8 * (int)(x & 3))) & 0xff;
+        if (st == FMASK_PARTIAL) {
+          const int pool = sload_wait(p.bindex + x);
+          const rsrc_t brs = make_rsrc(p.bbits + (int64_t)pool * 64, 512);
+          if (lane < 32) dma16(brs, lane * 16, lds_bw + buf * 8 * 512);
+        }
+      }
+      st_next = st;
+    }
   };
 
   int hi = 0;
@@ -833,6 +904,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkdv8(BwdParams p, int expand, i
   if (hi < p.group) {
     int i = 0, buf = 0;
     stage(hi, i, 0);
+    int st_cur = st_next;
     wait_all();
     barrier();
     while (true) {
@@ -851,7 +923,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkdv8(BwdParams p, int expand, i
         }
         wait_all();
       }
-      const int e = p.col_list[(int64_t)col_of(hi) * p.nqt + i];
+      const int e = entry_of(hi, i);
       if (more) stage(nh, ni, buf ^ 1);
       const int qt = e & 0x7fffffff;
 
@@ -867,14 +939,13 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkdv8(BwdParams p, int expand, i
       uint32_t keep = 0;
       if constexpr (KIND == FMASK_ENC_BITMAP) {
         // the wave's 32 rows are one half of a 64-row block row
-        int pool = 0;
-        const int st = block_state(p, mb * p.mh + mhh, 2 * qt + (rw >> 1), kt, &pool);
+        const int st = st_cur;
         wskip = st == FMASK_SKIP || na == 0;
         full = st == FMASK_FULL && (kt + 1) * BN <= p.skv && na == 32;
         if (!wskip && !full) {
           uint64_t colw = 0;  // the block's rows that see this lane's key
           if (st == FMASK_PARTIAL) {
-            const uint64_t roww = p.bbits[(int64_t)pool * 64 + lane];
+            const uint64_t roww = *(const uint64_t*)(smem + G::BW0 + (buf * 8 + w) * 512 + lane * 8);
 #pragma unroll 4
             for (int kk = 0; kk < 32; ++kk) {
               const uint64_t cw = __ballot((roww >> (kw * 32 + kk)) & 1ull);
@@ -972,7 +1043,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkdv8(BwdParams p, int expand, i
         {
           auto frag = [&](int m) INLINE -> bf16x8 {
             const int db = m / 4, ks = (m / 2) % 2;
-            return tr_frag<D>((m & 1) ? qb : ob, lr0 + 16 * ks, tlo[db], thi[db]);
+            return tr_frag<D>((m & 1) ? qb : ob, lr0 + 16 * ks, tlo0 ^ (db << 6), thi0 ^ (db << 6));
           };
           bf16x8 fr[kAhead];
 #pragma unroll
@@ -995,6 +1066,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkdv8(BwdParams p, int expand, i
       hi = nh;
       i = ni;
       buf ^= 1;
+      st_cur = st_next;
     }
   }
 

@@ -13,7 +13,9 @@ contributing nothing):
 
 ``attention_dense`` evaluates this with dense QK^T over ALL key columns for a
 chunk of rows, applies the materialised mask with np.where and multiplies the
-dense P by V.  ``attention_rows`` does the same for a list of sampled rows,
+dense P by V; ``attention_backward_dense`` gives its gradient the same way, and
+``attention_backward_sampled`` that gradient at sampled rows and keys.
+``attention_rows`` does the forward for a list of sampled rows,
 ``attention_bruteforce`` with scalar Python loops, and
 ``attention_listed_cells`` only over the cells a selected-key list names (the
 host FP64 reference "over the listed cells" that the llama.cpp selected-key PR
@@ -204,4 +206,59 @@ def attention_backward_dense(q, k, v, do, vis_fn, scale, row_chunk=512):
                 ds = p * (dp - delta[:, None])
                 dq[b, h, rows] = scale * (ds @ k[b, g])
                 dk[b, g] += scale * (ds.T @ q[b, h, rows])
+    return dq, dk, dv
+
+
+def attention_backward_sampled(q, k, v, do, vis_fn, scale, b, rows, keys, row_chunk=512):
+    """The gradient of attention_backward_dense at sampled outputs of batch
+    entry b: dQ at query rows `rows` (every head) and dK, dV at key positions
+    `keys` (every K/V head), from the same definition, evaluated only where
+    those outputs depend on it.
+
+    dQ_i = scale sum_j dS_ij K_j needs row i alone (its P, dP and D_i).
+    dK_j = scale sum_{h in group, i} dS_ij Q_i and dV_j = sum P_ij dO_i run over
+    the rows with P_ij > 0, i.e. the rows whose mask shows key j (P is zero
+    elsewhere): those rows are found from the materialised mask and evaluated
+    whole (P_ij needs the row's LSE, dS_ij its D_i).
+    Returns dq [Hq, len(rows), D], dk [Hkv, len(keys), D], dv [Hkv, len(keys), Dv].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    _, Hq, Sq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+
+    def row_terms(h, rr):
+        """P and dS of rows rr of head h against every key."""
+        g = h // G
+        vis = np.asarray(vis_fn(b, h, rr), dtype=bool)
+        s = scale * (q[b, h, rr] @ k[b, g].T)
+        _, lse = _softmax_rows(s, vis, v[b, g])
+        nonempty = np.isfinite(lse)
+        p = np.where(vis & nonempty[:, None], np.exp(s - np.where(nonempty, lse, 0.0)[:, None]), 0.0)
+        dp = do[b, h, rr] @ v[b, g].T
+        delta = (p * dp).sum(axis=1)
+        return p, p * (dp - delta[:, None])
+
+    dq = np.zeros((Hq, len(rows), D))
+    dk = np.zeros((Hkv, len(keys), D))
+    dv = np.zeros((Hkv, len(keys), v.shape[3]))
+    for h in range(Hq):
+        g = h // G
+        if len(rows):
+            _, ds = row_terms(h, rows)
+            dq[h] = scale * (ds @ k[b, g])
+        if len(keys):
+            for r0 in range(0, Sq, row_chunk):
+                rr = np.arange(r0, min(Sq, r0 + row_chunk))
+                rr = rr[np.asarray(vis_fn(b, h, rr), dtype=bool)[:, keys].any(axis=1)]
+                if len(rr) == 0:
+                    continue
+                p, ds = row_terms(h, rr)
+                dv[g] += p[:, keys].T @ do[b, h, rr]
+                dk[g] += scale * (ds[:, keys].T @ q[b, h, rr])
     return dq, dk, dv

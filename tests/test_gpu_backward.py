@@ -5,7 +5,8 @@ The forward output O and LSE the backward consumes come from the GPU forward
 (they are inputs of the operation, like dO); the reference gradient is the
 oracle's, computed from the same bf16 Q, K, V and dO alone.  Small shapes span
 several tiles with ragged tails, GQA and per-head masks; the 8K causal-document
-workload is checked on one K/V head group at its full size.
+workload is checked on one K/V head group at its full size, and the 32K one on
+sampled rows and keys (attention_backward_sampled).
 """
 
 import math
@@ -138,6 +139,48 @@ def test_bitmap_masks(D):
 def test_full_size_causal_doc_8k_one_group():
     w = synth.workload("causal_doc_8k")
     _grad_check(w, w["mask"], "causal_doc_8k heads 0..3", heads=(0, 4))
+
+
+def test_full_size_causal_doc_32k_sampled():
+    """The 32K causal-document backward at the size the bench times, against
+    the float64 oracle on sampled outputs (attention_backward_sampled, pinned to
+    the dense gradient on the CPU): dQ of 35 rows of query heads 0..3 (the
+    sequence's first and last rows, tile and document edges, seeded others) and
+    dK, dV of 12 keys of K/V head 0 in three documents (their first, middle and
+    last keys, and a tile edge)."""
+    w = synth.workload("causal_doc_32k")
+    spec = w["mask"]
+    arrays = synth.draw_qkv(w)
+    do_bits = synth.draw_dout(w)
+    q, k, v = to_device(w, arrays)
+    do = torch.from_numpy(do_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    enc = fm.encode(spec)
+    tiles = fm.classify(enc, 128, 64)
+    o, lse = fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"])
+    dq, dk, dv = fm.attn_bwd(q, k, v, o, lse, do, enc, tiles, scale=w["scale"])
+    torch.cuda.synchronize()
+    G = w["Hq"] // w["Hkv"]
+    S = w["Sq"]
+    L = np.array(w["doc_lengths"])
+    st = np.concatenate([[0], np.cumsum(L)])
+    rng = np.random.default_rng(7)
+    rows = sorted(set([0, 1, 127, 128, S - 1] + [int(st[d]) for d in (1, 7, 14)] +
+                      [int(st[d + 1] - 1) for d in (0, 7, 13)] + [int(x) for x in rng.choice(S, 24, replace=False)]))
+    keys = sorted(set([0, 1, 63, 64, int(L[0] - 1), int(st[3]), int(st[3] + L[3] // 2), int(st[4] - 1),
+                       int(st[13]), int(st[13] + 1), int(st[14] - 2), int(st[14] - 1)]))
+    qq, dd = (to_f64(w, a[:, :G]) for a in (arrays[0], do_bits))
+    kk, vv = (to_f64(w, a[:, :1]) for a in (arrays[1], arrays[2]))
+    rq, rk, rv = OA.attention_backward_sampled(qq, kk, vv, dd, OA.spec_vis_fn(spec), w["scale"], 0, rows, keys)
+    got = dict(dq=dq[0, :G][:, rows], dk=dk[0, :1][:, keys], dv=dv[0, :1][:, keys])
+    for name, ref in (("dq", rq), ("dk", rk), ("dv", rv)):
+        g = got[name].float().cpu().numpy().astype(np.float64)
+        assert np.isfinite(g).all(), f"{name} not finite"
+        scale = max(np.abs(ref).max(), 1e-6)
+        err = np.abs(g - ref)
+        print(f"causal_doc_32k sampled {name}: max {err.max() / scale:.2e}, mean {err.mean() / scale:.2e} "
+              f"of the largest sampled reference value", flush=True)
+        assert err.max() <= GRAD_TOL["max_rel"] * scale, f"{name} max err {err.max():.3e} (ref max {scale:.3e})"
+        assert err.mean() <= GRAD_TOL["mean_rel"] * scale, f"{name} mean err {err.mean():.3e}"
 
 
 def test_unsupported_combinations_are_refused():

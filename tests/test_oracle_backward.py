@@ -98,3 +98,23 @@ def test_causal_family_mask_matches_torch_causal_sdpa_gradient():
     assert np.abs(tq.grad.numpy() - dq).max() < 1e-12
     assert np.abs(tk.grad.numpy() - dk).max() < 1e-12
     assert np.abs(tv.grad.numpy() - dv).max() < 1e-12
+
+
+@pytest.mark.parametrize("seed", [4, 5, 6])
+def test_sampled_gradient_matches_the_dense_one(seed):
+    """attention_backward_sampled against the pinned dense gradient at every
+    sampled row and key, per batch entry (random masks with an empty row and
+    unseen keys, GQA 2)."""
+    q, k, v, do, vis, fn = _case(seed)
+    vis[1, :, :, 7] = False  # a key that no row sees
+    scale = 0.41
+    dq, dk, dv = OA.attention_backward_dense(q, k, v, do, fn, scale, row_chunk=6)
+    rng = np.random.default_rng(seed)
+    for b in range(q.shape[0]):
+        rows = np.sort(rng.choice(q.shape[2], 9, replace=False))
+        keys = np.sort(np.append(rng.choice(k.shape[2], 6, replace=False), 7))
+        sq, sk, sv = OA.attention_backward_sampled(q, k, v, do, fn, scale, b, rows, keys, row_chunk=5)
+        assert np.abs(sq - dq[b][:, rows]).max() < 1e-12
+        assert np.abs(sk - dk[b][:, keys]).max() < 1e-12
+        assert np.abs(sv - dv[b][:, keys]).max() < 1e-12
+    assert np.abs(OA.attention_backward_sampled(q, k, v, do, fn, scale, 1, [], [7])[1]).max() == 0.0

@@ -5,8 +5,8 @@ The forward output O and LSE the backward consumes come from the GPU forward
 (they are inputs of the operation, like dO); the reference gradient is the
 oracle's, computed from the same bf16 Q, K, V and dO alone.  Small shapes span
 several tiles with ragged tails, GQA and per-head masks; the 8K causal-document
-workload is checked on one K/V head group at its full size, and the 32K one on
-sampled rows and keys (attention_backward_sampled).
+workload is checked on one K/V head group at its full size, and the 32K one and
+the two bitmap workloads on sampled rows and keys (attention_backward_sampled).
 """
 
 import math
@@ -181,6 +181,44 @@ def test_full_size_causal_doc_32k_sampled():
               f"of the largest sampled reference value", flush=True)
         assert err.max() <= GRAD_TOL["max_rel"] * scale, f"{name} max err {err.max():.3e} (ref max {scale:.3e})"
         assert err.mean() <= GRAD_TOL["mean_rel"] * scale, f"{name} mean err {err.mean():.3e}"
+
+
+@pytest.mark.parametrize("name,b", [("tree_4k", 0), ("block_bitmap_16k", 2)])
+def test_full_size_bitmap_sampled(name, b):
+    """Bitmap masks at full size (the BFS-numbered tree, and one batch entry of
+    the per-batch random block pattern) against the float64 oracle on sampled
+    outputs: dQ of 28 rows and dK, dV of 12 keys of head 0 (block and tile
+    edges, the last row and key, seeded others)."""
+    w = synth.workload(name)
+    spec = w["mask"]
+    arrays = synth.draw_qkv(w)
+    do_bits = synth.draw_dout(w)
+    q, k, v = to_device(w, arrays)
+    do = torch.from_numpy(do_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    enc = fm.encode(spec)
+    assert enc.kind == fm.ENC_BITMAP
+    tiles = fm.classify(enc, 128, 64)
+    o, lse = fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"])
+    dq, dk, dv = fm.attn_bwd(q, k, v, o, lse, do, enc, tiles, scale=w["scale"])
+    torch.cuda.synchronize()
+    G = w["Hq"] // w["Hkv"]
+    S, K = w["Sq"], w["Skv"]
+    rng = np.random.default_rng(11)
+    rows = sorted(set([0, 63, 64, 127, 128, S - 1] + [int(x) for x in rng.choice(S, 22, replace=False)]))
+    keys = sorted(set([0, 63, 64, K // 2, K - 1] + [int(x) for x in rng.choice(K, 7, replace=False)]))
+    qq, dd = (to_f64(w, a[:, :G]) for a in (arrays[0], do_bits))
+    kk, vv = (to_f64(w, a[:, :1]) for a in (arrays[1], arrays[2]))
+    rq, rk, rv = OA.attention_backward_sampled(qq, kk, vv, dd, OA.spec_vis_fn(spec), w["scale"], b, rows, keys)
+    got = dict(dq=dq[b, :G][:, rows], dk=dk[b, :1][:, keys], dv=dv[b, :1][:, keys])
+    for nm, ref in (("dq", rq), ("dk", rk), ("dv", rv)):
+        g = got[nm].float().cpu().numpy().astype(np.float64)
+        assert np.isfinite(g).all(), f"{name} {nm} not finite"
+        scale = max(np.abs(ref).max(), 1e-6)
+        err = np.abs(g - ref)
+        print(f"{name} batch {b} sampled {nm}: max {err.max() / scale:.2e}, mean {err.mean() / scale:.2e} "
+              f"of the largest sampled reference value", flush=True)
+        assert err.max() <= GRAD_TOL["max_rel"] * scale, f"{name} {nm} max err {err.max():.3e} (ref max {scale:.3e})"
+        assert err.mean() <= GRAD_TOL["mean_rel"] * scale, f"{name} {nm} mean err {err.mean():.3e}"
 
 
 def test_unsupported_combinations_are_refused():

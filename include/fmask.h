@@ -406,9 +406,8 @@ size_t fmask_attn_bwd_workspace_bytes(const fmask_attn_args *args, const fmask_t
  * bytes (16-byte aligned); its contents are rewritten by every call.
  * Supported: BF16, d in {64, 128}, INTERVALS or BITMAP encodings (every
  * family but selected-key lists; the bitmap form holds tree, block and dense
- * masks; its block-state array read in aligned 4-byte words, so it must start
- * 4-byte aligned, as fmask_encode lays it out), the tile table at 128 x 64
- * (fmask_preferred_tile); otherwise FMASK_ERR_UNSUPPORTED.                     */
+ * masks), the tile table at 128 x 64 (fmask_preferred_tile); otherwise
+ * FMASK_ERR_UNSUPPORTED.                                                       */
 fmask_status fmask_attn_bwd(const fmask_attn_args *args, const void *q, const void *k,
                             const void *v, const void *o, const float *lse, const void *dout,
                             void *dq, void *dk, void *dv, void *workspace,

@@ -919,8 +919,6 @@ fmask_status fmask_attn_bwd(const fmask_attn_args* a, const void* q, const void*
       tiles->batch != enc->batch || tiles->heads != enc->heads)
     return fail(FMASK_ERR_INVALID, "tile table does not match the encoding");
   if (check_mask_data(enc) != FMASK_OK) return FMASK_ERR_INVALID;
-  if (enc->kind == FMASK_ENC_BITMAP && ((uintptr_t)enc->blk_state % 4))
-    return fail(FMASK_ERR_UNSUPPORTED, "backward: bitmap block states must start 4-byte aligned");
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
     return fail(FMASK_ERR_INVALID, "null tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||

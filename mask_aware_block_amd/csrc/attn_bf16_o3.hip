@@ -162,10 +162,18 @@ __global__ void __launch_bounds__(NT, 3) k_attn_o3(TileAttnParams p, int gsz) {
       binfo[kBinfo + i] = block_info(e, 1);
     }
   }
-  // This wave's block of list entry i (entry value e).
+  // This wave's block of list entry i (entry value e).  Past the staged
+  // entries the block is read with scalar loads: a vector load's wait would
+  // also drain the tile loads in flight.
+  const int qt_u = __builtin_amdgcn_readfirstlane(it.qt);
+  const int64_t bbase_u = (int64_t)__builtin_amdgcn_readfirstlane((int)(bbase));
   auto wave_block = [&](int i, int e) INLINE -> int {
     if (i < kBinfo) return __builtin_amdgcn_readfirstlane(binfo[(w >> 1) * kBinfo + i]);
-    return __builtin_amdgcn_readfirstlane(block_info(e, w >> 1));
+    const int bi = 2 * qt_u + (w >> 1), kt = e & 0x7fffffff;
+    if (bi >= p.nbq) return kBlkSkip;
+    const int64_t bx = (bbase_u + bi) * p.nbk + kt;
+    const int st = sload_byte(p.bstate + bx);
+    return st == FMASK_PARTIAL ? sload_wait(p.bindex + bx) : (st == FMASK_FULL ? kBlkFull : kBlkSkip);
   };
 
 

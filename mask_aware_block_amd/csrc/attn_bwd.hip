@@ -239,15 +239,13 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdParams p, int expand, int 
       dma4(irs, (w * p.skv + kt * BN + lane) * 4, lds_iv + buf * G::STAGE);
     } else {
       // this wave's 64 x 64 block of key tile kt (state read with a scalar
-      // load of its aligned word: the encoder pads the state array) and, when
-      // PARTIAL, the row words of its 32 rows, loaded into this wave's share
+      // load) and, when PARTIAL, the row words of its 32 rows, loaded into this wave's share
       // of the stage's interval area (which the bitmap form does not use)
       const int bi = 2 * qt + (w >> 1);
       int st = FMASK_SKIP;
       if (bi < p.nbq) {
         const int64_t x = ((int64_t)(mb * p.mh + mh) * p.nbq + bi) * p.nbk + kt;
-        const int wd = sload_wait((const int32_t*)(p.bstate + (x & ~(int64_t)3)));
-        st = (wd >> (8 * (int)(x & 3))) & 0xff;
+        st = sload_byte(p.bstate + x);
         if (st == FMASK_PARTIAL) {
           const int pool = sload_wait(p.bindex + x);
           dma4(make_rsrc(p.bbits + (int64_t)pool * 64 + (w & 1) * 32, 256), lane * 4, lds_iv + buf * G::STAGE);
@@ -539,8 +537,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkdv(BwdParams p, int expand, in
       int st = FMASK_SKIP;
       if (bi < p.nbq) {
         const int64_t x = ((int64_t)(mb * p.mh + (p.mh == 1 ? 0 : h)) * p.nbq + bi) * p.nbk + kt;
-        const int wd = sload_wait((const int32_t*)(p.bstate + (x & ~(int64_t)3)));
-        st = (wd >> (8 * (int)(x & 3))) & 0xff;
+        st = sload_byte(p.bstate + x);
         if (st == FMASK_PARTIAL) {
           const int pool = sload_wait(p.bindex + x);
           if (lane < 32) dma16(make_rsrc(p.bbits + (int64_t)pool * 64, 512), lane * 16, lds_bw + buf * 4 * 512);
@@ -855,9 +852,9 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkdv8(BwdParams p, int expand, i
   auto entry_of = [&](int hi, int i) INLINE -> int {
     return sload_wait(p.col_list + (int64_t)col_of(hi) * p.nqt + i);
   };
-  // Bitmap: this wave's 64 x 64 block of the staged pair (state, read with a
-  // scalar load of its aligned word: the encoder pads the state array) and,
-  // when PARTIAL, its 64 row words loaded into the stage's slot of this wave.
+  // Bitmap: this wave's 64 x 64 block of the staged pair (state read with a
+  // scalar load) and, when PARTIAL, its 64 row words loaded into the stage's
+  // slot of this wave.
   int st_next = FMASK_SKIP;
   const int lds_bw = __builtin_amdgcn_readfirstlane(lds_addr(smem) + G::BW0 + w * 512);
   auto stage = [&](int hi, int i, int buf) INLINE {
@@ -885,8 +882,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkdv8(BwdParams p, int expand, i
       int st = FMASK_SKIP;
       if (bi < p.nbq) {
         const int64_t x = ((int64_t)slice * p.nbq + bi) * p.nbk + kt;
-        const int wd = sload_wait((const int32_t*)(p.bstate + (x & ~(int64_t)3)));
-        st = (wd >> (8 * (int)(x & 3))) & 0xff;
+        st = sload_byte(p.bstate + x);
         if (st == FMASK_PARTIAL) {
           const int pool = sload_wait(p.bindex + x);
           const rsrc_t brs = make_rsrc(p.bbits + (int64_t)pool * 64, 512);

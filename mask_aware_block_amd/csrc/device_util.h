@@ -78,4 +78,13 @@ __device__ inline int sload_wait(const int32_t* p) {
   return v;
 }
 
+// One byte of a device array by a scalar load of the aligned 4-byte word that
+// holds it (wave-uniform address).  The word never leaves the byte's own
+// aligned 4 bytes, so any base alignment is fine.
+__device__ inline int sload_byte(const uint8_t* p) {
+  const uintptr_t a = (uintptr_t)p;
+  const int w = sload_wait((const int32_t*)(a & ~(uintptr_t)3));
+  return (w >> (8 * (int)(a & 3))) & 0xff;
+}
+
 }  // namespace fmask

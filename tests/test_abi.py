@@ -215,10 +215,6 @@ def test_split_backward_varlen_dense_host_validation():
     assert b"bitmap array" in L.fmask_last_error()
     bmp.blk_bits = p.value
     assert L.fmask_attn_bwd(*args, p, need - 16, ctypes.byref(bmp), ctypes.byref(t), None) == fm.ERR_CAPACITY
-    bmp.blk_state = p.value + 1  # the backward reads block states in aligned 4-byte words
-    assert L.fmask_attn_bwd(*args, p, need, ctypes.byref(bmp), ctypes.byref(t), None) == fm.ERR_UNSUPPORTED
-    assert b"4-byte aligned" in L.fmask_last_error()
-    bmp.blk_state = p.value
     # varlen: segment lengths must add up, modes must be known
     enc = fm.Encoded()
     cu = np.array([0, 100, 300], dtype=np.int32)

@@ -165,13 +165,17 @@ __global__ void __launch_bounds__(NT, D == 64 ? 3 : 2)
   auto shared_at = [&](int i) INLINE -> bool {
     return i < cnt0 && i < cnt1 && kt_of(0, i) == kt_of(1, i);
   };
+  // Past the staged entries the block info is read with scalar loads: a
+  // vector load's wait would also drain the tile loads in flight.
+  const int bbase_u = __builtin_amdgcn_readfirstlane((int)bbase);  // < 2^22 blocks (launcher)
   auto entry = [&](int i, int& kt, int& info) INLINE {
     if (i < kPList) {
       kt = __builtin_amdgcn_readfirstlane(lst[i]);
       info = __builtin_amdgcn_readfirstlane(inf[i]);
     } else {
       kt = sload_wait(list + i) & 0x7fffffff;
-      info = __builtin_amdgcn_readfirstlane(block_info(kt));
+      const int st = sload_byte(p.bstate + bbase_u + kt);
+      info = st == FMASK_PARTIAL ? sload_wait(p.bindex + bbase_u + kt) : (st == FMASK_FULL ? kBlkFull : kBlkSkip);
     }
   };
 

@@ -40,6 +40,15 @@
 namespace fmask {
 namespace {
 
+// A wave-uniform 64-bit value in scalar registers (both halves read from the
+// first active lane).
+__device__ inline int64_t rfl64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -235,10 +244,13 @@ __global__ void __launch_bounds__(64 * NW, 2) k_attn_tile_bf16(TileAttnParams p,
     uint64_t word = ~0ull;
     if (KIND == FMASK_ENC_BITMAP) {
       if (q0 + w * 32 >= p.sq) return;  // every row of this wave lies past the end
-      uint8_t st = p.bstate[(bbase + brow) * p.nbk + kt];
+      // (state and pool entry by scalar loads: a vector load's wait would also
+      // drain the next tile's loads in flight)
+      const int64_t bx = rfl64((int64_t)(bbase + brow) * p.nbk + kt);
+      const int st = sload_byte(p.bstate + bx);
       if (st == FMASK_SKIP) return;  // nothing visible in this wave's rows
       if (st == FMASK_PARTIAL) {
-        int32_t idx = p.bindex[(bbase + brow) * p.nbk + kt];
+        const int32_t idx = sload_wait(p.bindex + bx);
         word = p.bbits[(int64_t)idx * kBlk + (qrow & (kBlk - 1))];
         need_mask = true;
       } else {

@@ -218,6 +218,32 @@ def test_bitmap_long_tile_rows():
         compare(w, o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"long rows bm {bm}")
 
 
+def test_bitmap_large_pool_path():
+    """Bitmap encodings whose pool capacity passes 2^22 blocks go to the general
+    tile kernel (the 128-row and pair kernels use 32-bit pool offsets).  The
+    same small mask, with its descriptor's capacity raised past that bound,
+    takes that path at 128 x 64 and 64 x 64 tiles and must match the oracle
+    (the kernels index the pool only through its real entries)."""
+    S, K = 300, 700
+    w = _small("bf16", 128, S, K, B=1, Hq=4, Hkv=2, seed=17)
+    rng = np.random.default_rng(17)
+    nbq, nbk = -(-S // 64), -(-K // 64)
+    st, ix, bits = synth.block_pattern(rng, nbq, nbk, 0.3, 0.4)
+    spec = dict(family="block_bitmap", sq=S, skv=K, batch=1, heads=1, blk_state=st[None, None],
+                blk_index=ix[None, None].astype(np.int32), blk_bits=bits.reshape(-1, 64), force_diag=True)
+    arrays = synth.draw_qkv(w)
+    q, k, v = to_device(w, arrays)
+    enc = fm.encode(spec)
+    enc.struct.pool_cap = (1 << 22) + 1
+    qq, kk, vv = (to_f64(w, a) for a in arrays)
+    ro, rl = OA.attention_dense(qq, kk, vv, OA.spec_vis_fn(spec), w["scale"])
+    for bm in (128, 64):
+        tiles = fm.classify(enc, bm, 64)
+        o, lse = fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"])
+        torch.cuda.synchronize()
+        compare(w, o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"large-pool path bm {bm}")
+
+
 def _tile_check(w, spec, bm, what):
     arrays = synth.draw_qkv(w)
     q, k, v = to_device(w, arrays)

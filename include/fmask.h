@@ -33,6 +33,10 @@
  *    FMASK_ERR_UNSUPPORTED instead.
  *  - fmask_last_error() gives a human-readable detail of the last failure on the
  *    calling thread.
+ *  - sq or skv may be 0.  The tensors of an empty sequence (Q, O, LSE, dO, dQ
+ *    for sq = 0; K, V, dK, dV for skv = 0) may then be null, as empty device
+ *    tensors are; every other tensor pointer must be non-null.  With skv = 0
+ *    every row is empty: O = 0, LSE = -inf, dQ = 0; with sq = 0, dK = dV = 0.
  *  - Sizes: sq and skv at most 2^30, batch * heads at most 2^31 - 1 masks.  A
  *    problem whose encoding, tile table or workspace would exceed 2^44 bytes is
  *    refused with FMASK_ERR_UNSUPPORTED, and the matching *_bytes query returns

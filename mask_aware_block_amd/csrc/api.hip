@@ -302,6 +302,17 @@ fmask_status check_mask_data(const fmask_encoded* e) {
   return FMASK_OK;
 }
 
+// Tensor pointers are required when their tensor holds an element: Q and O
+// (and the backward's dO, dQ, LSE) for sq > 0, K and V (dK, dV) for skv > 0.
+// A zero-length sequence may come with null pointers, as empty device
+// tensors do.
+bool present(int64_t extent, std::initializer_list<const void*> ptrs) {
+  if (extent == 0) return true;
+  for (const void* x : ptrs)
+    if (!x) return false;
+  return true;
+}
+
 TileLayout tile_layout(const fmask_encoded* e, int32_t bm, int32_t bn) {
   TileLayout T;
   Carve c;
@@ -625,7 +636,7 @@ fmask_status fmask_attn_fwd(const fmask_attn_args* a, const void* q, const void*
   if (a->sq != enc->sq || a->skv != enc->skv) return fail(FMASK_ERR_INVALID, "sq / skv differ from the encoding");
   if (!(enc->batch == 1 || enc->batch == a->b)) return fail(FMASK_ERR_INVALID, "encoding batch must be 1 or b");
   if (!(enc->heads == 1 || enc->heads == a->hq)) return fail(FMASK_ERR_INVALID, "encoding heads must be 1 or hq");
-  if (!q || !k || !v || !o) return fail(FMASK_ERR_INVALID, "null tensor pointer");
+  if (!present(a->sq, {q, o}) || !present(a->skv, {k, v})) return fail(FMASK_ERR_INVALID, "null tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(FMASK_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
   const int64_t vec = a->dtype == FMASK_BF16 ? 8 : 4;
@@ -734,7 +745,7 @@ fmask_status split_fwd(const fmask_attn_args* a, const void* q, const void* k, c
     return fail(FMASK_ERR_INVALID, "sq / skv out of range");
   if (a->sq != enc->sq || a->skv != enc->skv) return fail(FMASK_ERR_INVALID, "sq / skv differ from the encoding");
   if (!(enc->batch == 1 || enc->batch == a->b)) return fail(FMASK_ERR_INVALID, "encoding batch must be 1 or b");
-  if (!q || !k || !v || !o) return fail(FMASK_ERR_INVALID, "null tensor pointer");
+  if (!present(a->sq, {q, o}) || !present(a->skv, {k, v})) return fail(FMASK_ERR_INVALID, "null tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(FMASK_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
   for (int i = 0; i < 3; ++i) {
@@ -837,7 +848,7 @@ fmask_status fmask_attn_fwd_blocks(const fmask_attn_args* a, const void* q, cons
   // by hand must keep fmask_encode's limit)
   if (enc->sel_n < 1 || enc->sel_n > FMASK_MAX_SEL_N)
     return fail(FMASK_ERR_INVALID, "sel_n must be in [1, %d]", FMASK_MAX_SEL_N);
-  if (!q || !k || !v || !o) return fail(FMASK_ERR_INVALID, "null tensor pointer");
+  if (!present(a->sq, {q, o}) || !present(a->skv, {k, v})) return fail(FMASK_ERR_INVALID, "null tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(FMASK_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
   for (int i = 0; i < 3; ++i) {
@@ -919,7 +930,7 @@ fmask_status fmask_attn_bwd(const fmask_attn_args* a, const void* q, const void*
       tiles->batch != enc->batch || tiles->heads != enc->heads)
     return fail(FMASK_ERR_INVALID, "tile table does not match the encoding");
   if (check_mask_data(enc) != FMASK_OK) return FMASK_ERR_INVALID;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+  if (!present(a->sq, {q, o, lse, dout, dq}) || !present(a->skv, {k, v, dk, dv}))
     return fail(FMASK_ERR_INVALID, "null tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))

@@ -190,6 +190,12 @@ def test_split_backward_varlen_dense_host_validation():
     assert b"interval array" in L.fmask_last_error()  # a hand-filled encoding without its mask data
     iv_enc.intervals = p.value
     assert L.fmask_attn_bwd(*args, p, need - 16, ctypes.byref(iv_enc), ctypes.byref(t), None) == fm.ERR_CAPACITY
+    # null tensor pointers are refused unless their sequence is empty
+    nargs = [ctypes.byref(a), None] + [p] * 3 + [ctypes.cast(p, ctypes.c_void_p)] + [p] * 4
+    assert L.fmask_attn_bwd(*nargs, p, need, ctypes.byref(iv_enc), ctypes.byref(t), None) == fm.ERR_INVALID
+    assert b"null tensor pointer" in L.fmask_last_error()
+    assert L.fmask_attn_fwd(ctypes.byref(a), p, None, p, p, None, ctypes.byref(iv_enc), ctypes.byref(t),
+                            None) == fm.ERR_INVALID
     t64 = fm.Tiles()
     t64.bm, t64.bn, t64.nqt, t64.nkt, t64.batch, t64.heads = 64, 64, 8, 8, 1, 1
     assert L.fmask_attn_bwd(*args, p, need, ctypes.byref(iv_enc), ctypes.byref(t64), None) == fm.ERR_UNSUPPORTED

@@ -221,6 +221,24 @@ def test_full_size_bitmap_sampled(name, b):
         assert err.mean() <= GRAD_TOL["mean_rel"] * scale, f"{name} {nm} mean err {err.mean():.3e}"
 
 
+@pytest.mark.parametrize("S,K", [(0, 100), (100, 0), (0, 0)])
+def test_zero_length_sequences(S, K):
+    """No query rows or no keys (empty device tensors, whose pointers are null):
+    the forward writes O = 0 and LSE = -inf for every row, the backward zero
+    dQ when there is no key and zero dK, dV when there is no row."""
+    w = _small(128, S, K, Hq=4, Hkv=2, B=2, seed=3)
+    q, k, v = to_device(w, synth.draw_qkv(w))
+    do = torch.from_numpy(synth.draw_dout(w).view(np.int16)).view(torch.bfloat16).cuda()
+    enc = fm.encode(dict(family="causal_bottom_right", sq=S, skv=K))
+    tiles = fm.classify(enc, 128, 64)
+    o, lse = fm.attn_fwd(q, k, v, enc, tiles, scale=w["scale"])
+    dq, dk, dv = fm.attn_bwd(q, k, v, o, lse, do, enc, tiles, scale=w["scale"])
+    torch.cuda.synchronize()
+    assert o.shape == q.shape and dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape
+    assert bool((o == 0).all()) and bool(torch.isneginf(lse).all())
+    assert bool((dq == 0).all()) and bool((dk == 0).all()) and bool((dv == 0).all())
+
+
 def test_unsupported_combinations_are_refused():
     w = _small(128, 64, 64)
     q, k, v = to_device(w, synth.draw_qkv(w))

@@ -116,26 +116,22 @@ def test_blocks_full_size_sampled():
 
 
 def test_blocks_degenerate_sizes():
-    """One key, one query; and no key at all (every list empty: O = 0 and
-    LSE = -inf, with no partial-state kernel launched)."""
+    """One key, one query; no key at all (every list empty: O = 0 and LSE =
+    -inf, with no partial-state kernel launched); no query."""
     for sq, skv in ((5, 1), (1, 33)):
         _check_all_rows(_workload(1, sq, skv, 128, 4, 2, 59 + skv, per_batch=True, n=8), f"blocks sq {sq} skv {skv}")
-    # skv = 0 through the C ABI (a zero-row tensor has no device pointer in the
-    # binding): valid one-row K and V buffers, skv set to 0 in the arguments
-    sq = 7
-    spec = dict(family="selected_key", sq=sq, skv=0, batch=1, sel=np.full((1, sq, 8), -1, np.int32), sel_cells=32)
-    enc = fm.encode(spec)
-    q = torch.randn(1, 4, sq, 128, device="cuda").to(torch.bfloat16)
-    kv = torch.zeros(1, 2, 1, 128, dtype=torch.bfloat16, device="cuda")
-    o = torch.full_like(q, 5.0)
-    lse = torch.zeros(1, 4, sq, dtype=torch.float32, device="cuda")
-    a = fm.attn_args(q, kv, kv, o, 1 / math.sqrt(128))
-    a.skv = 0
-    L = fm.lib()
-    need = L.fmask_attn_blocks_workspace_bytes(ctypes.byref(a), ctypes.byref(enc.struct))
-    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    st = L.fmask_attn_fwd_blocks(ctypes.byref(a), fm._ptr(q), fm._ptr(kv), fm._ptr(kv), fm._ptr(o), fm._ptr(lse),
-                                 ctypes.byref(enc.struct), fm._ptr(ws), need, None)
-    torch.cuda.synchronize()
-    assert st == fm.OK
-    assert bool((o == 0).all()) and bool(torch.isneginf(lse).all())
+    # no key, and no query: empty device tensors (null pointers) for K and V, or
+    # for Q and O, through the one-pass, block-major and split forms
+    for sq, skv in ((7, 0), (0, 64)):
+        sel = np.full((1, sq, 8), -1, np.int32)
+        spec = dict(family="selected_key", sq=sq, skv=skv, batch=1, sel=sel, sel_cells=32)
+        enc = fm.encode(spec)
+        q = torch.randn(1, 4, sq, 128, device="cuda").to(torch.bfloat16)
+        kv = torch.randn(1, 2, skv, 128, device="cuda").to(torch.bfloat16)
+        outs = [fm.attn_fwd(q, kv, kv, enc, None, scale=1 / math.sqrt(128)),
+                fm.attn_fwd_blocks(q, kv, kv, enc, scale=1 / math.sqrt(128)),
+                fm.attn_fwd_split(q, kv, kv, enc, splits=3, scale=1 / math.sqrt(128))]
+        torch.cuda.synchronize()
+        for o, lse in outs:
+            assert o.shape == q.shape and lse.shape == q.shape[:3]
+            assert bool((o == 0).all()) and bool(torch.isneginf(lse).all())

@@ -33,6 +33,8 @@
 // else hides the LDS latency).  The file is compiled with VGPR-form MFMAs (build.py).
 #include <float.h>
 
+#include <algorithm>
+
 #include "device_util.h"
 #include "internal.h"
 
@@ -106,32 +108,37 @@ __device__ inline int logical_item(int gsz) {
 }
 
 // ------------------------------------------------------------------ rows
-// One 16-lane (D = 128) or 8-lane (D = 64) group per row.
+// One 16-lane (D = 128) or 8-lane (D = 64) group per row; a workgroup covers
+// RPB consecutive rows of one (batch, query head), found with one uniform
+// division per block of rows (per-thread 64-bit index arithmetic cost more
+// issue time than the row's loads); the grid strides over the blocks of rows.
 template <int D>
-__global__ void __launch_bounds__(256) k_bwd_rows(BwdParams p, int64_t rows) {
+__global__ void __launch_bounds__(256) k_bwd_rows(BwdParams p, int32_t nrb, int64_t nblocks) {
   constexpr int LPR = D / 8;          // lanes per row, 8 values each
   constexpr int RPB = 256 / LPR;      // rows per block
-  const int64_t g = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   const int sub = threadIdx.x % LPR;
-  float acc = 0.f;
-  int64_t b = 0, h = 0, i = 0;
-  const bool ok = g < rows;
-  if (ok) {
-    i = g % p.sq;
-    h = (g / p.sq) % p.hq;
-    b = g / ((int64_t)p.sq * p.hq);
-    const __bf16* O = (const __bf16*)p.o + b * p.os[0] + h * p.os[1] + i * p.os[2];
-    const __bf16* dO = (const __bf16*)p.dout + b * p.os[0] + h * p.os[1] + i * p.os[2];
-    const bf16x8 x = *(const bf16x8*)(O + 8 * sub), y = *(const bf16x8*)(dO + 8 * sub);
+  for (int64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+    const int64_t bh = blk / nrb;     // (batch, query head), uniform
+    const int rb = (int)(blk - bh * nrb);
+    const int64_t h = bh % p.hq, b = bh / p.hq;
+    const int i = rb * RPB + (int)threadIdx.x / LPR;
+    float acc = 0.f;
+    const bool ok = i < p.sq;
+    if (ok) {
+      const __bf16* O = (const __bf16*)p.o + b * p.os[0] + h * p.os[1] + (int64_t)i * p.os[2];
+      const __bf16* dO = (const __bf16*)p.dout + b * p.os[0] + h * p.os[1] + (int64_t)i * p.os[2];
+      const bf16x8 x = *(const bf16x8*)(O + 8 * sub), y = *(const bf16x8*)(dO + 8 * sub);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc += (float)x[j] * (float)y[j];
-  }
+      for (int j = 0; j < 8; ++j) acc += (float)x[j] * (float)y[j];
+    }
 #pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (ok && sub == 0) {
-    const float lse = p.lse[(b * p.hq + h) * p.sq + i];
-    p.ws[2 * g] = acc;
-    p.ws[2 * g + 1] = lse == -INFINITY ? INFINITY : lse * kLog2e;
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (ok && sub == 0) {
+      const int64_t g = bh * p.sq + i;
+      const float lse = p.lse[g];
+      p.ws[2 * g] = acc;
+      p.ws[2 * g + 1] = lse == -INFINITY ? INFINITY : lse * kLog2e;
+    }
   }
 }
 
@@ -1130,10 +1137,12 @@ template <int D, int KIND>
 hipError_t launch_d(const BwdParams& p, hipStream_t s) {
   // (With no query row the dK / dV kernel still runs: its empty column lists
   // write zeros.  With no key the dQ kernel's empty lists do the same.)
-  const int64_t rows = (int64_t)p.b * p.hq * p.sq;
   constexpr int RPB = 256 / (D / 8);
-  if (rows > 0)
-    hipLaunchKernelGGL((k_bwd_rows<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p, rows);
+  const int64_t nrb = ((int64_t)p.sq + RPB - 1) / RPB;  // row blocks per (batch, query head)
+  const int64_t nblocks = nrb * p.b * p.hq;
+  if (nblocks > 0)
+    hipLaunchKernelGGL((k_bwd_rows<D>), dim3((unsigned)std::min<int64_t>(nblocks, (int64_t)1 << 20)), dim3(256), 0,
+                       s, p, (int32_t)nrb, nblocks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dQ: items like the forward (tile rows x (batch, head) expansion)

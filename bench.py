@@ -14,7 +14,7 @@ Also reported (one object each under "workloads"): the other workloads at
 their full sizes, attention kernel time and effective TFLOP/s (gathered GB/s
 for the selected-key workload).
 
-Prints ONE JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+Prints ONE JSON line.  --gpus N with N > 1 exits: the benchmark runs on one GPU.
 """
 
 import argparse
@@ -461,7 +461,7 @@ def main():
                          "prints its own JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on exactly one GPU; --gpus must be 1"}))
         sys.exit(2)
 
     import torch

@@ -71,7 +71,7 @@ def test_every_row_full_size(name):
             fp32 = {b: tuple(t[b].float().contiguous() for t in (q, k, v))}
         qf, kf, vf = fp32[b]
         rows = np.arange(r0, min(w["Sq"], r0 + CHUNK))
-        vis = torch.from_numpy(np.ascontiguousarray(OM.dense_vis(spec, b, 0, rows))).cuda()
+        vis = torch.from_numpy(np.array(OM.dense_vis(spec, b, 0, rows), dtype=bool)).cuda()
         ro, rl = _reference_chunk(qf[:, r0:r0 + len(rows)], kf, vf, vis, w["scale"], G)
         empty = torch.isneginf(rl)
         n += ro.numel()
@@ -104,7 +104,7 @@ def _reference_backward(q, k, v, do, spec, b, scale, G):
     dv = torch.zeros_like(v)
     for r0 in range(0, Sq, CHUNK):
         rows = np.arange(r0, min(Sq, r0 + CHUNK))
-        masked = ~torch.from_numpy(np.ascontiguousarray(OM.dense_vis(spec, b, 0, rows))).cuda()
+        masked = ~torch.from_numpy(np.array(OM.dense_vis(spec, b, 0, rows), dtype=bool)).cuda()
         for g in range(Hq // G):
             qc = q[g * G:(g + 1) * G, r0:r0 + len(rows)]
             dc = do[g * G:(g + 1) * G, r0:r0 + len(rows)]

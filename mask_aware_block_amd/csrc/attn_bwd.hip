@@ -4,13 +4,15 @@
 //
 // With P_ij = exp(s_ij - LSE_i) on visible cells, D_i = sum_d dO_id O_id and
 // dS = P * (dO V^T - D):  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
-// Three launches, no atomics:
-//   k_bwd_rows   D_i and LSE_i log2(e) per row (+inf for rows with no visible
-//                key, so that their P is exactly 0).
+// Two launches, no atomics:
 //   k_bwd_dq     one 128-row query tile per workgroup (four 32-row waves)
 //                walking the tile row's compact list of 64-key tiles, as in
 //                the forward: S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, then
-//                dQ^T += K^T dS^T.
+//                dQ^T += K^T dS^T.  Its prologue forms each row's D_i (from
+//                the row's dO, already in registers, and O) and LSE_i log2(e)
+//                (+inf for rows with no visible key, so that their P is
+//                exactly 0), and leaves both in the workspace for the dK/dV
+//                kernel, which runs after it.
 //   k_bwd_dkdv   one 64-key tile per workgroup walking its column list of
 //                128-row query tiles, for every query head of the K/V head:
 //                S = Q K^T and dP = dO V^T, then dV^T += dO^T P and
@@ -32,8 +34,6 @@
 // of registers (the four-wave dK/dV kernel runs one wave per SIMD, so nothing
 // else hides the LDS latency).  The file is compiled with VGPR-form MFMAs (build.py).
 #include <float.h>
-
-#include <algorithm>
 
 #include "device_util.h"
 #include "internal.h"
@@ -107,41 +107,6 @@ __device__ inline int logical_item(int gsz) {
   return ((k / gsz) * kXcds + xcd) * gsz + (k % gsz);
 }
 
-// ------------------------------------------------------------------ rows
-// One 16-lane (D = 128) or 8-lane (D = 64) group per row; a workgroup covers
-// RPB consecutive rows of one (batch, query head), found with one uniform
-// division per block of rows (per-thread 64-bit index arithmetic cost more
-// issue time than the row's loads); the grid strides over the blocks of rows.
-template <int D>
-__global__ void __launch_bounds__(256) k_bwd_rows(BwdParams p, int32_t nrb, int64_t nblocks) {
-  constexpr int LPR = D / 8;          // lanes per row, 8 values each
-  constexpr int RPB = 256 / LPR;      // rows per block
-  const int sub = threadIdx.x % LPR;
-  for (int64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
-    const int64_t bh = blk / nrb;     // (batch, query head), uniform
-    const int rb = (int)(blk - bh * nrb);
-    const int64_t h = bh % p.hq, b = bh / p.hq;
-    const int i = rb * RPB + (int)threadIdx.x / LPR;
-    float acc = 0.f;
-    const bool ok = i < p.sq;
-    if (ok) {
-      const __bf16* O = (const __bf16*)p.o + b * p.os[0] + h * p.os[1] + (int64_t)i * p.os[2];
-      const __bf16* dO = (const __bf16*)p.dout + b * p.os[0] + h * p.os[1] + (int64_t)i * p.os[2];
-      const bf16x8 x = *(const bf16x8*)(O + 8 * sub), y = *(const bf16x8*)(dO + 8 * sub);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc += (float)x[j] * (float)y[j];
-    }
-#pragma unroll
-    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-    if (ok && sub == 0) {
-      const int64_t g = bh * p.sq + i;
-      const float lse = p.lse[g];
-      p.ws[2 * g] = acc;
-      p.ws[2 * g + 1] = lse == -INFINITY ? INFINITY : lse * kLog2e;
-    }
-  }
-}
-
 // ------------------------------------------------------------------ dQ
 template <int D>
 struct GeoQ {
@@ -201,11 +166,27 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdParams p, int expand, int 
       df[t] = bf16x8{};
     }
   }
-  float dlt = 0.f, lse2 = INFINITY;
+  // D_i = sum_d dO_id O_id: this lane's half of row qrow (the d of its dO
+  // fragments), then the other half from lane ^ 32; with LSE_i log2(e) it goes
+  // to the workspace for the dK/dV kernel (every row of every (batch, query
+  // head) belongs to exactly one item of this launch).
+  float dpart = 0.f, lse2 = INFINITY;
+  const int64_t g = ((int64_t)b * p.hq + h) * p.sq + qrow;
   if (qrow < p.sq) {
-    const int64_t g = ((int64_t)b * p.hq + h) * p.sq + qrow;
-    dlt = p.ws[2 * g];
-    lse2 = p.ws[2 * g + 1];
+    const __bf16* Orow = (const __bf16*)p.o + b * p.os[0] + h * p.os[1] + qrow * p.os[2] + 8 * half;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      const bf16x8 x = *(const bf16x8*)(Orow + 16 * t);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dpart += (float)x[j] * (float)df[t][j];
+    }
+    const float lse = p.lse[g];
+    lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+  }
+  const float dlt = dpart + __shfl_xor(dpart, 32);
+  if (qrow < p.sq && half == 0) {
+    p.ws[2 * g] = dlt;
+    p.ws[2 * g + 1] = lse2;
   }
   wait_all();  // nothing tracked may stay pending once untracked loads fly
 
@@ -1137,15 +1118,9 @@ template <int D, int KIND>
 hipError_t launch_d(const BwdParams& p, hipStream_t s) {
   // (With no query row the dK / dV kernel still runs: its empty column lists
   // write zeros.  With no key the dQ kernel's empty lists do the same.)
-  constexpr int RPB = 256 / (D / 8);
-  const int64_t nrb = ((int64_t)p.sq + RPB - 1) / RPB;  // row blocks per (batch, query head)
-  const int64_t nblocks = nrb * p.b * p.hq;
-  if (nblocks > 0)
-    hipLaunchKernelGGL((k_bwd_rows<D>), dim3((unsigned)std::min<int64_t>(nblocks, (int64_t)1 << 20)), dim3(256), 0,
-                       s, p, (int32_t)nrb, nblocks);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // dQ: items like the forward (tile rows x (batch, head) expansion)
+  hipError_t e = hipSuccess;
+  // dQ (and the rows' D_i, LSE_i for the dK / dV kernel): items like the
+  // forward (tile rows x (batch, head) expansion)
   {
     const int expand = (p.mb == 1 ? p.b : 1) * (p.mh == 1 ? p.hq : 1);
     const int64_t n = (int64_t)p.mb * p.mh * p.nqt * expand;

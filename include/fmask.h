@@ -375,7 +375,7 @@ size_t fmask_attn_blocks_workspace_bytes(const fmask_attn_args *args, const fmas
  * block, the (query, entry) pairs that name it; each block's K and V are then
  * read once per K/V head and scored against the Q rows of those queries, which
  * gives one partial state (maximum, sum, O / sum rounded to bf16) per
- * (batch, query, entry, head) in `workspace`; a second kernel merges each
+ * (batch, query, head, entry) in `workspace`; a second kernel merges each
  * query's partials in entry order.  The result does not depend on the order
  * in which pairs reach a block.
  * Supported: BF16, d in {128, 256}, sel_cells == 32, hq / hkv in

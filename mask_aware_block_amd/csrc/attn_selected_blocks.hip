@@ -15,7 +15,7 @@
 //       gathered into registers, S^T = K Q^T and O^T = V^T P^T on MFMA with the
 //       block's exact maximum, and each row's partial state written out: the
 //       exp2-domain maximum m, the sum l and O / l in bf16, at the place of its
-//       (batch, query, entry, head), with non-temporal stores (read once, by the
+//       (batch, query, head, entry), with non-temporal stores (read once, by the
 //       merge, which loads them non-temporally too);
 //   k_blk_combine   one workgroup per (batch, query): per head the partials of
 //       its entries merged with factors l_k 2^(m_k - max m) (the split-K rule
@@ -108,6 +108,13 @@ __global__ void __launch_bounds__(256) k_blk_scatter(const int32_t* list, const 
 }
 
 // ---------------------------------------------------------------- partials
+
+// Place of the partial state of (batch b, query q, query head h, list entry e)
+// in the workspace: the entries of one (query, head) are consecutive, so the
+// merge reads each (query, head)'s partial O rows as one contiguous run.
+__device__ inline int64_t part_slot(const SelAttnParams& p, int b, int q, int h, int e) {
+  return (((int64_t)b * p.sq + q) * p.hq + h) * p.n + e;
+}
 
 template <int D>
 struct BGeo {
@@ -266,8 +273,7 @@ __global__ void __launch_bounds__(NT, 2) k_blk_partial(SelAttnParams p, int nblk
     }
     const float inv_l = 1.f / l_tot;  // l >= 1: the maximum's own term
     if (live && half == 0) {
-      const int64_t pair = ((int64_t)b * p.sq + q) * p.n + (ent & 0xff);
-      __builtin_nontemporal_store(f32x2{m2, l_tot}, pm + pair * p.hq + h);
+      __builtin_nontemporal_store(f32x2{m2, l_tot}, pm + part_slot(p, b, q, h, ent & 0xff));
     }
     const int rr = lane >> 3, ch = lane & 7;
 #pragma unroll
@@ -288,8 +294,8 @@ __global__ void __launch_bounds__(NT, 2) k_blk_partial(SelAttnParams p, int nblk
         if (orow < rows) {
           const int oe = orow / G, og = orow - oe * G;
           const int oent = entries[oe];
-          const int64_t pair = ((int64_t)b * p.sq + (oent >> 8)) * p.n + (oent & 0xff);
-          __builtin_nontemporal_store(v, (bf16x8*)(po + (pair * p.hq + kvh * G + og) * D + rd * 64 + ch * 8));
+          const int64_t slot = part_slot(p, b, oent >> 8, kvh * G + og, oent & 0xff);
+          __builtin_nontemporal_store(v, (bf16x8*)(po + slot * D + rd * 64 + ch * 8));
         }
       }
     }
@@ -311,14 +317,14 @@ __global__ void __launch_bounds__(NT) k_blk_combine(SelAttnParams p, const f32x2
   const int cnt = p.count[(int64_t)mbi * p.sq + q];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   __bf16* O = (__bf16*)p.o + b * p.os[0] + (int64_t)q * p.os[2];
-  const int64_t pair0 = ((int64_t)b * p.sq + q) * p.n;
+  const int64_t slot0 = part_slot(p, b, q, 0, 0);  // + h n + entry
   for (int h = w; h < p.hq; h += NW) {
     float acc[DPL];
 #pragma unroll
     for (int j = 0; j < DPL; ++j) acc[j] = 0.f;
     float lse = -INFINITY;
     if (cnt > 0) {
-      const f32x2 ml = lane < cnt ? __builtin_nontemporal_load(pm + (pair0 + lane) * p.hq + h)
+      const f32x2 ml = lane < cnt ? __builtin_nontemporal_load(pm + slot0 + h * p.n + lane)
                                   : f32x2{-FLT_MAX, 0.f};
       float M = ml.x;
 #pragma unroll
@@ -328,8 +334,8 @@ __global__ void __launch_bounds__(NT) k_blk_combine(SelAttnParams p, const f32x2
 #pragma unroll
       for (int d = 32; d >= 1; d >>= 1) L += __shfl_xor(L, d);
       const float wn = wk / L;
-      const __bf16* src = po + (pair0 * p.hq + h) * D + lane * DPL;
-      const int64_t stride = (int64_t)p.hq * D;
+      const __bf16* src = po + (slot0 + h * p.n) * D + lane * DPL;
+      const int64_t stride = D;  // the entries of one (query, head) are consecutive
       int k = 0;
       for (; k + 8 <= cnt; k += 8) {
         typedef __bf16 bfv __attribute__((ext_vector_type(DPL)));

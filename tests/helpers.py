@@ -17,6 +17,17 @@ TOL = {"f32": dict(max_abs=1e-5, mean_abs=1e-5, lse=1e-5),
        "bf16": dict(max_abs=2e-2, mean_abs=1e-3, lse=2.0 ** -8 + 5e-4)}
 
 
+# Gradient checks bound the error relative to the largest reference value of
+# each tensor, that scale floored at GRAD_SCALE_FLOOR.  Where the exact gradient
+# is zero by cancellation (a row with one visible key has dS = P (dP - D) = 0:
+# dP_ij and D_i are the same dot product of dO with V_j = O_i), the kernel's
+# fp32 dP and D, sums of D products of bf16 values, differ by rounding noise of
+# up to about D 2^-24 max|dO| max|V|, times scale max|K| in dQ (~1e-4 at
+# D = 128 for N(0,1) data).  The floor admits that noise (2e-2 x 5e-3 = 1e-4 max
+# abs, 1e-5 mean abs), still inside the absolute bf16 bound of 2e-2 / 1e-3.
+GRAD_SCALE_FLOOR = 5e-3
+
+
 def to_device(w, arrays, device="cuda"):
     import torch
     q, k, v = arrays

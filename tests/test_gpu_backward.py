@@ -16,7 +16,7 @@ import pytest
 
 import synth
 from oracle import attention as OA
-from tests.helpers import to_device, to_f64
+from tests.helpers import GRAD_SCALE_FLOOR, to_device, to_f64
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -56,7 +56,7 @@ def _grad_check(w, spec, what, heads=None):
     for name, got, ref in (("dq", dq[:, sl_q], rq), ("dk", dk[:, sl_k], rk), ("dv", dv[:, sl_k], rv)):
         g = got.float().cpu().numpy().astype(np.float64)
         assert np.isfinite(g).all(), f"{what}: {name} not finite"
-        scale = max(np.abs(ref).max(), 1e-6)
+        scale = max(np.abs(ref).max(), GRAD_SCALE_FLOOR)
         err = np.abs(g - ref)
         out[name] = (err.max() / scale, err.mean() / scale)
         assert err.max() <= GRAD_TOL["max_rel"] * scale, f"{what}: {name} max err {err.max():.3e} (ref max {scale:.3e})"
@@ -175,7 +175,7 @@ def test_full_size_causal_doc_32k_sampled():
     for name, ref in (("dq", rq), ("dk", rk), ("dv", rv)):
         g = got[name].float().cpu().numpy().astype(np.float64)
         assert np.isfinite(g).all(), f"{name} not finite"
-        scale = max(np.abs(ref).max(), 1e-6)
+        scale = max(np.abs(ref).max(), GRAD_SCALE_FLOOR)
         err = np.abs(g - ref)
         print(f"causal_doc_32k sampled {name}: max {err.max() / scale:.2e}, mean {err.mean() / scale:.2e} "
               f"of the largest sampled reference value", flush=True)
@@ -213,7 +213,7 @@ def test_full_size_bitmap_sampled(name, b):
     for nm, ref in (("dq", rq), ("dk", rk), ("dv", rv)):
         g = got[nm].float().cpu().numpy().astype(np.float64)
         assert np.isfinite(g).all(), f"{name} {nm} not finite"
-        scale = max(np.abs(ref).max(), 1e-6)
+        scale = max(np.abs(ref).max(), GRAD_SCALE_FLOOR)
         err = np.abs(g - ref)
         print(f"{name} batch {b} sampled {nm}: max {err.max() / scale:.2e}, mean {err.mean() / scale:.2e} "
               f"of the largest sampled reference value", flush=True)

@@ -16,7 +16,7 @@ import pytest
 
 import synth
 from oracle import masks as OM
-from tests.helpers import TOL, to_device
+from tests.helpers import GRAD_SCALE_FLOOR, TOL, to_device
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -145,7 +145,7 @@ def test_backward_every_row_full_size(name):
         for what, got, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
             g = got[b].float()
             assert bool(torch.isfinite(g).all()), f"{name} batch {b}: {what} not finite"
-            mag = max(float(r.abs().max()), 1e-6)
+            mag = max(float(r.abs().max()), GRAD_SCALE_FLOOR)
             err = (g - r).abs()
             stats[(b, what)] = (float(err.max()) / mag, float(err.mean()) / mag)
             assert float(err.max()) <= 2e-2 * mag, f"{name} batch {b}: {what} max abs err {float(err.max()):.3e}"

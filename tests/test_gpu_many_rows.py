@@ -21,7 +21,7 @@ import numpy as np
 import pytest
 
 from oracle import attention as OA
-from tests.helpers import TOL
+from tests.helpers import GRAD_SCALE_FLOOR, TOL
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -69,7 +69,7 @@ def test_many_rows_forward_and_backward():
         for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
             g = _f64(got[:, :, r])
             assert np.isfinite(g).all(), f"doc {d}: {name} not finite"
-            ref_max = max(np.abs(ref).max(), 1e-6)
+            ref_max = max(np.abs(ref).max(), GRAD_SCALE_FLOOR)
             err = np.abs(g - ref)
             assert err.max() <= GRAD_TOL["max_rel"] * ref_max, f"doc {d}: {name} max err {err.max():.3e}"
             assert err.mean() <= GRAD_TOL["mean_rel"] * ref_max, f"doc {d}: {name} mean err {err.mean():.3e}"

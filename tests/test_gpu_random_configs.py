@@ -17,7 +17,7 @@ import pytest
 import synth
 from oracle import attention as OA
 from oracle import masks as OM
-from tests.helpers import compare, to_device, to_f64
+from tests.helpers import GRAD_SCALE_FLOOR, compare, to_device, to_f64
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -105,7 +105,7 @@ def _case(seed):
     return w, spec, rng
 
 
-@pytest.mark.parametrize("seed", range(96))
+@pytest.mark.parametrize("seed", list(range(96)) + [531, 700, 776])
 def test_random_configuration(seed):
     w, spec, rng = _case(seed)
     desc = (f"seed {seed}: {spec['family']} B{w['B']} Hq{w['Hq']} Hkv{w['Hkv']} Sq{w['Sq']} Skv{w['Skv']} "
@@ -144,7 +144,7 @@ def test_random_configuration(seed):
         for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
             g = got.float().cpu().numpy().astype(np.float64)
             assert np.isfinite(g).all(), f"{desc}: {name} not finite"
-            scale = max(np.abs(ref).max(), 1e-6)
+            scale = max(np.abs(ref).max(), GRAD_SCALE_FLOOR)
             err = np.abs(g - ref)
             assert err.max() <= 2e-2 * scale, f"{desc}: {name} max err {err.max():.3e} (ref max {scale:.3e})"
             assert err.mean() <= 2e-3 * scale, f"{desc}: {name} mean err {err.mean():.3e}"
